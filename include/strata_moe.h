@@ -1,0 +1,211 @@
+/*
+ * strata_moe.h — C ABI of the routed Mixture-of-Experts expert layer for MI355X (gfx950).
+ *
+ * The layer: each token picks k of E experts from its router logits, every picked expert runs a
+ * SwiGLU feed-forward network on block-quantized 2- or 3-bit weights, and the token's output is
+ * the router-weighted sum of its experts' outputs.
+ *
+ * Sources.  The pages describe a model whose layers each hold 512 experts with 10 active per
+ * token over 48 layers ("Strata vs Llama.cpp vs vLLM", transcript at 08:23; "Local AI Is Now 6x
+ * Faster on Your PC", key technological idea).  They name the expert matrix multiply as the
+ * heaviest computation and say it dequantizes low-bit blocks during the multiply ("Two-Day Port,
+ * 8x Faster Prefill: Strata Engine Benchmarked", Where Strata Is Fast).  They say k-quants go down
+ * to two or three bits per weight and are dequantized on the fly ("Strata vs Llama.cpp vs vLLM",
+ * transcript at 04:12).  The pages print neither the router formula, the FFN form, nor any bit
+ * layout; the definitions below (softmax top-k routing, SwiGLU, the Q2/Q3 block formats) are this
+ * library's specification and are stated in full where each call is declared.
+ *
+ * Conventions that hold for every entry point:
+ *  - Every pointer argument that is not marked "host" is a device pointer (hipMalloc'd memory,
+ *    e.g. a torch tensor's data_ptr()).  The caller allocates and owns all buffers; the library
+ *    never allocates, frees or synchronises.  Scratch memory comes from a caller-provided
+ *    workspace whose size strata_moe_workspace_bytes() returns.
+ *  - Device pointers must be 16-byte aligned (128-bit loads and stores).
+ *  - All work is enqueued asynchronously on `stream` (NULL = the null stream).  The return code
+ *    is synchronous: arguments are validated before any HIP call, and on any error nothing has
+ *    been enqueued.  STRATA_ERR_HIP means a launch itself failed.  Device-side faults surface at
+ *    the caller's next synchronisation.
+ *  - T = 0 is a no-op that returns STRATA_OK.
+ *  - The library holds no global mutable state; calls on different streams with disjoint
+ *    outputs and workspaces may run concurrently.
+ *  - Non-finite logits, activations or scales are outside the contract (not checked).
+ *  - Results are deterministic: the same inputs give bit-identical outputs on every call
+ *    (no floating-point atomics anywhere).
+ */
+#ifndef STRATA_MOE_H
+#define STRATA_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STRATA_OK = 0,
+  STRATA_ERR_INVALID_ARGUMENT = 1,   /* null or misaligned pointer, non-positive size, k > E ... */
+  STRATA_ERR_UNSUPPORTED = 2,        /* well-formed but outside what the kernels handle        */
+  STRATA_ERR_WORKSPACE_TOO_SMALL = 3,
+  STRATA_ERR_HIP = 4                 /* a kernel launch failed                                  */
+} strata_status;
+
+/*
+ * Block-quantized weight formats.  A block is 32 consecutive weights along the reduction
+ * dimension of a matrix row, with one fp16 (IEEE binary16) scale d per block.
+ *
+ * STRATA_Q2_B32: 2-bit codes q in {0..3}; w = d * (q - 1.5).  A block's codes take 8 bytes:
+ *   weight i (0..31) sits in bits [2*(i%16), 2*(i%16)+1] of little-endian uint32 word i/16,
+ *   i.e. byte i/4, bits [2*(i%4), 2*(i%4)+1].
+ * STRATA_Q3_B32: 3-bit codes q in {0..7}; w = d * (q - 3.5).  A block's codes take 12 bytes
+ *   read as one 96-bit little-endian integer; weight i sits in bits [3*i, 3*i+2] (codes may
+ *   straddle byte and word edges).
+ *
+ * A matrix with R rows and reduction length K (K a multiple of 32) is stored as two arrays
+ * (structure of arrays, row-major):
+ *   codes  [R][K/32][8 or 12 bytes]
+ *   scales [R][K/32] fp16
+ * so w[r][c] = scale[r][c/32] * (code of weight c%32 in block [r][c/32] - offset).
+ */
+typedef enum {
+  STRATA_Q2_B32 = 2,
+  STRATA_Q3_B32 = 3
+} strata_qformat;
+
+/*
+ * One layer's expert weights, all device pointers, expert-major:
+ *   gate W_g and up W_u: per expert an [I][H] matrix (rows = intermediate features, reduction
+ *     along H): codes [E][I][H/32][cb], scales [E][I][H/32];
+ *   down W_d: per expert an [H][I] matrix (rows = hidden features, reduction along I):
+ *     codes [E][H][I/32][cb], scales [E][H][I/32];
+ * with cb = 8 (Q2) or 12 (Q3).  Expert e's arrays start at e times the per-expert size.
+ */
+typedef struct strata_moe_weights {
+  int32_t fmt;          /* strata_qformat */
+  int32_t num_experts;  /* E: 1..1024 */
+  int32_t hidden;       /* H: multiple of 128 */
+  int32_t inter;        /* I: multiple of 128 */
+  const void* gate_codes;
+  const void* up_codes;
+  const void* down_codes;
+  const uint16_t* gate_scales;
+  const uint16_t* up_scales;
+  const uint16_t* down_scales;
+} strata_moe_weights;
+
+/*
+ * Router: per-token top-k selection and weights.
+ * The pages say each token is routed to 10 of a layer's 512 experts and that the routers run on
+ * the GPU ("Strata vs Llama.cpp vs vLLM", transcript 08:23 and 09:28; "Strata - the details",
+ * How it works / memory tiers); they give no formula.  This library's definition: softmax over
+ * all E logits, keep the k largest, renormalise.  Selection is made on the fp32 logits
+ * themselves (softmax is monotone); expert a beats expert b iff l_a > l_b, or l_a == l_b and
+ * a < b.  Slot j (0..k-1) holds the j-th pick (descending logit).  The renormalised weights are
+ * w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k picks (the full softmax denominator
+ * cancels).
+ *
+ *   logits   fp32 [T][E] row-major (read)
+ *   topk_ids int32 [T][k] (written)
+ *   topk_w   fp32 [T][k] (written)
+ * Limits: 1 <= k <= min(E, 16), 1 <= E <= 1024.
+ */
+strata_status strata_moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                               int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
+ * Permute: group the S = T*k (token, slot) pairs by expert with a stable counting sort.
+ * Implied by per-expert matrix multiplies ("Two-Day Port, 8x Faster Prefill: Strata Engine
+ * Benchmarked", Where Strata Is Fast); the pages give no algorithm.  Slot s = t*k + j.
+ *   counts      int32 [E]    number of slots routed to expert e
+ *   offsets     int32 [E+1]  exclusive prefix sum of counts; offsets[E] = S
+ *   sorted_slot int32 [S]    position p -> slot; expert e's segment is
+ *                            [offsets[e], offsets[e+1]) in ascending slot order
+ *   slot_pos    int32 [S]    inverse: slot -> position
+ * Workspace: at least strata_moe_permute_workspace_bytes(T, E, k).
+ * Limits: as strata_moe_route; S < 2^31.
+ */
+strata_status strata_moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                 int32_t* slot_pos, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Expert FFN (prefill path): for every expert e and every slot s in its segment (token t =
+ * s / k), with x the token's activations widened exactly from bf16:
+ *   g = W_g x,  u = W_u x,  a = SiLU(g) * u  (SiLU(z) = z / (1 + exp(-z))),  out = W_d a.
+ * The pages call the expert matrix multiply the heaviest computation and describe dequantizing
+ * the low-bit blocks during the multiply ("Two-Day Port, 8x Faster Prefill: Strata Engine
+ * Benchmarked", Where Strata Is Fast); the gate/up/SiLU-mul/down form is this library's
+ * definition.  Weights are used exactly (codes enter the matrix cores as exact bf16 values and
+ * each block's fp16 scale is applied in fp32); a and out are rounded to bf16.
+ *
+ *   x           bf16 [T][H] (uint16 bit patterns)
+ *   offsets, sorted_slot  as produced by strata_moe_permute for this (T, k, E)
+ *   expert_out  bf16 [T*k][H], row s = slot s (unweighted expert output), written
+ * Workspace: at least strata_moe_workspace_bytes(T, E, k, H, I).
+ * Limits: w->hidden and w->inter multiples of 128; E, k as strata_moe_route.
+ */
+strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t* x, int32_t T,
+                                    int32_t k, const int32_t* offsets,
+                                    const int32_t* sorted_slot, uint16_t* expert_out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Combine: y[t] = sum_{j = 0..k-1, ascending} topk_w[t][j] * expert_out[t*k + j]   (fp32),
+ * and with accumulate != 0, y[t] += that sum instead (the residual add of a layer stack).
+ * The pages do not spell the combine out; this is the weighted sum of the routed outputs.
+ *   expert_out bf16 [T*k][H], topk_w fp32 [T][k], y fp32 [T][H].
+ */
+strata_status strata_moe_combine(const uint16_t* expert_out, const float* topk_w, int32_t T,
+                                 int32_t k, int32_t H, float* y, int32_t accumulate,
+                                 hipStream_t stream);
+
+/*
+ * Decode / verify step for T <= 8 tokens (the pages' multi-token-prediction check of up to 3
+ * drafted tokens plus one: "Strata - the details", How it works / speculation).  Computes the
+ * same function as route + permute + expert_ffn + combine, with a bandwidth-bound path: every
+ * touched expert's weights are streamed once and applied to all tokens that picked it.  The
+ * intermediate a is kept in fp32 and no bf16 rounding is applied to the expert outputs.
+ *   x bf16 [T][H], logits fp32 [T][E], y fp32 [T][H] (overwritten, or += with accumulate)
+ *   opt_topk_ids int32 [T][k], opt_topk_w fp32 [T][k]: written when not NULL.
+ * Workspace: at least strata_moe_workspace_bytes(T, E, k, H, I).
+ * Limits: 1 <= T <= 8; others as strata_moe_expert_ffn.
+ */
+strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
+                                const float* logits, int32_t T, int32_t k, float* y,
+                                int32_t accumulate, int32_t* opt_topk_ids, float* opt_topk_w,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One-call layer: y (=, or += with accumulate) MoE(x).  T <= 8 runs strata_moe_decode's path;
+ * larger T runs route -> permute -> expert_ffn -> combine.  Each opt_* pointer may be NULL; when
+ * given it receives that intermediate (same layout as the staged calls).  opt_counts,
+ * opt_offsets and opt_sorted_slot are only produced on the T > 8 path and must be NULL for
+ * T <= 8 (STRATA_ERR_INVALID_ARGUMENT otherwise).
+ */
+strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, const float* logits,
+                               int32_t T, int32_t k, float* y, int32_t accumulate,
+                               int32_t* opt_topk_ids, float* opt_topk_w, int32_t* opt_counts,
+                               int32_t* opt_offsets, int32_t* opt_sorted_slot, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * RMSNorm for a layer stack: x[t] = bf16_RNE(h[t] / sqrt(mean_i h[t][i]^2 + eps)), unit gain.
+ *   h fp32 [T][H] (read), x bf16 [T][H] (written).  H a multiple of 128.
+ */
+strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
+                                 hipStream_t stream);
+
+/* Workspace sizes in bytes (host functions; 0 for invalid shapes). */
+size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k);
+size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
+
+/* Static string for a status code (host function; never NULL). */
+const char* strata_status_string(strata_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STRATA_MOE_H */

@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin is chosen so that a plausible mistake in the oracle fails it: a wrong code bit order
+or offset (exhaustive closed-form dequantization), a wrong tie rule or slot order (brute-force
+stable sort), a wrong weight formula (full softmax then renormalise, a different route to the
+same numbers), a transposed or dropped FFN term (independent numpy/torch float64 layer), a
+wrong combine (k = 1 and scale-doubling identities), and an order dependence between tokens
+(permutation equivariance).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# ---------------------------------------------------------------------------------------------
+# Independent vectorised decoders of the formats, written from the format description (byte i/4
+# at bits 2*(i%4) for 2-bit codes; an LSB-first 96-bit little-endian bitstream for 3-bit codes).
+
+
+def codes_q2(blocks: np.ndarray) -> np.ndarray:
+    b = blocks.astype(np.uint8)[..., :, None]                    # [..., 8, 1]
+    q = (b >> (2 * np.arange(4, dtype=np.uint8))) & 3            # [..., 8, 4]: weight 4*byte + j
+    return q.reshape(*blocks.shape[:-1], 32).astype(np.int64)
+
+
+def codes_q3(blocks: np.ndarray) -> np.ndarray:
+    bits = np.unpackbits(blocks.astype(np.uint8), axis=-1, bitorder="little")  # [..., 96]
+    bits = bits.reshape(*blocks.shape[:-1], 32, 3).astype(np.int64)
+    return bits[..., 0] + 2 * bits[..., 1] + 4 * bits[..., 2]
+
+
+def f16_values(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def dequant_np(fmt, codes, scales):
+    q = codes_q2(codes) if fmt == 2 else codes_q3(codes)         # [R, nb, 32]
+    c0 = 1.5 if fmt == 2 else 3.5
+    w = f16_values(scales)[..., None] * (q - c0)
+    return w.reshape(*scales.shape[:-1], scales.shape[-1] * 32)
+
+
+def encode_q2(q: np.ndarray) -> np.ndarray:
+    """32 codes -> 8 bytes, byte i/4 holding weight i at bits 2*(i%4)."""
+    out = np.zeros(8, dtype=np.uint8)
+    for i, v in enumerate(q):
+        out[i // 4] |= np.uint8(int(v) << (2 * (i % 4)))
+    return out
+
+
+def encode_q3(q: np.ndarray) -> np.ndarray:
+    v = 0
+    for i, c in enumerate(q):
+        v |= int(c) << (3 * i)
+    return np.frombuffer(v.to_bytes(12, "little"), dtype=np.uint8).copy()
+
+
+SCALE_BITS = [0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x3555, 0x7BFF, 0xBC00, 0x8001]
+
+
+# ---------------------------------------------------------------------------------------------
+# Number formats
+
+
+def test_f16_decode_all_patterns(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_bf16_decode_is_upper_half_of_f32(oracle_lib):
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 65536, size=4000).astype(np.uint16)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_to_f64(int(b)) for b in bits])
+    ok = np.isfinite(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+# ---------------------------------------------------------------------------------------------
+# Dequantization: closed form, exhaustively over codes x positions x scales
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_dequant_closed_form_exhaustive(oracle_lib, fmt):
+    nq = 4 if fmt == 2 else 8
+    c0 = 1.5 if fmt == 2 else 3.5
+    enc = encode_q2 if fmt == 2 else encode_q3
+    for pos in range(32):
+        for q in range(nq):
+            codes = np.array([(pos + 3 * i + 1) % nq for i in range(32)], dtype=np.int64)
+            codes[pos] = q
+            blk = enc(codes)
+            assert oracle.code(fmt, blk, pos) == q
+            for sb in SCALE_BITS:
+                d = float(np.uint16(sb).view(np.float16))
+                got = oracle.dequant_block(fmt, blk, sb)
+                want = np.array([d * (float(c) - c0) for c in codes])
+                assert np.array_equal(got, want), (fmt, pos, q, hex(sb))
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_dequant_matrix_matches_vectorised_decoder(oracle_lib, fmt):
+    rng = np.random.default_rng(7)
+    cb = 8 if fmt == 2 else 12
+    codes = rng.integers(0, 256, size=(24, 8, cb)).astype(np.uint8)
+    scales = mi.f32_to_f16_bits(rng.standard_normal((24, 8)).astype(np.float32) * 0.02)
+    got = oracle.dequant_matrix(fmt, codes, scales)
+    assert np.array_equal(got, dequant_np(fmt, codes, scales))
+
+
+def test_q3_codes_straddling_byte_edges(oracle_lib):
+    # weights whose 3 bits cross a byte boundary: bit 3i mod 8 > 5
+    straddle = [i for i in range(32) if (3 * i) % 8 > 5]
+    assert straddle == [2, 5, 10, 13, 18, 21, 26, 29]
+    for i in straddle:
+        for q in range(8):
+            codes = np.zeros(32, dtype=np.int64)
+            codes[i] = q
+            assert oracle.code(3, encode_q3(codes), i) == q
+
+
+# ---------------------------------------------------------------------------------------------
+# Routing
+
+
+def brute_route(logits: np.ndarray, k: int):
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k))
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))
+        ids[t] = order[:k]
+        # full softmax over all experts, then renormalise the k kept probabilities
+        l = logits[t].astype(np.float64)
+        p = np.exp(l - l.max())
+        p /= p.sum()
+        kept = p[ids[t]]
+        w[t] = kept / kept.sum()
+    return ids, w
+
+
+@pytest.mark.parametrize("T,E,k,levels", [(16, 64, 4, None), (9, 17, 5, 4), (5, 512, 10, None),
+                                          (7, 8, 8, 2), (3, 33, 1, 3)])
+def test_route_brute_force(oracle_lib, T, E, k, levels):
+    rng = np.random.default_rng(T * 1000 + E)
+    if levels is None:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+    else:  # few distinct values: many ties
+        logits = rng.integers(0, levels, size=(T, E)).astype(np.float32) * 0.5
+    ids, w = oracle.route(logits, k)
+    bids, bw = brute_route(logits, k)
+    assert np.array_equal(ids, bids)
+    np.testing.assert_allclose(w, bw, rtol=1e-13, atol=0)
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == k
+        assert abs(w[t].sum() - 1.0) < 1e-14
+        assert np.all(np.diff(w[t]) <= 0)
+
+
+def test_route_all_equal_and_signed_zero(oracle_lib):
+    logits = np.zeros((2, 12), dtype=np.float32)
+    logits[1, :] = -0.0
+    logits[1, 5] = 0.0  # +0 == -0: still a tie, lower index wins
+    ids, w = oracle.route(logits, 4)
+    assert ids.tolist() == [[0, 1, 2, 3], [0, 1, 2, 3]]
+    assert np.all(w == 0.25)
+
+
+# ---------------------------------------------------------------------------------------------
+# Permutation
+
+
+@pytest.mark.parametrize("T,E,k", [(16, 64, 4), (1, 5, 5), (37, 3, 2), (64, 512, 10)])
+def test_permute_is_stable_sort(oracle_lib, T, E, k):
+    rng = np.random.default_rng(T + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, sorted_slot, slot_pos = oracle.permute(ids, E)
+    flat = ids.reshape(-1)
+    S = flat.size
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and offsets[-1] == S
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(sorted_slot, np.array(sorted(range(S), key=lambda s: flat[s])))
+    assert np.array_equal(np.sort(sorted_slot), np.arange(S))
+    assert np.array_equal(slot_pos[sorted_slot], np.arange(S))
+    for e in range(E):
+        seg = sorted_slot[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------------------------------------
+# Expert FFN and the whole layer against an independent float64 implementation
+
+
+def independent_layer(w, x_bits, logits, k):
+    """Vectorised numpy/torch float64 layer: stable argsort routing, full-softmax weights,
+    SwiGLU via torch matmul, weighted sum."""
+    E, H, I, fmt = w["E"], w["H"], w["I"], w["fmt"]
+    x = torch.from_numpy(mi.bf16_bits_to_f32(x_bits).astype(np.float64))
+    T = x.shape[0]
+    ids = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k]
+    l = logits.astype(np.float64)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    kept = np.take_along_axis(p, ids, axis=1)
+    rw = kept / kept.sum(axis=1, keepdims=True)
+    y = torch.zeros((T, H), dtype=torch.float64)
+    outs = torch.zeros((T * k, H), dtype=torch.float64)
+    for e in np.unique(ids):
+        Wg = torch.from_numpy(dequant_np(fmt, w["gate_codes"][e], w["gate_scales"][e]))
+        Wu = torch.from_numpy(dequant_np(fmt, w["up_codes"][e], w["up_scales"][e]))
+        Wd = torch.from_numpy(dequant_np(fmt, w["down_codes"][e], w["down_scales"][e]))
+        tok, slot = np.nonzero(ids == e)
+        xe = x[torch.from_numpy(tok)]
+        a = torch.nn.functional.silu(xe @ Wg.T) * (xe @ Wu.T)
+        o = a @ Wd.T
+        outs[torch.from_numpy(tok * k + slot)] = o
+    for j in range(k):
+        y += torch.from_numpy(rw[:, j:j + 1]) * outs[j::k]
+    return y.numpy(), ids, rw, outs.numpy()
+
+
+def small_shape(fmt=2, T=16, H=256, E=64, k=4, I=128, zipf=False):
+    return mi.Shape("t", T=T, H=H, E=E, k=k, I=I, fmt=fmt, zipf=zipf)
+
+
+@pytest.mark.parametrize("shape", [mi.TINY, small_shape(fmt=3, zipf=True, T=24),
+                                   small_shape(T=5, H=128, E=7, k=3, I=128)])
+def test_layer_matches_independent_float64(oracle_lib, shape):
+    w = mi.make_weights(shape, seed=0)
+    x = mi.make_x(shape)
+    logits = mi.make_logits(shape)
+    y, ids, rw, out, a = oracle.layer(w, x, logits, shape.k, intermediates=True)
+    yi, idsi, rwi, outi = independent_layer(w, x, logits, shape.k)
+    assert np.array_equal(ids, idsi)
+    np.testing.assert_allclose(rw, rwi, rtol=1e-13)
+    np.testing.assert_allclose(out, outi, rtol=1e-11, atol=1e-12 * np.abs(outi).max())
+    np.testing.assert_allclose(y, yi, rtol=1e-11, atol=1e-12 * np.abs(yi).max())
+    assert np.all(np.linalg.norm(y, axis=1) > 0)
+
+
+def test_single_expert_top1_is_plain_swiglu(oracle_lib):
+    shape = small_shape(T=6, H=256, E=1, k=1, I=128)
+    w = mi.make_weights(shape, seed=3)
+    x = mi.make_x(shape, seed=3)
+    logits = mi.make_logits(shape, seed=3)
+    y = oracle.layer(w, x, logits, 1)
+    Wg = dequant_np(2, w["gate_codes"][0], w["gate_scales"][0])
+    Wu = dequant_np(2, w["up_codes"][0], w["up_scales"][0])
+    Wd = dequant_np(2, w["down_codes"][0], w["down_scales"][0])
+    xf = torch.from_numpy(mi.bf16_bits_to_f32(x).astype(np.float64))
+    ref = (torch.nn.functional.silu(xf @ torch.from_numpy(Wg).T) * (xf @ torch.from_numpy(Wu).T)) \
+        @ torch.from_numpy(Wd).T
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_expert_ffn_matches_layer_slot(oracle_lib):
+    shape = mi.TINY
+    w = mi.make_weights(shape)
+    x = mi.make_x(shape)
+    logits = mi.make_logits(shape)
+    y, ids, rw, out, a = oracle.layer(w, x, logits, shape.k, intermediates=True)
+    for t, j in [(0, 0), (5, 3), (15, 2)]:
+        o, aa = oracle.expert_ffn(w, int(ids[t, j]), x[t])
+        assert np.array_equal(o, out[t * shape.k + j])
+        assert np.array_equal(aa, a[t * shape.k + j])
+
+
+def test_combine_identities(oracle_lib):
+    shape = small_shape(T=8, E=16, k=1)
+    w = mi.make_weights(shape)
+    x = mi.make_x(shape)
+    logits = mi.make_logits(shape)
+    y, ids, rw, out, a = oracle.layer(w, x, logits, 1, intermediates=True)
+    assert np.all(rw == 1.0)
+    assert np.array_equal(y, out)
+    # doubling every down-projection scale doubles the output exactly
+    w2 = dict(w)
+    w2["down_scales"] = (f16_values(w["down_scales"]) * 2).astype(np.float16).view(np.uint16)
+    shape4 = small_shape(T=8, E=16, k=4)
+    y4 = oracle.layer(w, x, mi.make_logits(shape4), 4)
+    y4d = oracle.layer(w2, x, mi.make_logits(shape4), 4)
+    assert np.array_equal(y4d, 2 * y4)
+
+
+def test_token_permutation_equivariance(oracle_lib):
+    shape = mi.TINY
+    w = mi.make_weights(shape)
+    x = mi.make_x(shape)
+    logits = mi.make_logits(shape)
+    y = oracle.layer(w, x, logits, shape.k)
+    perm = np.random.default_rng(5).permutation(shape.T)
+    yp = oracle.layer(w, x[perm], logits[perm], shape.k)
+    assert np.array_equal(yp, y[perm])
+    rows = [3, 0, 15, 3]
+    assert np.array_equal(oracle.layer_rows(w, x, logits, shape.k, rows), y[rows])
+
+
+def test_expert_relabelling_invariance(oracle_lib):
+    shape = mi.TINY
+    w = mi.make_weights(shape)
+    x = mi.make_x(shape)
+    logits = mi.make_logits(shape)
+    y = oracle.layer(w, x, logits, shape.k)
+    for t in range(shape.T):
+        assert len(np.unique(logits[t])) == shape.E  # no ties, so relabelling keeps the order
+    perm = np.random.default_rng(11).permutation(shape.E)  # new expert p holds old expert perm[p]
+    w2 = dict(w)
+    for name in ("gate_codes", "up_codes", "down_codes", "gate_scales", "up_scales", "down_scales"):
+        w2[name] = np.ascontiguousarray(w[name][perm])
+    y2 = oracle.layer(w2, x, np.ascontiguousarray(logits[:, perm]), shape.k)
+    assert np.array_equal(y2, y)
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm
+
+
+def test_rmsnorm_special_rows(oracle_lib):
+    H = 256
+    h = np.zeros((4, H), dtype=np.float32)
+    h[0] = 1.0                                    # -> 1/sqrt(1 + eps) rounds to 1.0 in bf16
+    h[1] = np.where(np.arange(H) % 2 == 0, 3.0, -3.0)  # -> +-1
+    h[2, 0] = 16.0                                # one spike: mean = 1 -> 16/sqrt(1+eps) -> 16
+    h[3] = 0.0                                    # all zero -> 0 / sqrt(eps) = 0
+    x = mi.bf16_bits_to_f32(oracle.rmsnorm(h, 1e-6))
+    assert np.all(x[0] == 1.0)
+    assert np.array_equal(x[1], np.where(np.arange(H) % 2 == 0, 1.0, -1.0).astype(np.float32))
+    assert x[2, 0] == 16.0 and np.all(x[2, 1:] == 0)
+    assert np.all(x[3] == 0)
+
+
+def test_rmsnorm_unit_rms_and_scale_invariance(oracle_lib):
+    rng = np.random.default_rng(2)
+    h = (rng.standard_normal((8, 3072)) * 7).astype(np.float32)
+    x = mi.bf16_bits_to_f32(oracle.rmsnorm(h, 1e-6)).astype(np.float64)
+    rms = np.sqrt((x ** 2).mean(axis=1))
+    assert np.all(np.abs(rms - 1) < 4e-3)  # bf16 rounding of each element
+    x2 = oracle.rmsnorm(h * np.float32(4.0), 1e-6)  # scaling by 4 is exact; eps effect < 1 ulp
+    assert np.mean(x2 == oracle.rmsnorm(h, 1e-6)) > 0.999
+
+
+# ---------------------------------------------------------------------------------------------
+# Golden regression values (written by tests/golden/make_golden.py from the oracle only)
+
+
+def test_golden_tiny_layer(oracle_lib):
+    path = os.path.join(GOLDEN, "tiny_layer.txt")
+    rows = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            key, *vals = line.split()
+            rows[key] = vals
+    shape = mi.TINY
+    y, ids, rw, out, a = oracle.layer(mi.make_weights(shape), mi.make_x(shape),
+                                      mi.make_logits(shape), shape.k, intermediates=True)
+    assert ids.reshape(-1).tolist() == [int(v) for v in rows["ids"]]
+    np.testing.assert_allclose(y[:, :8].reshape(-1), [float.fromhex(v) for v in rows["y_head"]],
+                               rtol=0, atol=0)
+    np.testing.assert_allclose(y.sum(axis=1), [float.fromhex(v) for v in rows["y_rowsum"]],
+                               rtol=1e-15)
+
+
+def test_pages_shape_facts():
+    facts = {}
+    with open(os.path.join(GOLDEN, "pages_shapes.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                facts[k] = int(v)
+    assert facts["experts_per_layer"] * facts["layers"] == facts["experts_total"]
+    for s in (mi.DECODE, mi.PREFILL, mi.SKEWED):
+        assert s.E == facts["experts_per_layer"] and s.k == facts["active_per_token"]
+    assert mi.DECODE.T == 1 + facts["mtp_drafts"]
+    assert mi.PREFILL.T == facts["max_prefill_chunk"]
+    assert mi.STACK_PREFILL.layers == facts["layers"]
