@@ -1,0 +1,193 @@
+"""Python binding of libstrata_moe.so, the MI355X routed-MoE expert layer.
+
+Argument marshalling only: every function below calls the C ABI entry point of the same name
+(declared in include/strata_moe.h) with device pointers taken from torch tensors and torch's
+current HIP stream.  All arithmetic runs in the library's gfx950 kernels.  There is no fallback:
+if the library is missing or was not built, import-time use raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstrata_moe.so")
+
+STRATA_OK, STRATA_ERR_INVALID_ARGUMENT, STRATA_ERR_UNSUPPORTED = 0, 1, 2
+STRATA_ERR_WORKSPACE_TOO_SMALL, STRATA_ERR_HIP = 3, 4
+Q2, Q3 = 2, 3
+CODE_BYTES = {Q2: 8, Q3: 12}
+
+EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "strata_moe_combine",
+           "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm",
+           "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
+           "strata_status_string"]
+
+
+class StrataError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("gate_codes", ctypes.c_void_p), ("up_codes", ctypes.c_void_p),
+                ("down_codes", ctypes.c_void_p), ("gate_scales", ctypes.c_void_p),
+                ("up_scales", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        W = ctypes.POINTER(CWeights)
+        sig = {
+            "strata_moe_route": [vp, i32, i32, i32, vp, vp, vp],
+            "strata_moe_permute": [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
+            "strata_moe_expert_ffn": [W, vp, i32, i32, vp, vp, vp, vp, sz, vp],
+            "strata_moe_combine": [vp, vp, i32, i32, i32, vp, i32, vp],
+            "strata_moe_decode": [W, vp, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp],
+            "strata_moe_layer": [W, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "strata_moe_rmsnorm": [vp, i32, i32, ctypes.c_float, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.strata_moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
+        L.strata_moe_permute_workspace_bytes.restype = sz
+        L.strata_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.strata_moe_workspace_bytes.restype = sz
+        L.strata_status_string.argtypes = [ctypes.c_int]
+        L.strata_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != STRATA_OK:
+        raise StrataError(fn, status, lib().strata_status_string(status).decode())
+
+
+def _p(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+@dataclass
+class Weights:
+    """One layer's packed expert weights as device tensors (see include/strata_moe.h)."""
+    fmt: int
+    E: int
+    H: int
+    I: int
+    gate_codes: torch.Tensor
+    up_codes: torch.Tensor
+    down_codes: torch.Tensor
+    gate_scales: torch.Tensor
+    up_scales: torch.Tensor
+    down_scales: torch.Tensor
+
+    def c_struct(self) -> CWeights:
+        return CWeights(self.fmt, self.E, self.H, self.I, _p(self.gate_codes), _p(self.up_codes),
+                        _p(self.down_codes), _p(self.gate_scales), _p(self.up_scales),
+                        _p(self.down_scales))
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.gate_codes, self.up_codes,
+                                                          self.down_codes, self.gate_scales,
+                                                          self.up_scales, self.down_scales))
+
+    @staticmethod
+    def from_numpy(w: dict, device="cuda") -> "Weights":
+        def t(a):
+            return torch.from_numpy(a).to(device)
+        return Weights(w["fmt"], w["E"], w["H"], w["I"], t(w["gate_codes"]), t(w["up_codes"]),
+                       t(w["down_codes"]), t(w["gate_scales"].view("int16")),
+                       t(w["up_scales"].view("int16")), t(w["down_scales"].view("int16")))
+
+
+def permute_workspace_bytes(T: int, E: int, k: int) -> int:
+    return lib().strata_moe_permute_workspace_bytes(T, E, k)
+
+
+def workspace_bytes(T: int, E: int, k: int, H: int, I: int) -> int:
+    return lib().strata_moe_workspace_bytes(T, E, k, H, I)
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def strata_moe_route(logits, k, topk_ids, topk_w, stream=None) -> None:
+    T, E = logits.shape
+    _check("strata_moe_route", lib().strata_moe_route(_p(logits), T, E, k, _p(topk_ids), _p(topk_w),
+                                                      _stream(stream)))
+
+
+def strata_moe_permute(topk_ids, E, counts, offsets, sorted_slot, slot_pos, workspace,
+                       stream=None) -> None:
+    T, k = topk_ids.shape
+    _check("strata_moe_permute", lib().strata_moe_permute(
+        _p(topk_ids), T, E, k, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_pos),
+        _p(workspace), workspace.numel() if workspace is not None else 0, _stream(stream)))
+
+
+def strata_moe_expert_ffn(w: Weights, x, k, offsets, sorted_slot, expert_out, workspace,
+                          stream=None) -> None:
+    cw = w.c_struct()
+    _check("strata_moe_expert_ffn", lib().strata_moe_expert_ffn(
+        ctypes.byref(cw), _p(x), x.shape[0], k, _p(offsets), _p(sorted_slot), _p(expert_out),
+        _p(workspace), workspace.numel(), _stream(stream)))
+
+
+def strata_moe_combine(expert_out, topk_w, y, accumulate=False, stream=None) -> None:
+    T, k = topk_w.shape
+    _check("strata_moe_combine", lib().strata_moe_combine(
+        _p(expert_out), _p(topk_w), T, k, y.shape[1], _p(y), int(accumulate), _stream(stream)))
+
+
+def strata_moe_decode(w: Weights, x, logits, k, y, accumulate=False, topk_ids=None, topk_w=None,
+                      workspace=None, stream=None) -> None:
+    cw = w.c_struct()
+    _check("strata_moe_decode", lib().strata_moe_decode(
+        ctypes.byref(cw), _p(x), _p(logits), x.shape[0], k, _p(y), int(accumulate), _p(topk_ids),
+        _p(topk_w), _p(workspace), workspace.numel() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def strata_moe_layer(w: Weights, x, logits, k, y, accumulate=False, topk_ids=None, topk_w=None,
+                     counts=None, offsets=None, sorted_slot=None, workspace=None,
+                     stream=None) -> None:
+    cw = w.c_struct()
+    _check("strata_moe_layer", lib().strata_moe_layer(
+        ctypes.byref(cw), _p(x), _p(logits), x.shape[0], k, _p(y), int(accumulate), _p(topk_ids),
+        _p(topk_w), _p(counts), _p(offsets), _p(sorted_slot), _p(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
+
+
+def strata_moe_rmsnorm(h, x, eps=1e-6, stream=None) -> None:
+    T, H = h.shape
+    _check("strata_moe_rmsnorm", lib().strata_moe_rmsnorm(_p(h), T, H, eps, _p(x), _stream(stream)))

@@ -1,0 +1,310 @@
+// C ABI of the MoE expert layer: argument validation, workspace layout and kernel dispatch.
+// Every check runs before the first HIP call, so an error return means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "strata_moe.h"
+
+using strata::Chunk;
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+constexpr int kMaxDecodeT = 8;
+
+size_t round_up(size_t b) { return (b + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool shape_ok(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return false;
+  if ((int64_t)T * k > INT32_MAX / 2) return false;
+  return true;
+}
+
+strata_status check_route_shape(int32_t T, int32_t E, int32_t k) {
+  if (!shape_ok(T, E, k) || k > E) return STRATA_ERR_INVALID_ARGUMENT;
+  if (E > kMaxE || k > kMaxK) return STRATA_ERR_UNSUPPORTED;
+  return STRATA_OK;
+}
+
+strata_status check_weights(const strata_moe_weights* w) {
+  if (!w) return STRATA_ERR_INVALID_ARGUMENT;
+  if (w->fmt != STRATA_Q2_B32 && w->fmt != STRATA_Q3_B32) return STRATA_ERR_INVALID_ARGUMENT;
+  if (w->num_experts < 1 || w->hidden < 1 || w->inter < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if (w->hidden % 32 || w->inter % 32) return STRATA_ERR_INVALID_ARGUMENT;
+  if (w->num_experts > kMaxE) return STRATA_ERR_UNSUPPORTED;
+  if (w->hidden % 256 || w->inter % 128) return STRATA_ERR_UNSUPPORTED;
+  const void* ptrs[6] = {w->gate_codes, w->up_codes, w->down_codes,
+                         w->gate_scales, w->up_scales, w->down_scales};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  return STRATA_OK;
+}
+
+strata_status from_hip(hipError_t e) { return e == hipSuccess ? STRATA_OK : STRATA_ERR_HIP; }
+
+// Workspace of the prefill path, carved in this order (each piece 256-byte aligned).
+struct PrefillWs {
+  int* ids;
+  float* w;
+  int* counts;
+  int* offsets;
+  int* sorted_slot;
+  int* slot_pos;
+  int* tile_hist;
+  int* tile_base;
+  Chunk* chunks;
+  int* n_chunks;
+  uint16_t* x16;
+  uint16_t* a16;
+  uint16_t* expert_out;
+  size_t bytes;
+  int max_chunks;
+};
+
+PrefillWs carve_prefill(void* base, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+  PrefillWs p{};
+  const size_t S = (size_t)T * k;
+  const size_t ntiles = (S + strata::kPermTile - 1) / strata::kPermTile;
+  p.max_chunks = (int)strata::max_chunks((int64_t)S, E);
+  uint8_t* c = static_cast<uint8_t*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* r = c ? c + off : nullptr;
+    off += round_up(bytes);
+    return r;
+  };
+  p.ids = static_cast<int*>(take(S * 4));
+  p.w = static_cast<float*>(take(S * 4));
+  p.counts = static_cast<int*>(take((size_t)E * 4));
+  p.offsets = static_cast<int*>(take((size_t)(E + 1) * 4));
+  p.sorted_slot = static_cast<int*>(take(S * 4));
+  p.slot_pos = static_cast<int*>(take(S * 4));
+  p.tile_hist = static_cast<int*>(take(ntiles * E * 4));
+  p.tile_base = static_cast<int*>(take(ntiles * E * 4));
+  p.chunks = static_cast<Chunk*>(take((size_t)p.max_chunks * sizeof(Chunk)));
+  p.n_chunks = static_cast<int*>(take(16));
+  p.x16 = static_cast<uint16_t*>(take((size_t)T * H * 2));
+  p.a16 = static_cast<uint16_t*>(take(S * I * 2));
+  p.expert_out = static_cast<uint16_t*>(take(S * H * 2));
+  p.bytes = off;
+  return p;
+}
+
+__global__ void chunks_from_offsets_kernel(const int* offsets, int E, Chunk* chunks, int* n_chunks) {
+  // one workgroup of 1024 threads, thread e = expert (E <= 1024)
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int nfrag = (cnt + 31) / 32;
+  const int per = strata::kChunkRows / 32;
+  const int nch = (nfrag + per - 1) / per;
+  const int lane = e & 63, wv = e >> 6;
+  int inc = nch;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < 16; ++i) {
+    if (i < wv) base += wsum[i];
+    tot += wsum[i];
+  }
+  base += inc - nch;
+  if (e < E && nch > 0) {
+    const int fb = nfrag / nch, extra = nfrag % nch;
+    int row = offsets[e], used = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int nf = fb + (c < extra ? 1 : 0);
+      const int rows = min(nf * 32, cnt - used * 32);
+      chunks[base + c] = Chunk{e, row, rows, 0};
+      row += rows;
+      used += nf;
+    }
+  }
+  if (e == 0) *n_chunks = tot;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* strata_status_string(strata_status st) {
+  switch (st) {
+    case STRATA_OK: return "ok";
+    case STRATA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case STRATA_ERR_UNSUPPORTED: return "unsupported shape";
+    case STRATA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case STRATA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k) {
+  if (!shape_ok(T, E, k)) return 0;
+  const size_t S = (size_t)T * k;
+  const size_t ntiles = (S + strata::kPermTile - 1) / strata::kPermTile;
+  return 2 * round_up(ntiles * E * 4);
+}
+
+size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+  if (!shape_ok(T, E, k) || H < 1 || I < 1) return 0;
+  const size_t pre = carve_prefill(nullptr, T, E, k, H, I).bytes;
+  const size_t dec = T <= kMaxDecodeT ? strata::decode_workspace_bytes(T, E, k, H, I) : 0;
+  return pre > dec ? pre : dec;
+}
+
+strata_status strata_moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                               int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  strata_status st = check_route_shape(T, E, k);
+  if (st != STRATA_OK) return st;
+  if (T == 0) return STRATA_OK;
+  if (!logits || !topk_ids || !topk_w) return STRATA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_route(logits, T, E, k, topk_ids, topk_w, stream));
+}
+
+strata_status strata_moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                 int32_t* slot_pos, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  strata_status st = check_route_shape(T, E, k);
+  if (st != STRATA_OK) return st;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[6] = {topk_ids, counts, offsets, sorted_slot, slot_pos, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  const size_t need = strata_moe_permute_workspace_bytes(T, E, k);
+  if (workspace_bytes < need) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t S = (size_t)T * k;
+  const size_t ntiles = (S + strata::kPermTile - 1) / strata::kPermTile;
+  int* hist = static_cast<int*>(workspace);
+  int* base = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + round_up(ntiles * E * 4));
+  return from_hip(strata::launch_permute(topk_ids, T, E, k, counts, offsets, sorted_slot, slot_pos,
+                                         hist, base, nullptr, nullptr, stream));
+}
+
+strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t* x, int32_t T,
+                                    int32_t k, const int32_t* offsets, const int32_t* sorted_slot,
+                                    uint16_t* expert_out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  st = check_route_shape(T, w->num_experts, k);
+  if (st != STRATA_OK) return st;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[5] = {x, offsets, sorted_slot, expert_out, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  PrefillWs p = carve_prefill(workspace, T, E, k, H, I);
+  chunks_from_offsets_kernel<<<1, 1024, 0, stream>>>(offsets, E, p.chunks, p.n_chunks);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, stream);
+  if (e == hipSuccess)
+    e = strata::launch_ffn_up(w->fmt, p.x16, sorted_slot, k, p.chunks, p.n_chunks, p.max_chunks,
+                              w->gate_codes, w->up_codes, w->gate_scales, w->up_scales, E, H, I,
+                              p.a16, stream);
+  if (e == hipSuccess)
+    e = strata::launch_ffn_down(w->fmt, p.a16, sorted_slot, p.chunks, p.n_chunks, p.max_chunks,
+                                w->down_codes, w->down_scales, E, H, I, expert_out, stream);
+  return from_hip(e);
+}
+
+strata_status strata_moe_combine(const uint16_t* expert_out, const float* topk_w, int32_t T,
+                                 int32_t k, int32_t H, float* y, int32_t accumulate,
+                                 hipStream_t stream) {
+  if (T < 0 || k < 1 || H < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)T * k > INT32_MAX / 2) return STRATA_ERR_INVALID_ARGUMENT;
+  if (H % 8) return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  if (!expert_out || !topk_w || !y) return STRATA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(expert_out) || !aligned16(topk_w) || !aligned16(y)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_combine(expert_out, topk_w, T, k, H, y, accumulate, stream));
+}
+
+strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x, const float* logits,
+                                int32_t T, int32_t k, float* y, int32_t accumulate,
+                                int32_t* opt_topk_ids, float* opt_topk_w, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  st = check_route_shape(T, w->num_experts, k);
+  if (st != STRATA_OK) return st;
+  if (T > kMaxDecodeT) return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[4] = {x, logits, y, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  if ((opt_topk_ids && !aligned16(opt_topk_ids)) || (opt_topk_w && !aligned16(opt_topk_w)))
+    return STRATA_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(strata::launch_decode(w->fmt, x, logits, T, E, k, H, I, w->gate_codes, w->up_codes,
+                                        w->down_codes, w->gate_scales, w->up_scales, w->down_scales,
+                                        y, accumulate, opt_topk_ids, opt_topk_w, workspace, stream));
+}
+
+strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, const float* logits,
+                               int32_t T, int32_t k, float* y, int32_t accumulate,
+                               int32_t* opt_topk_ids, float* opt_topk_w, int32_t* opt_counts,
+                               int32_t* opt_offsets, int32_t* opt_sorted_slot, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  st = check_route_shape(T, w->num_experts, k);
+  if (st != STRATA_OK) return st;
+  if (T <= kMaxDecodeT && (opt_counts || opt_offsets || opt_sorted_slot))
+    return STRATA_ERR_INVALID_ARGUMENT;
+  if (T == 0) return STRATA_OK;
+  if (T <= kMaxDecodeT)
+    return strata_moe_decode(w, x, logits, T, k, y, accumulate, opt_topk_ids, opt_topk_w, workspace,
+                             workspace_bytes, stream);
+  const void* ptrs[4] = {x, logits, y, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  const void* opts[5] = {opt_topk_ids, opt_topk_w, opt_counts, opt_offsets, opt_sorted_slot};
+  for (const void* p : opts)
+    if (p && !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  PrefillWs p = carve_prefill(workspace, T, E, k, H, I);
+  int* ids = opt_topk_ids ? opt_topk_ids : p.ids;
+  float* rw = opt_topk_w ? opt_topk_w : p.w;
+  int* counts = opt_counts ? opt_counts : p.counts;
+  int* offsets = opt_offsets ? opt_offsets : p.offsets;
+  int* sorted = opt_sorted_slot ? opt_sorted_slot : p.sorted_slot;
+  hipError_t e = strata::launch_route(logits, T, E, k, ids, rw, stream);
+  if (e == hipSuccess)
+    e = strata::launch_permute(ids, T, E, k, counts, offsets, sorted, p.slot_pos, p.tile_hist,
+                               p.tile_base, p.chunks, p.n_chunks, stream);
+  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, stream);
+  if (e == hipSuccess)
+    e = strata::launch_ffn_up(w->fmt, p.x16, sorted, k, p.chunks, p.n_chunks, p.max_chunks,
+                              w->gate_codes, w->up_codes, w->gate_scales, w->up_scales, E, H, I,
+                              p.a16, stream);
+  if (e == hipSuccess)
+    e = strata::launch_ffn_down(w->fmt, p.a16, sorted, p.chunks, p.n_chunks, p.max_chunks,
+                                w->down_codes, w->down_scales, E, H, I, p.expert_out, stream);
+  if (e == hipSuccess) e = strata::launch_combine(p.expert_out, rw, T, k, H, y, accumulate, stream);
+  return from_hip(e);
+}
+
+strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
+                                 hipStream_t stream) {
+  if (T < 0 || H < 1 || !(eps >= 0.0f)) return STRATA_ERR_INVALID_ARGUMENT;
+  if (H % 4) return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  if (!h || !x || !aligned16(h) || !aligned16(x)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_rmsnorm(h, T, H, eps, x, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Launchers of the gfx950 kernels (host side).  Arguments are validated by the C ABI layer
+// before any of these is called; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace strata {
+
+// Chunk of one expert's segment of the sorted slot order, processed by one GEMM work unit.
+struct Chunk {
+  int32_t expert;
+  int32_t row_start;  // first sorted position
+  int32_t nrows;      // 1..kChunkRows
+  int32_t pad;
+};
+
+constexpr int kChunkRows = 256;  // rows of one GEMM work unit (8 fragments of 32)
+constexpr int kPermTile = 1024;  // slots per permute tile
+
+// Upper bound of the number of chunks for S slots over E experts.
+inline int64_t max_chunks(int64_t S, int64_t E) {
+  return S / kChunkRows + (E < S ? E : S) + 1;
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+                        hipStream_t s);
+
+// Stable counting sort; also writes the GEMM chunk list (chunks, *n_chunks) when chunks != NULL.
+hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int* offsets,
+                          int* sorted_slot, int* slot_pos, int* tile_hist, int* tile_base,
+                          Chunk* chunks, int* n_chunks, hipStream_t s);
+
+// x bf16 [T][H] -> fp16 in the fragment order of the grouped GEMM (see prefill.hip).
+hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, hipStream_t s);
+
+hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k,
+                         const Chunk* chunks, const int* n_chunks, int max_chunks,
+                         const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
+                         const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
+                         hipStream_t s);
+
+hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot,
+                           const Chunk* chunks, const int* n_chunks, int max_chunks,
+                           const void* down_codes, const uint16_t* down_scales, int E, int H,
+                           int I, uint16_t* expert_out, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* expert_out, const float* w, int T, int k, int H,
+                          float* y, int accumulate, hipStream_t s);
+
+hipError_t launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, hipStream_t s);
+
+// Decode path (T <= 8).
+hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T, int E, int k,
+                         int H, int I, const void* gate_codes, const void* up_codes,
+                         const void* down_codes, const uint16_t* gate_scales,
+                         const uint16_t* up_scales, const uint16_t* down_scales, float* y,
+                         int accumulate, int* ids, float* w, void* ws, hipStream_t s);
+size_t decode_workspace_bytes(int T, int E, int k, int H, int I);
+
+}  // namespace strata

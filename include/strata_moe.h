@@ -84,7 +84,7 @@ typedef enum {
 typedef struct strata_moe_weights {
   int32_t fmt;          /* strata_qformat */
   int32_t num_experts;  /* E: 1..1024 */
-  int32_t hidden;       /* H: multiple of 128 */
+  int32_t hidden;       /* H: multiple of 256 */
   int32_t inter;        /* I: multiple of 128 */
   const void* gate_codes;
   const void* up_codes;
@@ -144,7 +144,7 @@ strata_status strata_moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, 
  *   offsets, sorted_slot  as produced by strata_moe_permute for this (T, k, E)
  *   expert_out  bf16 [T*k][H], row s = slot s (unweighted expert output), written
  * Workspace: at least strata_moe_workspace_bytes(T, E, k, H, I).
- * Limits: w->hidden and w->inter multiples of 128; E, k as strata_moe_route.
+ * Limits: w->hidden a multiple of 256, w->inter a multiple of 128; E, k as strata_moe_route.
  */
 strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t* x, int32_t T,
                                     int32_t k, const int32_t* offsets,
@@ -192,7 +192,7 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
 
 /*
  * RMSNorm for a layer stack: x[t] = bf16_RNE(h[t] / sqrt(mean_i h[t][i]^2 + eps)), unit gain.
- *   h fp32 [T][H] (read), x bf16 [T][H] (written).  H a multiple of 128.
+ *   h fp32 [T][H] (read), x bf16 [T][H] (written).  H a multiple of 4.
  */
 strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
                                  hipStream_t stream);

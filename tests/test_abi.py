@@ -1,0 +1,117 @@
+"""The C ABI on the host: the library loads, exports every entry point the header declares, and
+rejects bad arguments with the documented status before touching the GPU (no compute call is
+made here: every call below fails validation or is the T = 0 no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_expert_ffn_fp32_amd as sm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "strata_moe.h")
+
+OK, INVAL, UNSUP, WS = 0, 1, 2, 3
+A = 0x10000      # a 16-byte aligned stand-in address (never dereferenced: validation fails first)
+MIS = 0x10004    # misaligned stand-in
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sm.LIB_PATH):
+        pytest.skip("libstrata_moe.so not built")
+    return sm.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(strata_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert "strata_moe_layer" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(sm.EXPORTS) == names
+
+
+def weights(fmt=2, E=512, H=3072, I=768, ptr=A):
+    return sm.CWeights(fmt, E, H, I, ptr, ptr, ptr, ptr, ptr, ptr)
+
+
+def test_status_strings(L):
+    for st, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape"),
+                     (3, b"workspace too small"), (4, b"HIP launch error"), (99, b"unknown status")]:
+        assert L.strata_status_string(st) == text
+
+
+def test_route_validation(L):
+    assert L.strata_moe_route(A, 4, 8, 9, A, A, None) == INVAL        # k > E
+    assert L.strata_moe_route(A, 4, 512, 0, A, A, None) == INVAL      # k = 0
+    assert L.strata_moe_route(A, -1, 512, 10, A, A, None) == INVAL    # T < 0
+    assert L.strata_moe_route(A, 4, 2048, 10, A, A, None) == UNSUP    # E > 1024
+    assert L.strata_moe_route(A, 4, 512, 17, A, A, None) == UNSUP     # k > 16
+    assert L.strata_moe_route(None, 4, 512, 10, A, A, None) == INVAL  # null
+    assert L.strata_moe_route(MIS, 4, 512, 10, A, A, None) == INVAL   # misaligned
+    assert L.strata_moe_route(None, 0, 512, 10, None, None, None) == OK  # T = 0: no-op
+
+
+def test_permute_validation(L):
+    need = L.strata_moe_permute_workspace_bytes(8192, 512, 10)
+    assert need >= 2 * 80 * 512 * 4
+    assert L.strata_moe_permute(A, 8192, 512, 10, A, A, A, A, A, need - 1, None) == WS
+    assert L.strata_moe_permute(A, 8192, 512, 10, A, A, None, A, A, need, None) == INVAL
+    assert L.strata_moe_permute(A, 8192, 512, 10, A, MIS, A, A, A, need, None) == INVAL
+    assert L.strata_moe_permute(A, 10, 4, 5, A, A, A, A, A, need, None) == INVAL
+
+
+def test_weights_validation(L):
+    ws = L.strata_moe_workspace_bytes(8192, 512, 10, 3072, 768)
+    call = lambda w, T=8192, k=10, wsb=ws: L.strata_moe_layer(
+        ctypes.byref(w), A, A, T, k, A, 0, None, None, None, None, None, A, wsb, None)
+    assert call(weights(fmt=4)) == INVAL
+    assert call(weights(H=3000)) == INVAL          # not a multiple of 32
+    assert call(weights(H=3072 + 128)) == UNSUP    # multiple of 32 but not of 256
+    assert call(weights(I=800)) == UNSUP           # not a multiple of 128
+    assert call(weights(E=2000)) == UNSUP
+    assert call(weights(ptr=MIS)) == INVAL
+    assert call(weights(ptr=0)) == INVAL
+    assert call(weights(), k=0) == INVAL
+    assert call(weights(), wsb=ws - 1) == WS
+    assert L.strata_moe_layer(None, A, A, 16, 4, A, 0, None, None, None, None, None, A, ws, None) == INVAL
+    # decode path: permutation outputs are not produced for T <= 8
+    assert L.strata_moe_layer(ctypes.byref(weights()), A, A, 4, 10, A, 0, None, None, A, None, None,
+                              A, ws, None) == INVAL
+    assert L.strata_moe_decode(ctypes.byref(weights()), A, A, 9, 10, A, 0, None, None, A, ws,
+                               None) == UNSUP
+    assert L.strata_moe_expert_ffn(ctypes.byref(weights()), A, 8192, 10, A, A, A, A, ws - 1,
+                                   None) == WS
+
+
+def test_combine_and_rmsnorm_validation(L):
+    assert L.strata_moe_combine(A, A, 4, 10, 3072, None, 0, None) == INVAL
+    assert L.strata_moe_combine(A, A, 4, 10, 3071, A, 0, None) == UNSUP
+    assert L.strata_moe_combine(A, A, 0, 10, 3072, A, 0, None) == OK
+    assert L.strata_moe_rmsnorm(A, 4, 3072, ctypes.c_float(-1.0), A, None) == INVAL
+    assert L.strata_moe_rmsnorm(A, 4, 3071, ctypes.c_float(1e-6), A, None) == UNSUP
+    assert L.strata_moe_rmsnorm(MIS, 4, 3072, ctypes.c_float(1e-6), A, None) == INVAL
+
+
+def test_workspace_sizes(L):
+    assert L.strata_moe_workspace_bytes(-1, 512, 10, 3072, 768) == 0
+    small = L.strata_moe_workspace_bytes(16, 64, 4, 256, 128)
+    big = L.strata_moe_workspace_bytes(8192, 512, 10, 3072, 768)
+    assert 0 < small < big
+    # prefill: intermediate a (S x I fp16) and expert outputs (S x H bf16) dominate
+    S = 8192 * 10
+    assert big >= S * 768 * 2 + S * 3072 * 2 + 8192 * 3072 * 2
+
+
+def test_python_binding_raises():
+    if not os.path.exists(sm.LIB_PATH):
+        pytest.skip("libstrata_moe.so not built")
+    with pytest.raises(sm.StrataError) as ei:
+        sm._check("strata_moe_route", INVAL)
+    assert ei.value.status == INVAL

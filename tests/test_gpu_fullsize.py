@@ -1,0 +1,104 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+* decode:  T=4,    H=3072, E=512, k=10, I=768, 2-bit: every output row against the oracle.
+* prefill: T=8192, same dims: routing, counts, offsets and permutation bit-exact over all 81,920
+           slots; layer output rows on a seeded sample of tokens (the oracle computes those rows
+           one by one; tokens are independent in the layer).
+* skewed:  T=2048, 3-bit, Zipf-biased routing: same checks.
+* stack:   two layers of h <- h + MoE(RMSNorm(h)) at the prefill shape, each layer checked
+           teacher-forced (the oracle gets the GPU's h and x of that layer).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_expert_ffn_fp32_amd as sm
+import moe_inputs as mi
+import oracle
+from gpu_helpers import TOL_REL_L2, Layer, dev, rel_l2_rows, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False):
+    s, T = L.shape, L.T
+    S = T * s.k
+    x = L.x if x is None else x
+    logits = L.logits if logits is None else logits
+    y = torch.empty((T, s.H), dtype=torch.float32, device=dev()) if y is None else y
+    ids = torch.empty((T, s.k), dtype=torch.int32, device=dev())
+    rw = torch.empty((T, s.k), dtype=torch.float32, device=dev())
+    extra = {}
+    if T > 8:
+        extra = dict(counts=torch.empty(s.E, dtype=torch.int32, device=dev()),
+                     offsets=torch.empty(s.E + 1, dtype=torch.int32, device=dev()),
+                     sorted_slot=torch.empty(S, dtype=torch.int32, device=dev()))
+    sm.strata_moe_layer(L.w, x, logits, s.k, y, accumulate=accumulate, topk_ids=ids, topk_w=rw,
+                        workspace=L.workspace(), **extra)
+    torch.cuda.synchronize()
+    return y, ids, rw, extra
+
+
+def test_decode_full_size():
+    log("decode full size: generating")
+    L = Layer(mi.DECODE)
+    y, ids, rw, _ = run_layer(L)
+    y_ref, ids_ref, w_ref, _, _ = oracle.layer(L.w_np, L.x_np, L.l_np, 10, intermediates=True)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    err = rel_l2_rows(y.cpu().numpy(), y_ref)
+    log(f"decode full size max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL_REL_L2
+
+
+@pytest.mark.parametrize("name,n_rows", [("prefill", 12), ("skewed", 12)])
+def test_prefill_full_size(name, n_rows):
+    s = mi.SHAPES[name]
+    log(f"{name} full size: generating")
+    L = Layer(s)
+    y, ids, rw, extra = run_layer(L)
+    ids_ref, w_ref = oracle.route(L.l_np, s.k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(rw.cpu().numpy(), w_ref, rtol=1e-6)
+    counts, offsets, ss, _ = oracle.permute(ids_ref, s.E)
+    assert np.array_equal(extra["counts"].cpu().numpy(), counts)
+    assert np.array_equal(extra["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(extra["sorted_slot"].cpu().numpy(), ss)
+    rows = np.random.default_rng(2024).choice(s.T, size=n_rows, replace=False)
+    if name == "skewed":  # include tokens of the hottest experts and of the coldest touched one
+        hot = int(np.argmax(counts))
+        cold = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+        rows = np.concatenate([rows, np.nonzero((ids_ref == hot).any(axis=1))[0][:2],
+                               np.nonzero((ids_ref == cold).any(axis=1))[0][:2]])
+    y_ref = oracle.layer_rows(L.w_np, L.x_np, L.l_np, s.k, rows)
+    err = rel_l2_rows(y.cpu().numpy()[rows], y_ref)
+    log(f"{name} full size: sampled rows {len(rows)}, max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL_REL_L2
+    y2, _, _, _ = run_layer(L)
+    assert torch.equal(y, y2), "second call differs"
+
+
+def test_stack_two_layers_teacher_forced():
+    s = mi.PREFILL
+    h = to_dev(mi.make_h0(s))
+    x = torch.empty((s.T, s.H), dtype=torch.int16, device=dev())
+    rows = np.random.default_rng(7).choice(s.T, size=6, replace=False)
+    for layer in range(2):
+        log(f"stack layer {layer}: generating")
+        L = Layer(s, layer=layer)
+        h_in = h.cpu().numpy()
+        sm.strata_moe_rmsnorm(h, x, 1e-6)
+        torch.cuda.synchronize()
+        x_np = x.cpu().numpy().view(np.uint16)
+        x_ref = oracle.rmsnorm(h_in, 1e-6)
+        d = np.abs(x_np.astype(np.int32) - x_ref.astype(np.int32))
+        assert d.max() <= 1 and np.mean(d == 0) > 0.999
+        run_layer(L, x=x, y=h, accumulate=True)
+        y_rows = h.cpu().numpy()[rows] - h_in[rows]
+        y_ref = oracle.layer_rows(L.w_np, x_np, L.l_np, s.k, rows)  # teacher-forced on the GPU's x
+        err = rel_l2_rows(y_rows, y_ref)
+        log(f"stack layer {layer}: max rel-L2 {err.max():.3e}")
+        assert err.max() <= TOL_REL_L2

@@ -1,0 +1,253 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: routing ids, counts, offsets and the permutation bit-exact; router weights within 1e-6
+relative; expert outputs and layer outputs within 5e-3 per-row relative L2 against the fp64
+oracle.  Inputs come from the seeded generator shared with the oracle's tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_expert_ffn_fp32_amd as sm
+import moe_inputs as mi
+import oracle
+from gpu_helpers import TOL_REL_L2, Layer, bf16_tensor_to_f64, dev, rel_l2_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def shape(name="s", T=16, H=256, E=64, k=4, I=128, fmt=2, zipf=False):
+    return mi.Shape(name, T=T, H=H, E=E, k=k, I=I, fmt=fmt, zipf=zipf)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# Route
+
+
+def gpu_route(logits_np, k):
+    T, E = logits_np.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev())
+    w = torch.empty((T, k), dtype=torch.float32, device=dev())
+    sm.strata_moe_route(to_dev(logits_np), k, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k,kind", [
+    (16, 64, 4, "normal"), (4, 512, 10, "normal"), (8192, 512, 10, "normal"),
+    (2048, 512, 10, "zipf"), (333, 1024, 16, "normal"), (50, 5, 5, "normal"), (7, 1, 1, "normal"),
+    (257, 512, 10, "ties"), (64, 64, 8, "ties2"), (31, 200, 3, "signed_zero")])
+def test_route_bit_exact(T, E, k, kind):
+    log(f"route T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(T * 7 + E)
+    if kind == "normal":
+        logits = mi.normal_f32(0, 900 + E, T * E).reshape(T, E)
+    elif kind == "zipf":
+        logits = mi.make_logits(mi.SKEWED, T=T)
+    elif kind == "ties":
+        logits = (rng.integers(0, 6, size=(T, E)) * 0.25).astype(np.float32)
+    elif kind == "ties2":
+        logits = np.zeros((T, E), dtype=np.float32)
+        logits[::2, 5:] = 1.0
+    else:
+        logits = np.where(rng.random((T, E)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        logits[:, 17] = -1.0
+    ids, w = gpu_route(logits, k)
+    rids, rw = oracle.route(logits, k)
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=1e-6, atol=0)
+    assert np.all(np.abs(w.astype(np.float64).sum(axis=1) - 1) < 1e-6)
+
+
+# ---------------------------------------------------------------------------------------------
+# Permute
+
+
+def gpu_permute(ids_np, E):
+    T, k = ids_np.shape
+    S = T * k
+    ids = to_dev(ids_np.astype(np.int32))
+    counts = torch.empty(E, dtype=torch.int32, device=dev())
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev())
+    ss = torch.empty(S, dtype=torch.int32, device=dev())
+    sp = torch.empty(S, dtype=torch.int32, device=dev())
+    ws = sm.alloc_workspace(sm.permute_workspace_bytes(T, E, k), dev())
+    sm.strata_moe_permute(ids, E, counts, offsets, ss, sp, ws)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in (counts, offsets, ss, sp)]
+
+
+@pytest.mark.parametrize("T,E,k,kind", [
+    (16, 64, 4, "route"), (4, 512, 10, "route"), (8192, 512, 10, "route"), (2048, 512, 10, "zipf"),
+    (103, 7, 7, "route"), (1, 1024, 16, "route"), (5000, 3, 2, "route"), (3000, 1024, 1, "one"),
+    (4096, 512, 10, "hot")])
+def test_permute_bit_exact(T, E, k, kind):
+    log(f"permute T={T} E={E} k={k} {kind}")
+    if kind == "zipf":
+        ids, _ = oracle.route(mi.make_logits(mi.SKEWED, T=T), k)
+    elif kind == "one":
+        ids = np.full((T, 1), 77, dtype=np.int32)
+    elif kind == "hot":  # every token picks experts 0..9: ten segments of T rows each
+        ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    else:
+        ids, _ = oracle.route(mi.normal_f32(0, 77, T * E).reshape(T, E), k)
+    got = gpu_permute(ids, E)
+    want = oracle.permute(ids, E)
+    for g, r, name in zip(got, want, ("counts", "offsets", "sorted_slot", "slot_pos")):
+        assert np.array_equal(g, r), name
+
+
+def test_permute_twice_identical():
+    ids, _ = oracle.route(mi.normal_f32(0, 5, 8192 * 512).reshape(8192, 512), 10)
+    a = gpu_permute(ids, 512)
+    b = gpu_permute(ids, 512)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------------------------
+# Expert FFN (staged prefill path) and combine
+
+
+def staged(L: Layer, ids_np=None):
+    """route -> permute -> expert_ffn -> combine through the staged entry points."""
+    s, T = L.shape, L.T
+    S = T * s.k
+    ids = torch.empty((T, s.k), dtype=torch.int32, device=dev())
+    rw = torch.empty((T, s.k), dtype=torch.float32, device=dev())
+    sm.strata_moe_route(L.logits, s.k, ids, rw)
+    counts = torch.empty(s.E, dtype=torch.int32, device=dev())
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device=dev())
+    ss = torch.empty(S, dtype=torch.int32, device=dev())
+    sp = torch.empty(S, dtype=torch.int32, device=dev())
+    ws = L.workspace()
+    sm.strata_moe_permute(ids, s.E, counts, offsets, ss, sp, ws)
+    out = torch.empty((S, s.H), dtype=torch.int16, device=dev())
+    sm.strata_moe_expert_ffn(L.w, L.x, s.k, offsets, ss, out, ws)
+    y = torch.empty((T, s.H), dtype=torch.float32, device=dev())
+    sm.strata_moe_combine(out, rw, y)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), rw.cpu().numpy(), bf16_tensor_to_f64(out), y.cpu().numpy()
+
+
+SMALL_SHAPES = [
+    shape("tiny"),
+    shape("tiny_q3", fmt=3),
+    shape("ragged", T=77, H=512, E=16, k=3, I=256),          # chunks of ~14 rows, ragged fragments
+    shape("hot", T=300, H=256, E=4, k=2, I=128),             # 150 rows per expert: 5 fragments
+    shape("big_expert", T=700, H=256, E=2, k=1, I=128),      # 350 rows: 2 chunks
+    shape("q3_zipf", T=200, H=512, E=64, k=6, I=256, fmt=3, zipf=True),
+    shape("one_expert", T=9, H=256, E=1, k=1, I=128),
+]
+
+
+@pytest.mark.parametrize("s", SMALL_SHAPES, ids=lambda s: s.name)
+def test_staged_prefill_path(s):
+    log(f"staged {s}")
+    L = Layer(s)
+    y_ref, ids_ref, w_ref, out_ref, _ = oracle.layer(L.w_np, L.x_np, L.l_np, s.k, intermediates=True)
+    ids, rw, out, y = staged(L)
+    assert np.array_equal(ids, ids_ref)
+    np.testing.assert_allclose(rw, w_ref, rtol=1e-6)
+    e_out = rel_l2_rows(out, out_ref)
+    e_y = rel_l2_rows(y, y_ref)
+    log(f"  expert_out max rel-L2 {e_out.max():.3e}, y max rel-L2 {e_y.max():.3e}")
+    assert e_out.max() <= TOL_REL_L2
+    assert e_y.max() <= TOL_REL_L2
+
+
+def test_combine_against_oracle():
+    rng = np.random.default_rng(3)
+    T, k, H = 37, 5, 512
+    out_bits = mi.f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    y0 = rng.standard_normal((T, H)).astype(np.float32)
+    ref = oracle.combine(mi.bf16_bits_to_f32(out_bits).astype(np.float64), w.astype(np.float64), k)
+    out_d = torch.from_numpy(out_bits.view(np.int16)).to(dev())
+    y = to_dev(y0.copy())
+    sm.strata_moe_combine(out_d, to_dev(w), y, accumulate=False)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(y.cpu().numpy(), ref, rtol=1e-5, atol=1e-6)
+    y = to_dev(y0.copy())
+    sm.strata_moe_combine(out_d, to_dev(w), y, accumulate=True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(y.cpu().numpy(), ref + y0, rtol=1e-5, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------------------------
+# One-call layer: prefill and decode paths, determinism, accumulate
+
+
+def gpu_layer(L: Layer, accumulate=False, y0=None, want_ids=False):
+    s, T = L.shape, L.T
+    y = to_dev(y0.copy()) if y0 is not None else torch.empty((T, s.H), dtype=torch.float32, device=dev())
+    ids = torch.empty((T, s.k), dtype=torch.int32, device=dev())
+    rw = torch.empty((T, s.k), dtype=torch.float32, device=dev())
+    sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, accumulate=accumulate, topk_ids=ids, topk_w=rw,
+                        workspace=L.workspace())
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy(), rw.cpu().numpy()
+
+
+@pytest.mark.parametrize("s", SMALL_SHAPES + [shape("t9", T=9), shape("t8", T=8), shape("t1", T=1),
+                                              shape("t5_q3", T=5, fmt=3), shape("t3_e1", T=3, E=1, k=1)],
+                         ids=lambda s: s.name)
+def test_layer_against_oracle(s):
+    log(f"layer {s}")
+    L = Layer(s)
+    y_ref, ids_ref, w_ref, _, _ = oracle.layer(L.w_np, L.x_np, L.l_np, s.k, intermediates=True)
+    y, ids, rw = gpu_layer(L)
+    assert np.array_equal(ids, ids_ref)
+    err = rel_l2_rows(y, y_ref)
+    log(f"  y max rel-L2 {err.max():.3e} (T={s.T}, {'decode' if s.T <= 8 else 'prefill'} path)")
+    assert err.max() <= TOL_REL_L2
+    y2, _, _ = gpu_layer(L)
+    assert np.array_equal(y, y2), "second call differs"
+    y0 = np.random.default_rng(1).standard_normal((s.T, s.H)).astype(np.float32)
+    ya, _, _ = gpu_layer(L, accumulate=True, y0=y0)
+    np.testing.assert_allclose(ya, y0 + y, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 6, 8])
+def test_decode_matches_prefill_path(T):
+    s = shape("dp", T=T, H=512, E=32, k=4, I=256)
+    L = Layer(s)
+    y_dec, _, _ = gpu_layer(L)
+    _, _, _, y_pre = staged(L)
+    y_ref = oracle.layer(L.w_np, L.x_np, L.l_np, s.k)
+    assert rel_l2_rows(y_dec, y_ref).max() <= TOL_REL_L2
+    assert rel_l2_rows(y_pre, y_ref).max() <= TOL_REL_L2
+    assert rel_l2_rows(y_dec, y_pre).max() <= 2 * TOL_REL_L2
+
+
+def test_zero_tokens_is_noop():
+    s = shape("t0", T=4)
+    L = Layer(s)
+    y = torch.full((1, s.H), 7.0, device=dev())
+    empty_x = L.x[:0]
+    sm.strata_moe_layer(L.w, empty_x, L.logits[:0], s.k, y, workspace=L.workspace())
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm
+
+
+def test_rmsnorm_against_oracle():
+    rng = np.random.default_rng(9)
+    h = (rng.standard_normal((64, 3072)) * 3).astype(np.float32)
+    h[0] = 0.0
+    h[1] = 1.0
+    x = torch.empty((64, 3072), dtype=torch.int16, device=dev())
+    sm.strata_moe_rmsnorm(to_dev(h), x, 1e-6)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy().view(np.uint16).astype(np.int32)
+    ref = oracle.rmsnorm(h, 1e-6).astype(np.int32)
+    diff = np.abs(got - ref)
+    assert diff.max() <= 1              # at most one bf16 ulp (rounding of a near-tie)
+    assert np.mean(diff == 0) > 0.999
