@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X routed-MoE expert layer (one GPU).
+
+Headline (the default workload): one decode / multi-token-verify step of one MoE layer,
+T = 4 tokens (1 + 3 drafts), H = 3072, E = 512 experts, top-10, I = 768, 2-bit block-quantized
+experts.  A step is one call of the whole layer (route, group, gate/up + SiLU*mul, down,
+weighted combine).  To keep the 256 MB Infinity Cache from serving the ~86 MB of touched
+experts, the steps cycle over 16 resident layers (each with its own weights, activations and
+logits): a layer's experts are re-read only after ~1.4 GB of other layers' traffic.
+
+Secondary (same JSON line, key "prefill"): one prefill chunk of one layer, T = 8192, same
+dimensions; a step is one whole-layer call.
+
+value = whole-job layer-tokens/s = T * steps / timed seconds, inputs resident in HBM.
+roofline: HBM-bound decode (touched experts' packed bytes per layer call / call duration, peak
+8 TB/s) and MFMA-bound prefill (6*T*k*H*I FLOP per expert-FFN call / call duration, dense fp16
+peak 2.5 PFLOP/s), durations from HIP events on the stream the library launches on.
+cpu_baseline: the CPU oracle (single-threaded C, fp64) on a bounded sample of decode layers.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s (T=4 decode, T=8192 prefill) + % of HBM/MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def event_time_ms(fn, steps, stream):
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def bench_decode(args, stream):
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import Layer
+
+    s = mi.DECODE
+    n_layers = args.decode_layers
+    t0 = time.time()
+    layers = []
+    for l in range(n_layers):
+        layers.append(Layer(s, seed=args.seed, layer=l))
+        del layers[-1].w_np  # host copy no longer needed
+    log(f"decode: {n_layers} layers generated and uploaded in {time.time() - t0:.1f}s")
+    ws = layers[0].workspace()
+    y = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    touched = []
+    for L in layers:
+        ids = np.argsort(-L.l_np.astype(np.float64), axis=1, kind="stable")[:, :s.k]
+        touched.append(len(np.unique(ids)))
+    bytes_per_layer = [n * s.expert_bytes for n in touched]
+
+    def step(i):
+        L = layers[i % n_layers]
+        sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    ms = event_time_ms(step, args.steps, stream)
+    ms_per_step = ms / args.steps
+    algo_bytes = float(np.mean([bytes_per_layer[i % n_layers] for i in range(args.steps)]))
+    achieved_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
+    return {
+        "ms_per_step": ms_per_step,
+        "value": s.T / (ms_per_step * 1e-3),
+        "touched_experts_mean": float(np.mean(touched)),
+        "bytes_per_layer": algo_bytes,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "strata_moe_decode (route, gate/up GEMV, down GEMV, combine)",
+                     "unit_of_work": "touched experts' packed bytes (2,211,840 B each) per layer"},
+        "layers": layers,
+    }
+
+
+def bench_prefill(args, stream):
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import Layer
+
+    s = mi.SHAPES[args.prefill_workload]
+    t0 = time.time()
+    L = Layer(s, seed=args.seed)
+    del L.w_np
+    log(f"prefill: layer generated and uploaded in {time.time() - t0:.1f}s")
+    ws = L.workspace()
+    y = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    S = s.T * s.k
+    flops = 6.0 * S * s.H * s.I
+
+    def step(i):
+        sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=stream)
+
+    for i in range(max(2, args.warmup // 10)):
+        step(i)
+    steps = args.prefill_steps
+    ms = event_time_ms(step, steps, stream)
+    ms_per_step = ms / steps
+    # the expert-FFN entry point alone (x conversion + up GEMM + down GEMM), on the same stream
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(s.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(S, dtype=torch.int32, device="cuda")
+    sp = torch.empty(S, dtype=torch.int32, device="cuda")
+    out = torch.empty((S, s.H), dtype=torch.int16, device="cuda")
+    sm.strata_moe_route(L.logits, s.k, ids, rw, stream=stream)
+    sm.strata_moe_permute(ids, s.E, counts, offsets, ss, sp, ws, stream=stream)
+
+    def ffn(i):
+        sm.strata_moe_expert_ffn(L.w, L.x, s.k, offsets, ss, out, ws, stream=stream)
+
+    ffn(0)
+    ms_ffn = event_time_ms(ffn, steps, stream) / steps
+    tflops_ffn = flops / (ms_ffn * 1e-3) / 1e12
+    tflops_layer = flops / (ms_per_step * 1e-3) / 1e12
+    return {
+        "workload": f"{s.name} T={s.T} H={s.H} E={s.E} k={s.k} I={s.I} "
+                    f"{'Q3' if s.fmt == 3 else 'Q2'}-block experts",
+        "value": s.T / (ms_per_step * 1e-3),
+        "unit": "layer-tokens/s",
+        "ms_per_step": ms_per_step,
+        "steps": steps,
+        "layer_tflops": tflops_layer,
+        "layer_frac": tflops_layer / MFMA_F16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": tflops_ffn, "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops_ffn / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "strata_moe_expert_ffn (x to fp16, gate/up GEMM, down GEMM)",
+                     "ms_per_call": ms_ffn, "unit_of_work": "6*T*k*H*I FLOP per call"},
+        "dtype": "f16 MFMA, fp32 accumulate",
+    }
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--decode-layers", type=int, default=16)
+    p.add_argument("--prefill-steps", type=int, default=10)
+    p.add_argument("--prefill-workload", default="prefill", choices=["prefill", "skewed"])
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu", action="store_true")
+    args = p.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every layer's "
+              "experts fit in one MI355X's HBM and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    import oracle
+
+    sm.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    dec = bench_decode(args, stream)
+    log(f"decode: {dec['ms_per_step'] * 1e3:.2f} us/layer, {dec['value']:.4g} layer-tokens/s, "
+        f"{dec['roofline']['achieved']:.0f} GB/s ({dec['roofline']['frac'] * 100:.1f}% of HBM peak)")
+    layers = dec.pop("layers")
+    pre = None
+    if not args.no_prefill:
+        for L in layers:
+            del L.w
+        torch.cuda.empty_cache()
+        pre = bench_prefill(args, stream)
+        log(f"prefill: {pre['ms_per_step']:.3f} ms/layer, {pre['value']:.4g} tokens/s, layer "
+            f"{pre['layer_tflops']:.0f} TFLOP/s; expert FFN {pre['roofline']['achieved']:.0f} TFLOP/s "
+            f"({pre['roofline']['frac'] * 100:.1f}% of MFMA peak)")
+    cpu = None
+    if not args.no_cpu:
+        s = mi.DECODE
+        t0 = time.time()
+        n = 0
+        cpu_time = 0.0
+        while n < len(layers) and (time.time() - t0) < args.cpu_seconds:
+            w_np = mi.make_weights(s, args.seed, n)
+            L = layers[n]
+            t1 = time.perf_counter()
+            oracle.layer(w_np, L.x_np, L.l_np, s.k)
+            cpu_time += time.perf_counter() - t1
+            n += 1
+        cpu = {"value": n * s.T / cpu_time, "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} decode layers (T=4 each) of the benchmark's 16, full layer each, "
+                         f"{cpu_time:.1f}s of single-threaded oracle time"}
+        log(f"cpu oracle: {cpu['value']:.3g} layer-tokens/s over {n} layers ({cpu_time:.1f}s)")
+
+    s = mi.DECODE
+    line = {
+        "metric": METRIC,
+        "value": dec["value"],
+        "unit": "layer-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox inputs, random-init 2-bit experts)",
+        "config": {"workload": f"decode/verify step of one MoE layer: T={s.T} (1+3 drafts), "
+                               f"H={s.H}, E={s.E}, top-{s.k}, I={s.I}, Q2-block experts; "
+                               f"{args.decode_layers} resident layers cycled",
+                   "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I, "format": "Q2_B32",
+                   "touched_experts_mean": dec["touched_experts_mean"],
+                   "parallelism": "single GPU"},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        line["prefill"] = pre
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,7 @@ struct Chunk {
   int32_t pad;
 };
 
-constexpr int kChunkRows = 256;  // rows of one GEMM work unit (8 fragments of 32)
+constexpr int kChunkRows = 224;  // rows of one GEMM work unit (at most 7 fragments of 32)
 constexpr int kPermTile = 1024;  // slots per permute tile
 
 // Upper bound of the number of chunks for S slots over E experts.

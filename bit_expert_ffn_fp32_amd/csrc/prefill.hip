@@ -4,7 +4,7 @@
 // low-bit blocks are dequantized on the fly inside it ("Two-Day Port, 8x Faster Prefill: Strata
 // Engine Benchmarked", Where Strata Is Fast); a larger prefill batch lets every expert's weights
 // serve more tokens (same section).  Here every work unit is weight-stationary: one (expert,
-// output slice) pair streams its packed 2- or 3-bit blocks once per chunk of up to 256 of the
+// output slice) pair streams its packed 2- or 3-bit blocks once per chunk of up to 224 of the
 // expert's tokens, decodes them in registers and feeds v_mfma_f32_32x32x16_f16 with fp32
 // accumulation.
 //
@@ -16,7 +16,7 @@
 //
 // Operand order.  Within every group of 8 consecutive reduction indices the GEMM feeds the
 // matrix cores the order P8 = {0,4,1,5,2,6,3,7}: the decoder then produces each fp16 pair from one
-// byte-table lookup (v_perm_b32).  The activations are stored in the same order (x by the
+// byte-table lookup (v_perm_b32) in a per-block table of the four products fp16(d * (q - 1.5)).  The activations are stored in the same order (x by the
 // conversion kernel, the intermediate by the up-projection epilogue), so the sums are unchanged.
 //
 // Work distribution.  Units (chunk, slice) are numbered so that the units of one expert are
@@ -30,19 +30,55 @@
 
 namespace strata {
 
-constexpr int kGemmThreads = 256;               // 4 waves, one per SIMD
-constexpr int kKC = 128;                        // reduction indices per pipeline stage
-constexpr int kLdsRow = kKC + 8;                // halfs per LDS row (16-byte pad: no bank conflicts)
-constexpr int kFrags = kChunkRows / 32;         // 32-row fragments per chunk
-constexpr int kLdsTile = kChunkRows * kLdsRow;  // halfs per stage buffer
-constexpr size_t kGemmLds = 2 * kLdsTile * sizeof(uint16_t) + kChunkRows * sizeof(int);
+constexpr int kGemmThreads = 256;                 // 4 waves, one per SIMD
+constexpr int kKS = 64;                           // reduction indices per pipeline stage (2 blocks)
+constexpr int kFrags = kChunkRows / 32;           // 32-row fragments per chunk
+constexpr int kWScaleBytes = 256 * 2 * 2;         // 256 weight rows x 2 fp16 scales per stage
+constexpr int kLdsBudget = 150 * 1024;            // ring of stage buffers
+constexpr size_t kGemmLds = kLdsBudget + kChunkRows * sizeof(int);
+
+// Stage geometry of a unit with NF fragments: as many stage buffers as fit in the ring (the
+// copies of all but the computed stage are in flight, hiding the ~2-3 us copy latency), capped
+// so that the vector-memory counter can express the waits (at most 63 outstanding operations).
+template <int FMT, int NF>
+struct Pipe {
+  static constexpr int kCB = FMT == 2 ? 8 : 12;
+  static constexpr int kXBytes = NF * 32 * kKS * 2;         // activation tile
+  static constexpr int kWCodeBytes = 256 * 2 * kCB;          // 256 weight rows x 2 blocks
+  static constexpr int kStage = kXBytes + kWCodeBytes + kWScaleBytes;
+  static constexpr int kPer = NF + (FMT == 2 ? 1 : 6) + 1;   // copy instructions per wave per stage
+  static constexpr int kByLds = kLdsBudget / kStage;
+  static constexpr int kByCnt = 63 / kPer + 1;               // (buffers - 2) * kPer <= 63, with margin
+  static constexpr int kNBuf = kByLds < kByCnt ? (kByLds < 8 ? kByLds : 8) : (kByCnt < 8 ? kByCnt : 8);
+  static constexpr int kPD = kNBuf - 1;
+  static_assert(kNBuf >= 2, "ring too small");
+  static_assert((kPD - 1) * kPer <= 63, "vmcnt range");
+};
 
 STRATA_DEVICE int p8inv(int m) { return ((m & 3) << 1) | (m >> 2); }  // position of index m
 
+// s_waitcnt with only the vector-memory counter constrained (at most N outstanding).
+template <int N>
+STRATA_DEVICE void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Waits until at most P later stages' copies are outstanding, for a runtime P in [0, PMAX].
+template <int PER, int PMAX>
+STRATA_DEVICE void wait_pending(int p) {
+  if constexpr (PMAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (p >= PMAX) wait_vmcnt<PMAX * PER>();
+    else wait_pending<PER, PMAX - 1>(p);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
-// Block decoders.  A lane owns two consecutive blocks (64 reduction indices) of one weight row per
-// stage and produces, for stage step s (0..7), the 8 fp16 weights of indices 8s .. 8s+7 of that
-// 64-range in P8 order.
+// Block decoders.  Per stage a lane owns one block (32 reduction indices) of each of its two
+// weight rows and produces, for step s (0..3), the 8 fp16 weights of indices 8s .. 8s+7 of the
+// block in P8 order.
 
 struct Q2Tab {
   uint32_t lo, hi;  // byte q of lo/hi = low/high byte of fp16(d * (q - 1.5))
@@ -50,95 +86,47 @@ struct Q2Tab {
 
 STRATA_DEVICE Q2Tab q2_table(uint16_t dbits) {
   const _Float16 d = __builtin_bit_cast(_Float16, dbits);
-  const float df = (float)d;
-  const uint32_t w0 = __builtin_bit_cast(uint16_t, (_Float16)(df * -1.5f));
-  const uint32_t w1 = __builtin_bit_cast(uint16_t, (_Float16)(df * -0.5f));
-  const uint32_t w2 = __builtin_bit_cast(uint16_t, (_Float16)(df * 0.5f));
-  const uint32_t w3 = __builtin_bit_cast(uint16_t, (_Float16)(df * 1.5f));
-  const uint32_t p01 = w0 | (w1 << 16), p23 = w2 | (w3 << 16);
-  return Q2Tab{__builtin_amdgcn_perm(p23, p01, 0x06040200u), __builtin_amdgcn_perm(p23, p01, 0x07050301u)};
+  const half2_t dd = {d, d};
+  const half2_t p01 = dd * half2_t{(_Float16)-1.5f, (_Float16)-0.5f};  // one rounding each
+  const half2_t p23 = dd * half2_t{(_Float16)0.5f, (_Float16)1.5f};
+  const uint32_t u01 = __builtin_bit_cast(uint32_t, p01), u23 = __builtin_bit_cast(uint32_t, p23);
+  return Q2Tab{__builtin_amdgcn_perm(u23, u01, 0x06040200u), __builtin_amdgcn_perm(u23, u01, 0x07050301u)};
 }
 
-// codes: the lane's 16 code bytes (2 blocks); bytes 2s, 2s+1 hold the 8 codes of step s.
-STRATA_DEVICE half8_t q2_decode(const u32x4_t& codes, int s, const Q2Tab& tab) {
-  const uint32_t word = codes[s >> 1];
+// code: the block's 8 code bytes; bytes 2s, 2s+1 hold the codes of step s.
+STRATA_DEVICE half8_t q2_decode(uint32_t w0, uint32_t w1, int s, const Q2Tab& tab) {
+  const uint32_t word = (s >> 1) ? w1 : w0;
   const uint32_t X = __builtin_amdgcn_perm(word, word, (s & 1) ? 0x03030202u : 0x01010000u);
+  const uint32_t mask = 0x03030303u, base = 0x04000400u;
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t sel = ((X >> (2 * i)) & 0x03030303u) | 0x04000400u;
+    const uint32_t sel = ((X >> (2 * i)) & mask) | (base & ~mask);
     r[i] = __builtin_amdgcn_perm(tab.hi, tab.lo, sel);
   }
   return __builtin_bit_cast(half8_t, r);
 }
 
-// 3-bit codes: the lane's 24 code bytes (2 blocks of 12) as 6 words; step s covers codes
-// 8(s%4) .. 8(s%4)+7 of block s/4, i.e. 24 bits at bit offset 24(s%4) of that block.
-STRATA_DEVICE half8_t q3_decode(const uint32_t* cw, int s, float d) {
-  const int base = (s >> 2) * 3;
-  const int o = 24 * (s & 3);
-  const uint32_t lo = cw[base + (o >> 5)];
-  const uint32_t hi = cw[base + ((o >> 5) < 2 ? (o >> 5) + 1 : 2)];
-  const uint32_t v = __builtin_amdgcn_alignbit(hi, lo, o & 31);
+// 3-bit: the block's 12 code bytes as 3 words; step s covers bits 24s .. 24s+23.
+STRATA_DEVICE half8_t q3_decode(uint32_t w0, uint32_t w1, uint32_t w2, int s, float d) {
+  uint32_t v;
+  if (s == 0) v = w0;
+  else if (s == 1) v = __builtin_amdgcn_alignbit(w1, w0, 24);
+  else if (s == 2) v = __builtin_amdgcn_alignbit(w2, w1, 16);
+  else v = w2 >> 8;
   const float off = -3.5f * d;  // exact: 13 significant bits
   half8_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t qa = (v >> (3 * i)) & 7u, qb = (v >> (3 * i + 12)) & 7u;
-    r[2 * i] = (_Float16)__builtin_fmaf((float)qa, d, off);      // exact in fp32, one rounding
+    r[2 * i] = (_Float16)__builtin_fmaf((float)qa, d, off);  // exact in fp32, one rounding
     r[2 * i + 1] = (_Float16)__builtin_fmaf((float)qb, d, off);
   }
   return r;
 }
 
-// Per-lane weight stream of one stage: two blocks of one row.
-template <int FMT>
-struct RowStage {
-  uint32_t c[6];   // code bytes (Q2: 16 B in c[0..3]; Q3: 24 B)
-  uint32_t sc;     // the two blocks' fp16 scales
-};
-
-template <int FMT>
-STRATA_DEVICE void load_stage(RowStage<FMT>& st, const uint8_t* row_codes, const uint16_t* row_scales,
-                              int blk) {
-  constexpr int CB = FMT == 2 ? 8 : 12;
-  const uint8_t* p = row_codes + (size_t)blk * CB;
-  if constexpr (FMT == 2) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    st.c[0] = v[0]; st.c[1] = v[1]; st.c[2] = v[2]; st.c[3] = v[3];
-  } else {
-    const uint2* q = reinterpret_cast<const uint2*>(p);  // 8-byte aligned (blk even)
-    const uint2 a = q[0], b = q[1], c = q[2];
-    st.c[0] = a.x; st.c[1] = a.y; st.c[2] = b.x; st.c[3] = b.y; st.c[4] = c.x; st.c[5] = c.y;
-  }
-  st.sc = *reinterpret_cast<const uint32_t*>(row_scales + blk);
-}
-
-template <int FMT>
-struct StageDecoder {
-  Q2Tab t0, t1;
-  float d0, d1;
-  STRATA_DEVICE void init(const RowStage<FMT>& st) {
-    if constexpr (FMT == 2) {
-      t0 = q2_table((uint16_t)(st.sc & 0xFFFFu));
-      t1 = q2_table((uint16_t)(st.sc >> 16));
-    } else {
-      d0 = f16_to_f32((uint16_t)(st.sc & 0xFFFFu));
-      d1 = f16_to_f32((uint16_t)(st.sc >> 16));
-    }
-  }
-  STRATA_DEVICE half8_t get(const RowStage<FMT>& st, int s) const {
-    if constexpr (FMT == 2) {
-      const u32x4_t c = {st.c[0], st.c[1], st.c[2], st.c[3]};
-      return q2_decode(c, s, s < 4 ? t0 : t1);
-    } else {
-      return q3_decode(st.c, s, s < 4 ? d0 : d1);
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------------------------
-// Shared pieces of the two GEMMs.
+// Work units.
 
 struct UnitInfo {
   int expert, row_start, nrows, nfrag, slice;
@@ -161,47 +149,207 @@ STRATA_DEVICE bool pick_unit(const Chunk* chunks, const int* n_chunks, int n_sli
   return true;
 }
 
-// Stage loader of the activation tile: rows (nfrag*32) x 128 fp16 = 16 pieces of 16 B per row.
-struct TileLoad {
-  u32x4_t v[16];
+// ---------------------------------------------------------------------------------------------
+// The K loop shared by both projections.
+//
+// Every stage (64 reduction indices) is copied global -> LDS by the workgroup with
+// global_load_lds (lane i of a wave instruction lands at the instruction's LDS base + size*i):
+//  * activation tile: NF*32 rows x 64 fp16 = 8 pieces of 16 B per row; piece c of row r sits in
+//    slot c ^ (r % 8) so that a fragment read (8 consecutive rows, one piece each, per LDS cycle)
+//    hits distinct banks; wave w copies the 8-row groups q = w, w+4, ...;
+//  * weights: the 64 rows of each wave (32 of stream 0, 32 of stream 1), both blocks' codes and
+//    scales of the stage.
+// Stages are issued kPD ahead into a ring of kNBuf buffers; each stage waits on the vector-memory
+// counter for its own copies and a barrier makes them visible to all waves.
+
+// The weight row this lane copies: lane l of a wave copies row l % 32 of stream l / 32.
+struct WeightRows {
+  const uint8_t* code_row;
+  const uint16_t* scale_row;
 };
 
-STRATA_DEVICE void load_tile(TileLoad& tl, const uint16_t* __restrict__ src, const int* rows_lds,
-                             int ld, int k0, int nfrag, bool gather) {
-  const int npieces = nfrag * 32 * 16;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int p = threadIdx.x + i * kGemmThreads;
-    if (p < npieces) {
-      const int r = p >> 4, c = p & 15;
-      const int row = rows_lds[r];
-      (void)gather;
-      tl.v[i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)row * ld + k0 + c * 8);
-    }
-  }
+template <int FMT>
+STRATA_DEVICE WeightRows weight_rows(const uint8_t* codes0, const uint8_t* codes1,
+                                     const uint16_t* scales0, const uint16_t* scales1, int nb) {
+  constexpr int CB = FMT == 2 ? 8 : 12;
+  const int lane = threadIdx.x & 63, row = lane & 31;
+  const bool second = lane >= 32;
+  WeightRows wr;
+  wr.code_row = (second ? codes1 : codes0) + (size_t)row * nb * CB;
+  wr.scale_row = (second ? scales1 : scales0) + (size_t)row * nb;
+  return wr;
 }
 
-STRATA_DEVICE void store_tile(const TileLoad& tl, uint16_t* lds, int nfrag) {
-  const int npieces = nfrag * 32 * 16;
+template <int FMT, int NF>
+STRATA_DEVICE void issue_stage(uint8_t* stage, const uint16_t* __restrict__ src, const int (&xoff)[NF],
+                               const WeightRows& wr, int j) {
+  constexpr int CB = FMT == 2 ? 8 : 12;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k0 = j * kKS;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int p = threadIdx.x + i * kGemmThreads;
-    if (p < npieces) {
-      const int r = p >> 4, c = p & 15;
-      *reinterpret_cast<u32x4_t*>(lds + r * kLdsRow + c * 8) = tl.v[i];
-    }
+  for (int g = 0; g < NF; ++g) {
+    const int q = wave + 4 * g;
+    __builtin_amdgcn_global_load_lds(src + xoff[g] + k0, stage + q * 1024, 16, 0, 0);
   }
+  const uint8_t* crow = wr.code_row + 2 * j * CB;
+  uint8_t* carea = stage + Pipe<FMT, NF>::kXBytes + wave * 64 * 2 * CB;
+  if constexpr (FMT == 2) {
+    __builtin_amdgcn_global_load_lds(crow, carea, 16, 0, 0);  // [64 rows][2 blocks][8 B]
+  } else {
+    // [2 blocks][3 words][64 rows] dwords
+#pragma unroll
+    for (int w = 0; w < 6; ++w)
+      __builtin_amdgcn_global_load_lds(crow + 4 * w, carea + w * 256, 4, 0, 0);
+  }
+  const uint16_t* srow = wr.scale_row + 2 * j;
+  __builtin_amdgcn_global_load_lds(srow, stage + Pipe<FMT, NF>::kXBytes + Pipe<FMT, NF>::kWCodeBytes + wave * 256, 4, 0, 0);
 }
 
-STRATA_DEVICE half8_t lds_frag(const uint16_t* lds, int f, int lane, int s) {
-  const int row = f * 32 + (lane & 31);
-  const int col = (lane >> 5) * 64 + s * 8;
-  return *reinterpret_cast<const half8_t*>(lds + row * kLdsRow + col);
+template <int FMT, int NF>
+STRATA_DEVICE void gemm_core(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const uint16_t* __restrict__ src,
+                             int ld, int K, const int* rows_lds, const WeightRows& wr,
+                             uint8_t* lds) {
+  using P = Pipe<FMT, NF>;
+  constexpr int CB = P::kCB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    acc0[f] = f32x16_t{};
+    acc1[f] = f32x16_t{};
+  }
+  int xoff[NF];
+#pragma unroll
+  for (int g = 0; g < NF; ++g) {
+    const int r = 8 * (wave + 4 * g) + (lane >> 3);
+    xoff[g] = rows_lds[r] * ld + (((lane & 7) ^ (lane >> 3)) << 3);
+  }
+  const int NK = K / kKS;
+#pragma unroll
+  for (int j = 0; j < P::kPD; ++j)
+    if (j < NK) issue_stage<FMT, NF>(lds + j * P::kStage, src, xoff, wr, j);
+  for (int j = 0; j < NK; ++j) {
+    // this wave's copies of stage j have landed (at most the later stages are outstanding) ...
+    {
+      const int later = NK - 1 - j;
+      wait_pending<P::kPer, P::kPD - 1>(later < P::kPD - 1 ? later : P::kPD - 1);
+    }
+    // ... and so have every other wave's.  A bare s_barrier: __syncthreads() would also drain the
+    // copies still in flight for the later stages.
+    __builtin_amdgcn_s_barrier();
+    if (j + P::kPD < NK) issue_stage<FMT, NF>(lds + ((j + P::kPD) % P::kNBuf) * P::kStage, src, xoff, wr, j + P::kPD);
+    const uint8_t* stage = lds + (j % P::kNBuf) * P::kStage;
+    const uint8_t* carea = stage + P::kXBytes + wave * 64 * 2 * CB;
+    const uint16_t* sarea = reinterpret_cast<const uint16_t*>(stage + P::kXBytes + P::kWCodeBytes + wave * 256);
+    // this lane's block (hh) of its row in each stream
+    uint32_t cw0[3], cw1[3];
+    if constexpr (FMT == 2) {
+      const uint2 v0 = *reinterpret_cast<const uint2*>(carea + m * 16 + hh * 8);
+      const uint2 v1 = *reinterpret_cast<const uint2*>(carea + (32 + m) * 16 + hh * 8);
+      cw0[0] = v0.x; cw0[1] = v0.y; cw1[0] = v1.x; cw1[1] = v1.y;
+      cw0[2] = cw1[2] = 0;
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(carea) + hh * 3 * 64;
+      cw0[0] = p[m]; cw0[1] = p[64 + m]; cw0[2] = p[128 + m];
+      cw1[0] = p[32 + m]; cw1[1] = p[96 + m]; cw1[2] = p[160 + m];
+    }
+    const uint16_t d0 = sarea[m * 2 + hh], d1 = sarea[(32 + m) * 2 + hh];
+    Q2Tab t0, t1;
+    float f0 = 0.0f, f1 = 0.0f;
+    if constexpr (FMT == 2) {
+      t0 = q2_table(d0);
+      t1 = q2_table(d1);
+    } else {
+      f0 = f16_to_f32(d0);
+      f1 = f16_to_f32(d1);
+    }
+    const uint8_t* xt = stage;
+    // Software pipeline over the 4 steps of the stage: scheduling region s holds the matrix ops
+    // of step s together with the fragment reads and the weight decode of step s+1, so the
+    // decode's VALU work issues between the matrix ops and the reads have a full step to land.
+    half8_t a[2][NF];
+    half8_t b[2][2];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      a[0][f] = *reinterpret_cast<const half8_t*>(xt + (f * 32 + m) * 128 + ((hh << 2) ^ (m & 7)) * 16);
+    if constexpr (FMT == 2) {
+      b[0][0] = q2_decode(cw0[0], cw0[1], 0, t0);
+      b[0][1] = q2_decode(cw1[0], cw1[1], 0, t1);
+    } else {
+      b[0][0] = q3_decode(cw0[0], cw0[1], cw0[2], 0, f0);
+      b[0][1] = q3_decode(cw1[0], cw1[1], cw1[2], 0, f1);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s < 3) {
+        const int slot = ((hh << 2) + s + 1) ^ (m & 7);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          a[nxt][f] = *reinterpret_cast<const half8_t*>(xt + (f * 32 + m) * 128 + slot * 16);
+        if constexpr (FMT == 2) {
+          b[nxt][0] = q2_decode(cw0[0], cw0[1], s + 1, t0);
+          b[nxt][1] = q2_decode(cw1[0], cw1[1], s + 1, t1);
+        } else {
+          b[nxt][0] = q3_decode(cw0[0], cw0[1], cw0[2], s + 1, f0);
+          b[nxt][1] = q3_decode(cw1[0], cw1[1], cw1[2], s + 1, f1);
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        acc0[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][f], b[cur][0], acc0[f], 0, 0, 0);
+        acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][f], b[cur][1], acc1[f], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // every wave is done with the stage buffers before the epilogue reuses them
+}
+
+// Row of a 32x32 accumulator tile held in register r of this lane.
+STRATA_DEVICE int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+STRATA_DEVICE float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---------------------------------------------------------------------------------------------
 // Up projection: A[p][n] = SiLU(x_t . W_g[n]) * (x_t . W_u[n]) for the chunk's rows p.
 // Slice = 128 outputs; wave w owns outputs slice*128 + w*32 + (lane % 32), gate and up.
+
+constexpr int kUpOutRow = 128 + 8;   // halfs per LDS row of the staged output tile
+constexpr int kDownOutRow = 256;     // 224 rows x 256 halfs fit in the stage ring
+
+template <int FMT, int NF>
+STRATA_DEVICE void up_unit(const UnitInfo& u, const uint16_t* __restrict__ x16, const WeightRows& wr,
+                           int H, int I, uint16_t* __restrict__ a16, uint8_t* lds_bytes,
+                           const int* rows_lds) {
+  f32x16_t accg[NF], accu[NF];
+  gemm_core<FMT, NF>(accg, accu, x16, H, H, rows_lds, wr, lds_bytes);
+  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_bytes);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 31, hh = lane >> 5;
+  // stage SiLU(g)*u as fp16 in LDS (columns in P8 order within groups of 8), then 16-byte stores
+  const int lcol = wave * 32 + (nl & ~7) + p8inv(nl & 7);
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = f * 32 + acc_row(r, hh);
+      lds[row * kUpOutRow + lcol] =
+          __builtin_bit_cast(uint16_t, f32_to_f16_sat(silu_mul(accg[f][r], accu[f][r])));
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2 * NF; ++i) {
+    const int p = threadIdx.x + i * kGemmThreads;  // 16 pieces per row
+    const int r = p >> 4, c = p & 15;
+    if (r < u.nrows)
+      *reinterpret_cast<u32x4_t*>(a16 + (size_t)(u.row_start + r) * I + u.slice * 128 + c * 8) =
+          *reinterpret_cast<const u32x4_t*>(lds + r * kUpOutRow + c * 8);
+  }
+}
 
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
@@ -211,90 +359,63 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
     const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales, int H, int I,
     uint16_t* __restrict__ a16) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  int* rows_lds = reinterpret_cast<int*>(smem + 2 * kLdsTile * sizeof(uint16_t));
+  int* rows_lds = reinterpret_cast<int*>(smem + kLdsBudget);
   UnitInfo u;
   if (!pick_unit(chunks, n_chunks, I / 128, u)) return;
   constexpr int CB = FMT == 2 ? 8 : 12;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 31, hh = lane >> 5;
+  const int wave = threadIdx.x >> 6;
   const int nbh = H / 32;
-  const int n = u.slice * 128 + wave * 32 + nl;
-  const size_t grow = (size_t)u.expert * I + n;
-  const uint8_t* gc = gate_codes + grow * nbh * CB;
-  const uint8_t* uc = up_codes + grow * nbh * CB;
-  const uint16_t* gs = gate_scales + grow * nbh;
-  const uint16_t* us = up_scales + grow * nbh;
-
+  const size_t row0 = (size_t)u.expert * I + u.slice * 128 + wave * 32;
+  const WeightRows wr = weight_rows<FMT>(gate_codes + row0 * nbh * CB, up_codes + row0 * nbh * CB,
+                                         gate_scales + row0 * nbh, up_scales + row0 * nbh, nbh);
   for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads)
     rows_lds[r] = sorted_slot[u.row_start + (r < u.nrows ? r : 0)] / k;
   __syncthreads();
-
-  f32x16_t accg[kFrags], accu[kFrags];
-#pragma unroll
-  for (int f = 0; f < kFrags; ++f) {
-    accg[f] = f32x16_t{};
-    accu[f] = f32x16_t{};
-  }
-  const int NK = H / kKC;
-  TileLoad tl;
-  RowStage<FMT> sg, su, ng, nu;
-  load_tile(tl, x16, rows_lds, H, 0, u.nfrag, true);
-  load_stage<FMT>(sg, gc, gs, 2 * hh);
-  load_stage<FMT>(su, uc, us, 2 * hh);
-  store_tile(tl, xs, u.nfrag);
-  __syncthreads();
-  for (int j = 0; j < NK; ++j) {
-    const uint16_t* cur = xs + (j & 1) * kLdsTile;
-    if (j + 1 < NK) {
-      load_tile(tl, x16, rows_lds, H, (j + 1) * kKC, u.nfrag, true);
-      load_stage<FMT>(ng, gc, gs, 4 * (j + 1) + 2 * hh);
-      load_stage<FMT>(nu, uc, us, 4 * (j + 1) + 2 * hh);
-    }
-    StageDecoder<FMT> dg, du;
-    dg.init(sg);
-    du.init(su);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const half8_t bg = dg.get(sg, s);
-      const half8_t bu = du.get(su, s);
-#pragma unroll
-      for (int f = 0; f < kFrags; ++f) {
-        if (f < u.nfrag) {
-          const half8_t a = lds_frag(cur, f, lane, s);
-          accg[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bg, accg[f], 0, 0, 0);
-          accu[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bu, accu[f], 0, 0, 0);
-        }
-      }
-    }
-    if (j + 1 < NK) {
-      store_tile(tl, xs + ((j + 1) & 1) * kLdsTile, u.nfrag);
-      sg = ng;
-      su = nu;
-    }
-    __syncthreads();
-  }
-  // epilogue: lane holds column n, rows 8*(r/4) + 4*hh + r%4 of every fragment
-  const int col = (n & ~7) | p8inv(n & 7);
-#pragma unroll
-  for (int f = 0; f < kFrags; ++f) {
-    if (f < u.nfrag) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = f * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (row < u.nrows) {
-          const float g = accg[f][r], up = accu[f][r];
-          const float a = g / (1.0f + expf(-g)) * up;
-          a16[(size_t)(u.row_start + row) * I + col] = __builtin_bit_cast(uint16_t, f32_to_f16_sat(a));
-        }
-      }
-    }
+  switch (u.nfrag) {
+    case 1: up_unit<FMT, 1>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    case 2: up_unit<FMT, 2>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    case 3: up_unit<FMT, 3>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    case 4: up_unit<FMT, 4>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    case 5: up_unit<FMT, 5>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    case 6: up_unit<FMT, 6>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    default: up_unit<FMT, 7>(u, x16, wr, H, I, a16, smem, rows_lds); break;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Down projection: out[slot(p)][h] = A[p] . W_d[h] for the chunk's rows p, written as bf16 in
 // slot order.  Slice = 256 outputs; wave w owns h = slice*256 + w*64 + nf*32 + (lane % 32).
+
+template <int FMT, int NF>
+STRATA_DEVICE void down_unit(const UnitInfo& u, const uint16_t* __restrict__ a16,
+                             const int* __restrict__ sorted_slot, const WeightRows& wr, int H,
+                             int I, uint16_t* __restrict__ expert_out, uint8_t* lds_bytes,
+                             const int* rows_lds) {
+  f32x16_t acc0[NF], acc1[NF];
+  gemm_core<FMT, NF>(acc0, acc1, a16, I, I, rows_lds, wr, lds_bytes);
+  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_bytes);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = f * 32 + acc_row(r, hh);
+      lds[row * kDownOutRow + wave * 64 + nl] = f32_to_bf16(acc0[f][r]);
+      lds[row * kDownOutRow + wave * 64 + 32 + nl] = f32_to_bf16(acc1[f][r]);
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4 * NF; ++i) {
+    const int p = threadIdx.x + i * kGemmThreads;  // 32 pieces per row
+    const int r = p >> 5, c = p & 31;
+    if (r < u.nrows) {
+      const size_t slot = (size_t)sorted_slot[u.row_start + r];
+      *reinterpret_cast<u32x4_t*>(expert_out + slot * H + u.slice * 256 + c * 8) =
+          *reinterpret_cast<const u32x4_t*>(lds + r * kDownOutRow + c * 8);
+    }
+  }
+}
 
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
@@ -303,82 +424,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
     const uint8_t* __restrict__ down_codes, const uint16_t* __restrict__ down_scales, int H, int I,
     uint16_t* __restrict__ expert_out) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* as = reinterpret_cast<uint16_t*>(smem);
-  int* rows_lds = reinterpret_cast<int*>(smem + 2 * kLdsTile * sizeof(uint16_t));
+  int* rows_lds = reinterpret_cast<int*>(smem + kLdsBudget);
   UnitInfo u;
   if (!pick_unit(chunks, n_chunks, H / 256, u)) return;
   constexpr int CB = FMT == 2 ? 8 : 12;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 31, hh = lane >> 5;
+  const int wave = threadIdx.x >> 6;
   const int nbi = I / 32;
-  const int h0 = u.slice * 256 + wave * 64 + nl;
-  const size_t r0 = (size_t)u.expert * H + h0, r1 = r0 + 32;
-  const uint8_t* c0 = down_codes + r0 * nbi * CB;
-  const uint8_t* c1 = down_codes + r1 * nbi * CB;
-  const uint16_t* s0 = down_scales + r0 * nbi;
-  const uint16_t* s1 = down_scales + r1 * nbi;
-
+  const size_t row0 = (size_t)u.expert * H + u.slice * 256 + wave * 64;
+  const WeightRows wr = weight_rows<FMT>(down_codes + row0 * nbi * CB, down_codes + (row0 + 32) * nbi * CB,
+                                         down_scales + row0 * nbi, down_scales + (row0 + 32) * nbi, nbi);
   for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads)
     rows_lds[r] = u.row_start + (r < u.nrows ? r : 0);
   __syncthreads();
-
-  f32x16_t acc0[kFrags], acc1[kFrags];
-#pragma unroll
-  for (int f = 0; f < kFrags; ++f) {
-    acc0[f] = f32x16_t{};
-    acc1[f] = f32x16_t{};
-  }
-  const int NK = I / kKC;
-  TileLoad tl;
-  RowStage<FMT> st0, st1, nx0, nx1;
-  load_tile(tl, a16, rows_lds, I, 0, u.nfrag, false);
-  load_stage<FMT>(st0, c0, s0, 2 * hh);
-  load_stage<FMT>(st1, c1, s1, 2 * hh);
-  store_tile(tl, as, u.nfrag);
-  __syncthreads();
-  for (int j = 0; j < NK; ++j) {
-    const uint16_t* cur = as + (j & 1) * kLdsTile;
-    if (j + 1 < NK) {
-      load_tile(tl, a16, rows_lds, I, (j + 1) * kKC, u.nfrag, false);
-      load_stage<FMT>(nx0, c0, s0, 4 * (j + 1) + 2 * hh);
-      load_stage<FMT>(nx1, c1, s1, 4 * (j + 1) + 2 * hh);
-    }
-    StageDecoder<FMT> d0, d1;
-    d0.init(st0);
-    d1.init(st1);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const half8_t b0 = d0.get(st0, s);
-      const half8_t b1 = d1.get(st1, s);
-#pragma unroll
-      for (int f = 0; f < kFrags; ++f) {
-        if (f < u.nfrag) {
-          const half8_t a = lds_frag(cur, f, lane, s);
-          acc0[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc0[f], 0, 0, 0);
-          acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc1[f], 0, 0, 0);
-        }
-      }
-    }
-    if (j + 1 < NK) {
-      store_tile(tl, as + ((j + 1) & 1) * kLdsTile, u.nfrag);
-      st0 = nx0;
-      st1 = nx1;
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int f = 0; f < kFrags; ++f) {
-    if (f < u.nfrag) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = f * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (row < u.nrows) {
-          const size_t slot = (size_t)sorted_slot[u.row_start + row];
-          expert_out[slot * H + h0] = f32_to_bf16(acc0[f][r]);
-          expert_out[slot * H + h0 + 32] = f32_to_bf16(acc1[f][r]);
-        }
-      }
-    }
+  switch (u.nfrag) {
+    case 1: down_unit<FMT, 1>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    case 2: down_unit<FMT, 2>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    case 3: down_unit<FMT, 3>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    case 4: down_unit<FMT, 4>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    case 5: down_unit<FMT, 5>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    case 6: down_unit<FMT, 6>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    default: down_unit<FMT, 7>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
   }
 }
 
