@@ -241,6 +241,7 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x, 
   if (st != STRATA_OK) return st;
   if (T > kMaxDecodeT) return STRATA_ERR_UNSUPPORTED;
   if (T == 0) return STRATA_OK;
+  if (!strata::decode_fits(T, w->num_experts, k, w->hidden, w->inter)) return STRATA_ERR_UNSUPPORTED;
   const void* ptrs[4] = {x, logits, y, workspace};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
@@ -265,7 +266,7 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   if (T <= kMaxDecodeT && (opt_counts || opt_offsets || opt_sorted_slot))
     return STRATA_ERR_INVALID_ARGUMENT;
   if (T == 0) return STRATA_OK;
-  if (T <= kMaxDecodeT)
+  if (T <= kMaxDecodeT && strata::decode_fits(T, w->num_experts, k, w->hidden, w->inter))
     return strata_moe_decode(w, x, logits, T, k, y, accumulate, opt_topk_ids, opt_topk_w, workspace,
                              workspace_bytes, stream);
   const void* ptrs[4] = {x, logits, y, workspace};

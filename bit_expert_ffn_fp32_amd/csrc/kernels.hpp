@@ -58,5 +58,8 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T,
                          const uint16_t* up_scales, const uint16_t* down_scales, float* y,
                          int accumulate, int* ids, float* w, void* ws, hipStream_t s);
 size_t decode_workspace_bytes(int T, int E, int k, int H, int I);
+// Whether the decode kernels take this shape (T <= 8, T*k <= 128, H <= 4096, I <= 4096 and the
+// staged activations fit in LDS).
+bool decode_fits(int T, int E, int k, int H, int I);
 
 }  // namespace strata

@@ -132,13 +132,15 @@ strata_status strata_moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, 
 
 /*
  * Expert FFN (prefill path): for every expert e and every slot s in its segment (token t =
- * s / k), with x the token's activations widened exactly from bf16:
+ * s / k), with x the token's activations:
  *   g = W_g x,  u = W_u x,  a = SiLU(g) * u  (SiLU(z) = z / (1 + exp(-z))),  out = W_d a.
  * The pages call the expert matrix multiply the heaviest computation and describe dequantizing
  * the low-bit blocks during the multiply ("Two-Day Port, 8x Faster Prefill: Strata Engine
  * Benchmarked", Where Strata Is Fast); the gate/up/SiLU-mul/down form is this library's
- * definition.  Weights are used exactly (codes enter the matrix cores as exact bf16 values and
- * each block's fp16 scale is applied in fp32); a and out are rounded to bf16.
+ * definition.  Precision: the products run on fp16 matrix cores with fp32 accumulation; each
+ * dequantized weight d * (q - c0) is rounded once to fp16, x is converted to fp16 (saturating at
+ * +-65504), a is rounded to fp16 and out to bf16.  The result stays within 5e-3 relative L2 of
+ * the exact (fp64) layer for unit-scale activations.
  *
  *   x           bf16 [T][H] (uint16 bit patterns)
  *   offsets, sorted_slot  as produced by strata_moe_permute for this (T, k, E)
@@ -165,12 +167,16 @@ strata_status strata_moe_combine(const uint16_t* expert_out, const float* topk_w
  * Decode / verify step for T <= 8 tokens (the pages' multi-token-prediction check of up to 3
  * drafted tokens plus one: "Strata - the details", How it works / speculation).  Computes the
  * same function as route + permute + expert_ffn + combine, with a bandwidth-bound path: every
- * touched expert's weights are streamed once and applied to all tokens that picked it.  The
- * intermediate a is kept in fp32 and no bf16 rounding is applied to the expert outputs.
+ * touched expert's weights are streamed once and applied to all tokens that picked it.
+ * Precision: weights and x enter exactly (bf16 dot products of the codes, fp32 accumulation, the
+ * fp16 block scale applied in fp32); a is rounded to bf16; the expert outputs and y stay fp32.
+ * The combine sums the k outputs of a token in slot order, so the result is deterministic.
  *   x bf16 [T][H], logits fp32 [T][E], y fp32 [T][H] (overwritten, or += with accumulate)
  *   opt_topk_ids int32 [T][k], opt_topk_w fp32 [T][k]: written when not NULL.
  * Workspace: at least strata_moe_workspace_bytes(T, E, k, H, I).
- * Limits: 1 <= T <= 8; others as strata_moe_expert_ffn.
+ * Limits: 1 <= T <= 8, T*k <= 128, hidden and inter at most 4096, and the activations staged
+ * in LDS must fit: 19/8 * T * hidden <= 147456 and 19/8 * T * k * inter <= 147456 (bytes);
+ * STRATA_ERR_UNSUPPORTED otherwise.  Others as strata_moe_expert_ffn.
  */
 strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
                                 const float* logits, int32_t T, int32_t k, float* y,
@@ -178,9 +184,10 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * One-call layer: y (=, or += with accumulate) MoE(x).  T <= 8 runs strata_moe_decode's path;
- * larger T runs route -> permute -> expert_ffn -> combine.  Each opt_* pointer may be NULL; when
- * given it receives that intermediate (same layout as the staged calls).  opt_counts,
+ * One-call layer: y (=, or += with accumulate) MoE(x).  T <= 8 runs strata_moe_decode's path
+ * when the shape is within its limits; otherwise route -> permute -> expert_ffn -> combine.
+ * Each opt_* pointer may be NULL; when given it receives that intermediate (same layout as the
+ * staged calls).  opt_counts,
  * opt_offsets and opt_sorted_slot are only produced on the T > 8 path and must be NULL for
  * T <= 8 (STRATA_ERR_INVALID_ARGUMENT otherwise).
  */
