@@ -8,10 +8,11 @@
 //
 // Two kernels (a kernel boundary costs ~1.7 us on MI355X; a grid-wide barrier inside one kernel
 // costs far more, because the per-XCD L2s must be written back and invalidated):
-//  K1 up:   every workgroup routes all T tokens itself (one wave per token), lists the distinct
-//           experts and the (token, slot) pairs of each, and works through a contiguous range of
-//           items (distinct expert, 16 rows of I): a = SiLU(g) * u per token, rounded to bf16.
-//           Workgroup 0 publishes the routing for K2 and the caller.
+//  K1 up:   one 16-wave workgroup per CU.  Every workgroup routes all T tokens itself (one wave
+//           per token), lists the distinct experts and the (token, slot) pairs of each, and works
+//           through a contiguous range of items (distinct expert, 16 rows of I), four waves per
+//           item: a = SiLU(g) * u per token, rounded to bf16.  Workgroup 0 publishes the routing
+//           for K2 and the caller.
 //  K2 down: workgroup b owns rows [b R, (b+1) R) of H (R = H / 256) for ALL distinct experts, so it
 //           holds every slot's down output for its rows and forms y = sum_j w_j out_j itself, in
 //           slot order: deterministic, and no third launch.
@@ -33,9 +34,9 @@
 
 namespace strata {
 
-constexpr int kDecThreads = 256;   // K1: 4 waves
+constexpr int kUpThreads = 1024;   // K1: 16 waves, one workgroup per CU
 constexpr int kDnThreads = 1024;   // K2: 16 waves, one workgroup per CU
-constexpr int kDnGrid = 256;
+constexpr int kGrid = 256;         // one workgroup per CU
 constexpr int kDecMaxT = 8;
 constexpr int kDecMaxS = 128;      // T * k <= 8 * 16
 constexpr int kDecMaxR = 16;       // rows of H per K2 workgroup (H <= 4096)
@@ -68,28 +69,34 @@ STRATA_DEVICE float sum4(float v) {
   return v;
 }
 
-// Wave-wide max of unsigned keys / min of ints, result uniform (read from lane 63).
+// Wave-wide max of unsigned keys / min of ints, result uniform (read from lane 63).  The DPP
+// moves take the identity of the operation as their fill value so that each step folds into one
+// DPP-modified max / min.
+template <int CTRL, int ROW_MASK = 0xF>
+STRATA_DEVICE uint32_t dpp_u(uint32_t v, uint32_t fill) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
 STRATA_DEVICE uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)dpp_i<0xB1>((int)v));
-  v = max(v, (uint32_t)dpp_i<0x4E>((int)v));
-  v = max(v, (uint32_t)dpp_i<0x124>((int)v));
-  v = max(v, (uint32_t)dpp_i<0x128>((int)v));
-  v = max(v, (uint32_t)dpp_i<0x142, 0xA>((int)v));  // row_bcast:15
-  v = max(v, (uint32_t)dpp_i<0x143, 0xC>((int)v));  // row_bcast:31
+  v = max(v, dpp_u<0xB1>(v, 0u));
+  v = max(v, dpp_u<0x4E>(v, 0u));
+  v = max(v, dpp_u<0x124>(v, 0u));
+  v = max(v, dpp_u<0x128>(v, 0u));
+  v = max(v, dpp_u<0x142, 0xA>(v, 0u));  // row_bcast:15
+  v = max(v, dpp_u<0x143, 0xC>(v, 0u));  // row_bcast:31
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 STRATA_DEVICE int wave_min_i(int v) {
-  v = min(v, dpp_i<0xB1>(v));
-  v = min(v, dpp_i<0x4E>(v));
-  v = min(v, dpp_i<0x124>(v));
-  v = min(v, dpp_i<0x128>(v));
-  v = min(v, dpp_i<0x142, 0xA>(v));
-  v = min(v, dpp_i<0x143, 0xC>(v));
+  v = min(v, (int)dpp_u<0xB1>((uint32_t)v, 0x7FFFFFFFu));
+  v = min(v, (int)dpp_u<0x4E>((uint32_t)v, 0x7FFFFFFFu));
+  v = min(v, (int)dpp_u<0x124>((uint32_t)v, 0x7FFFFFFFu));
+  v = min(v, (int)dpp_u<0x128>((uint32_t)v, 0x7FFFFFFFu));
+  v = min(v, (int)dpp_u<0x142, 0xA>((uint32_t)v, 0x7FFFFFFFu));
+  v = min(v, (int)dpp_u<0x143, 0xC>((uint32_t)v, 0x7FFFFFFFu));
   return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Order-preserving map of a logit to an unsigned key (-0 is first made +0, so equal logits get
-// equal keys), and back.
+// equal keys; every finite logit maps to a key above 0, which marks an empty entry), and back.
 STRATA_DEVICE uint32_t route_key(float v) {
   const uint32_t b = __float_as_uint(v + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -98,40 +105,72 @@ STRATA_DEVICE float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// Top-k of one token's logits by one wave: k rounds of "largest remaining logit, equal logits to
-// the lower expert index"; weights = softmax over the k kept logits (same rule as the router).
+// One token's logits, lane l holding experts l, l + 64, ...  The loads are unconditional
+// (clamped addresses) so that they are all in flight together.
 template <int NPL>
-STRATA_DEVICE void route_token_wave(const float* __restrict__ row, int E, int k, int* ids_out,
-                                    float* w_out) {
+struct TokenKeys {
+  float v[NPL];       // raw logits, converted once they have arrived
+  uint64_t c[NPL];    // (key << 32) | ~expert: larger is preferred, ties to the lower expert
+};
+template <int NPL>
+STRATA_DEVICE void load_token_logits(const float* __restrict__ row, int E, TokenKeys<NPL>& tk) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[NPL];
-  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) tk.v[i] = row[min(lane + 64 * i, E - 1)];
+}
+
+// Sorts the lane's entries, largest first (Batcher's odd-even merge network; NPL a power of 2).
+template <int NPL>
+STRATA_DEVICE void sort_lane_desc(uint64_t (&c)[NPL]) {
+#pragma unroll
+  for (int p = 1; p < NPL; p <<= 1)
+#pragma unroll
+    for (int kk = p; kk >= 1; kk >>= 1)
+#pragma unroll
+      for (int j = kk % p; j + kk < NPL; j += 2 * kk)
+#pragma unroll
+        for (int i = 0; i < kk && i + j + kk < NPL; ++i)
+          if ((i + j) / (2 * p) == (i + j + kk) / (2 * p)) {
+            const uint64_t a = c[i + j], b = c[i + j + kk];
+            const bool sw = b > a;
+            c[i + j] = sw ? b : a;
+            c[i + j + kk] = sw ? a : b;
+          }
+}
+
+// Top-k of one token by one wave: k rounds of "largest remaining logit, equal logits to the lower
+// expert index"; weights = softmax over the k kept logits (the router kernel's rule).  Each lane
+// sorts its own entries once; a round takes the maximum of the lanes' heads and the winning lane
+// pops its head.
+template <int NPL>
+STRATA_DEVICE void select_token_wave(TokenKeys<NPL>& tk, int E, int k, int* ids_out,
+                                     float* w_out) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e]) : 0u;
-    if (e >= E) taken |= 1u << i;
+    tk.c[i] = e < E ? ((uint64_t)route_key(tk.v[i]) << 32) | (uint32_t)~e : 0ull;
   }
+  sort_lane_desc<NPL>(tk.c);
   uint32_t my_key = 0;
   int my_i = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t bk = 0;
-    int bi = -1;  // this lane's best remaining entry (lowest i among equal keys)
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (!((taken >> i) & 1u) && (bi < 0 || key[i] > bk)) { bk = key[i]; bi = i; }
-    const uint32_t m = wave_max_u32(bi >= 0 ? bk : 0u);
-    const bool cand = bi >= 0 && bk == m;
+    const uint32_t hk = (uint32_t)(tk.c[0] >> 32);
+    const uint32_t m = wave_max_u32(hk);
+    const bool cand = hk == m;
     const uint64_t ball = __ballot(cand);
     int win;
     if (__popcll(ball) == 1) {  // the usual case: one lane holds the maximum
       const int wl = __ffsll((unsigned long long)ball) - 1;
-      win = wl + 64 * __builtin_amdgcn_readlane(bi, wl);
+      win = (int)~(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)tk.c[0], wl);
     } else {                    // equal logits in several lanes: lowest expert index
-      win = wave_min_i(cand ? lane + 64 * bi : 0x7FFFFFFF);
+      win = (int)~wave_max_u32(cand ? (uint32_t)tk.c[0] : 0u);
     }
-    if ((win & 63) == lane) taken |= 1u << (win >> 6);
     if (lane == j) { my_key = m; my_i = win; }
+    const bool pop = lane == (win & 63);
+#pragma unroll
+    for (int i = 0; i + 1 < NPL; ++i) tk.c[i] = pop ? tk.c[i + 1] : tk.c[i];
+    tk.c[NPL - 1] = pop ? 0ull : tk.c[NPL - 1];
   }
   const float top = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
   const float ex = lane < k ? expf(key_value(my_key) - top) : 0.0f;
@@ -142,17 +181,29 @@ STRATA_DEVICE void route_token_wave(const float* __restrict__ row, int E, int k,
   }
 }
 
-STRATA_DEVICE void route_all_tokens(const float* __restrict__ logits, int T, int E, int k,
-                                    int* ids_s, float* w_s) {
-  const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  for (int t = wave; t < T; t += nwaves) {
-    const float* row = logits + (size_t)t * E;
-    if (E <= 64) route_token_wave<1>(row, E, k, ids_s + t * k, w_s + t * k);
-    else if (E <= 128) route_token_wave<2>(row, E, k, ids_s + t * k, w_s + t * k);
-    else if (E <= 256) route_token_wave<4>(row, E, k, ids_s + t * k, w_s + t * k);
-    else if (E <= 512) route_token_wave<8>(row, E, k, ids_s + t * k, w_s + t * k);
-    else route_token_wave<16>(row, E, k, ids_s + t * k, w_s + t * k);
+// Routes all T tokens into LDS, one wave per token (T <= NWAVES).  `prefetch` runs first: its
+// loads and the logit loads are in flight together.
+template <int NPL, int NWAVES, typename F>
+STRATA_DEVICE void route_tokens_npl(const float* __restrict__ logits, int T, int E, int k,
+                                    int* ids_s, float* w_s, F&& prefetch) {
+  static_assert(NWAVES >= kDecMaxT, "one wave per token");
+  const int t = threadIdx.x >> 6;
+  prefetch();
+  if (t < T) {
+    TokenKeys<NPL> tk;
+    load_token_logits<NPL>(logits + (size_t)t * E, E, tk);
+    select_token_wave<NPL>(tk, E, k, ids_s + t * k, w_s + t * k);
   }
+}
+
+template <int NWAVES, typename F>
+STRATA_DEVICE void route_tokens(const float* __restrict__ logits, int T, int E, int k, int* ids_s,
+                                float* w_s, F&& prefetch) {
+  if (E <= 64) route_tokens_npl<1, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
+  else if (E <= 128) route_tokens_npl<2, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
+  else if (E <= 256) route_tokens_npl<4, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
+  else if (E <= 512) route_tokens_npl<8, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
+  else route_tokens_npl<16, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -169,38 +220,48 @@ struct RouteTable {
   int nd;
 };
 
-// Builds the table from rt.ids (visible to the workgroup).  scratch: 2 E ints of LDS.
-STRATA_DEVICE void build_table(RouteTable& rt, int T, int k, int E, int* scratch) {
-  int* first_slot = scratch;      // per expert: lowest slot that picked it
-  int* pos_of = scratch + E;      // per expert: its index in the distinct list
-  __shared__ int wave_cnt[kDecMaxS / 64];
+// The part of the table K2 needs, as K1 publishes it in the workspace.
+struct GlobalTable {
+  int nd;
+  int pad[3];
+  int dexp[kDecMaxS];
+  int dtp[kDecMaxS];
+  uint8_t dslot[kDecMaxS][kDecMaxT];
+};
+
+// Clears what build_table accumulates into; must be visible (a barrier) before build_table.
+// scratch: E ints of LDS that stay untouched until build_table returns.
+template <int NTHREADS>
+STRATA_DEVICE void table_clear(RouteTable& rt, int S, int E, int* scratch) {
+  for (int e = threadIdx.x; e < E; e += NTHREADS) scratch[e] = 0x7FFFFFFF;
+  if (threadIdx.x < S) rt.dtp[threadIdx.x] = 0;
+}
+
+// Builds the table from rt.ids (visible to the workgroup) after table_clear.
+STRATA_DEVICE void build_table(RouteTable& rt, int T, int k, int* scratch) {
+  int* first_slot = scratch;  // per expert: lowest slot that picked it
+  __shared__ uint64_t first_mask[kDecMaxS / 64];
   const int S = T * k, q = threadIdx.x;
-  for (int e = q; e < E; e += blockDim.x) first_slot[e] = 0x7FFFFFFF;
-  if (q < S) rt.dtp[q] = 0;
+  const int id = q < S ? rt.ids[q] : 0;
+  if (q < S) atomicMin(&first_slot[id], q);
   __syncthreads();
-  if (q < S) atomicMin(&first_slot[rt.ids[q]], q);
+  const int f = q < S ? first_slot[id] : 0;  // the slot that represents this slot's expert
+  const uint64_t ball = __ballot(q < S && f == q);
+  if ((q & 63) == 0 && (q >> 6) < kDecMaxS / 64) first_mask[q >> 6] = ball;
   __syncthreads();
-  const bool first = q < S && first_slot[rt.ids[q]] == q;
-  const uint64_t ball = __ballot(first);
-  const int lane = q & 63, wv = q >> 6;
-  if (lane == 0 && wv < kDecMaxS / 64) wave_cnt[wv] = __popcll(ball);
-  __syncthreads();
-  if (first) {
-    int pos = __popcll(ball & ((1ull << lane) - 1ull));
-    for (int i = 0; i < wv; ++i) pos += wave_cnt[i];
-    rt.dexp[pos] = rt.ids[q];
-    pos_of[rt.ids[q]] = pos;
-  }
-  if (q == 0) rt.nd = wave_cnt[0] + (S > 64 ? wave_cnt[1] : 0);
-  __syncthreads();
-  // each slot appends itself to its expert's list; a token picks an expert at most once and the
-  // per-token arithmetic does not depend on the position in the list
   if (q < S) {
-    const int p = pos_of[rt.ids[q]];
-    const int idx = atomicAdd(&rt.dtp[p], 1);
-    rt.dtok[p][idx] = (uint8_t)(q / k);
-    rt.dslot[p][idx] = (uint8_t)q;
+    // the expert's position in the distinct list: first occurrences before f
+    const uint64_t m0 = first_mask[0];
+    const int pos = f < 64 ? __popcll(m0 & ((1ull << f) - 1ull))
+                           : __popcll(m0) + __popcll(first_mask[1] & ((1ull << (f - 64)) - 1ull));
+    if (f == q) rt.dexp[pos] = id;
+    // a token picks an expert at most once, and the per-token arithmetic does not depend on the
+    // position in the expert's list
+    const int idx = atomicAdd(&rt.dtp[pos], 1);
+    rt.dtok[pos][idx] = (uint8_t)(q / k);
+    rt.dslot[pos][idx] = (uint8_t)q;
   }
+  if (q == 0) rt.nd = __popcll(first_mask[0]) + (S > 64 ? __popcll(first_mask[1]) : 0);
   __syncthreads();
 }
 
@@ -271,17 +332,28 @@ STRATA_DEVICE void load_row_chunks(RowChunks<FMT, MC>& rc, const uint8_t* row_co
   }
 }
 
-// 2-bit word -> 8 bf16 pairs (codes m, m + 8); magic = 0x40004000 (kept in a register).
-STRATA_DEVICE void q2_word_pairs(uint32_t w, uint32_t magic, uint32_t out[8]) {
+// Masks and the bf16 2.0 pattern of the 2-bit decode, held in VGPRs so that each pair is one
+// v_and_or_b32 (gfx9 VOP3 takes no literal operand).
+struct Q2Consts {
+  uint32_t m0, m1, m2, magic;
+};
+STRATA_DEVICE Q2Consts q2_consts() {
+  Q2Consts k{0x00030003u, 0x000C000Cu, 0x00300030u, 0x40004000u};
+  asm volatile("" : "+v"(k.m0), "+v"(k.m1), "+v"(k.m2), "+v"(k.magic));
+  return k;
+}
+
+// 2-bit word -> 8 bf16 pairs (codes m, m + 8).
+STRATA_DEVICE void q2_word_pairs(uint32_t w, const Q2Consts& k, uint32_t out[8]) {
   const uint32_t w6 = w >> 6, w12 = w >> 12;
-  out[0] = (w & 0x00030003u) | magic;    // codes 0, 8:  2 + q/64
-  out[1] = (w & 0x000C000Cu) | magic;    // codes 1, 9:  2 + q/16
-  out[2] = (w & 0x00300030u) | magic;    // codes 2, 10: 2 + q/4
-  out[3] = (w6 & 0x00030003u) | magic;   // codes 3, 11
-  out[4] = (w6 & 0x000C000Cu) | magic;   // codes 4, 12
-  out[5] = (w6 & 0x00300030u) | magic;   // codes 5, 13
-  out[6] = (w12 & 0x00030003u) | magic;  // codes 6, 14
-  out[7] = (w12 & 0x000C000Cu) | magic;  // codes 7, 15
+  out[0] = (w & k.m0) | k.magic;    // codes 0, 8:  2 + q/64
+  out[1] = (w & k.m1) | k.magic;    // codes 1, 9:  2 + q/16
+  out[2] = (w & k.m2) | k.magic;    // codes 2, 10: 2 + q/4
+  out[3] = (w6 & k.m0) | k.magic;   // codes 3, 11
+  out[4] = (w6 & k.m1) | k.magic;   // codes 4, 12
+  out[5] = (w6 & k.m2) | k.magic;   // codes 5, 13
+  out[6] = (w12 & k.m0) | k.magic;  // codes 6, 14
+  out[7] = (w12 & k.m1) | k.magic;  // codes 7, 15
 }
 
 // 3-bit: 16 codes = 48 bits; bf16(4 + q/2) = 0x4080 | q << 4.
@@ -296,9 +368,9 @@ STRATA_DEVICE void q3_word_pairs(uint64_t v, uint32_t out[8]) {
 
 // Word q (0..3) of a chunk (its code words cw) as bf16 pairs.
 template <int FMT>
-STRATA_DEVICE void chunk_word_pairs(const uint32_t* cw, int q, uint32_t magic, uint32_t pr[8]) {
+STRATA_DEVICE void chunk_word_pairs(const uint32_t* cw, int q, const Q2Consts& k, uint32_t pr[8]) {
   if constexpr (FMT == 2) {
-    q2_word_pairs(cw[q], magic, pr);
+    q2_word_pairs(cw[q], k, pr);
   } else {
     // block q/2 = words (q/2)*3 .. +2; word q%2 = bits 48*(q%2) .. of the block's 96 bits
     const int b = (q >> 1) * 3;
@@ -308,9 +380,8 @@ STRATA_DEVICE void chunk_word_pairs(const uint32_t* cw, int q, uint32_t magic, u
   }
 }
 
-// init + sum of 8 bf16 pair products, two chains.
-STRATA_DEVICE float dot8(const uint32_t pr[8], const uint32_t xw[8], float init) {
-  float p0 = init, p1 = 0.0f;
+// Adds the 8 bf16 pair products of a word to two accumulation chains.
+STRATA_DEVICE void dot8(const uint32_t pr[8], const uint32_t xw[8], float& p0, float& p1) {
 #pragma unroll
   for (int m = 0; m < 8; m += 2) {
     p0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr[m]),
@@ -318,16 +389,14 @@ STRATA_DEVICE float dot8(const uint32_t pr[8], const uint32_t xw[8], float init)
     p1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr[m + 1]),
                                          __builtin_bit_cast(bf16x2_t, xw[m + 1]), p1, false);
   }
-  return p0 + p1;
 }
 
 // Partial dot products of NR weight rows (this lane's chunks) with one staged activation row;
 // the activations are read from LDS once per word and applied to all NR rows.
 template <int FMT, int MC, int NR>
-STRATA_DEVICE void row_dots(const RowChunks<FMT, MC> (&rc)[NR], int nchunk, int c0, int cstep,
+STRATA_DEVICE void row_dots(RowChunks<FMT, MC> (&rc)[NR], int nchunk, int c0, int cstep,
                             const uint32_t* prow, const float* crow, float (&acc)[NR]) {
-  // bf16 2.0 in both halves, opaque to constant folding so that it lives in a VGPR
-  const uint32_t magic = 0x40004000u | (uint32_t)(threadIdx.x >> 10);
+  const Q2Consts kq = q2_consts();
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = 0.0f;
 #pragma unroll
@@ -335,20 +404,18 @@ STRATA_DEVICE void row_dots(const RowChunks<FMT, MC> (&rc)[NR], int nchunk, int 
     const int ch = c0 + cstep * i;
     if (ch < nchunk) {
       const float2 cc = *reinterpret_cast<const float2*>(crow + 2 * ch);
-      float p[NR][2];
-      uint32_t cw[NR][RowChunks<FMT, MC>::kWords];
+      float p[NR][2][2];  // [row][block][chain]
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
-        p[j][0] = -cc.x;
-        p[j][1] = -cc.y;
+        p[j][0][0] = -cc.x;
+        p[j][1][0] = -cc.y;
+        p[j][0][1] = 0.0f;
+        p[j][1][1] = 0.0f;
         // Decode afresh for every activation row: an empty asm hides that the code words are the
         // same on each call, so the compiler does not keep all decoded pairs of the row live
         // across the caller's token loop (which would cost occupancy).
 #pragma unroll
-        for (int q = 0; q < RowChunks<FMT, MC>::kWords; ++q) {
-          cw[j][q] = rc[j].w[i][q];
-          asm volatile("" : "+v"(cw[j][q]));
-        }
+        for (int q = 0; q < RowChunks<FMT, MC>::kWords; ++q) asm volatile("" : "+v"(rc[j].w[i][q]));
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -358,16 +425,16 @@ STRATA_DEVICE void row_dots(const RowChunks<FMT, MC> (&rc)[NR], int nchunk, int 
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
           uint32_t pr[8];
-          chunk_word_pairs<FMT>(cw[j], q, magic, pr);
-          p[j][q >> 1] = dot8(pr, xw, p[j][q >> 1]);
+          chunk_word_pairs<FMT>(rc[j].w[i], q, kq, pr);
+          dot8(pr, xw, p[j][q >> 1][0], p[j][q >> 1][1]);
         }
       }
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         const float d0 = f16_to_f32((uint16_t)(rc[j].sc[i] & 0xFFFFu));
         const float d1 = f16_to_f32((uint16_t)(rc[j].sc[i] >> 16));
-        acc[j] = __builtin_fmaf(d0, p[j][0], acc[j]);
-        acc[j] = __builtin_fmaf(d1, p[j][1], acc[j]);
+        acc[j] = __builtin_fmaf(d0, p[j][0][0] + p[j][0][1], acc[j]);
+        acc[j] = __builtin_fmaf(d1, p[j][1][0] + p[j][1][1], acc[j]);
       }
     }
     // one chunk's activations at a time: keeps the register footprint at four waves per SIMD,
@@ -378,7 +445,7 @@ STRATA_DEVICE void row_dots(const RowChunks<FMT, MC> (&rc)[NR], int nchunk, int 
 
 // Contiguous range of work items of this workgroup.
 STRATA_DEVICE void item_range(int n_items, int& begin, int& end) {
-  const int G = gridDim.x, b = blockIdx.x;
+  const int G = kGrid, b = blockIdx.x;  // the launch grid (a constant: no dispatch-packet read)
   const int per = n_items / G, extra = n_items % G;
   begin = b * per + (b < extra ? b : extra);
   end = begin + per + (b < extra ? 1 : 0);
@@ -388,77 +455,89 @@ STRATA_DEVICE void item_range(int n_items, int& begin, int& end) {
 // K1: route + gate/up GEMV + SiLU*mul.  Items (distinct expert d, block of 16 rows of I).
 
 template <int FMT, int MC>
-__global__ __launch_bounds__(kDecThreads) void decode_up_kernel(
+__global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ logits, int T, int E, int k, int H,
     int I, const uint8_t* __restrict__ gate_codes, const uint8_t* __restrict__ up_codes,
     const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales,
     uint16_t* __restrict__ a16 /* [S][I] bf16 */, int* __restrict__ ids_ws,
-    float* __restrict__ w_ws) {
+    float* __restrict__ w_ws, GlobalTable* __restrict__ gt) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ RouteTable rt;
   const int tid = threadIdx.x, S = T * k;
   const int nb = H / 32, nblk = T * nb, nchunk = H / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)T * rs * 4);
-  // the first staging pass of x (two blocks per thread), loaded ahead of the routing
-  u32x4_t xv[2][4];
+  table_clear<kUpThreads>(rt, S, E, reinterpret_cast<int*>(smem));  // visible after the routing
+  // x (one 32-value block per thread: T * H / 32 <= 1024) is loaded while the routing runs
+  u32x4_t xv[4];
+  route_tokens<kUpThreads / 64>(logits, T, E, k, rt.ids, rt.w, [&] {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)min(tid, nblk - 1) * 32);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int b = tid + p * kDecThreads;
-    if (b < nblk) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)b * 32);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xv[p][v] = src[v];
+    for (int v = 0; v < 4; ++v) xv[v] = src[v];
+  });
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < S) { ids_ws[tid] = rt.ids[tid]; w_ws[tid] = rt.w[tid]; }
+  build_table(rt, T, k, reinterpret_cast<int*>(smem));
+  if (blockIdx.x == 0) {  // the table for K2
+    if (tid == 0) gt->nd = rt.nd;
+    if (tid < rt.nd) {
+      gt->dexp[tid] = rt.dexp[tid];
+      gt->dtp[tid] = rt.dtp[tid];
+      *reinterpret_cast<uint2*>(gt->dslot[tid]) = *reinterpret_cast<const uint2*>(rt.dslot[tid]);
     }
   }
-  route_all_tokens(logits, T, E, k, rt.ids, rt.w);
-  __syncthreads();
-  if (blockIdx.x == 0)
-    for (int i = tid; i < S; i += kDecThreads) { ids_ws[i] = rt.ids[i]; w_ws[i] = rt.w[i]; }
-  build_table(rt, T, k, E, reinterpret_cast<int*>(smem));
   const int blocks = I / kUpRows;
   int it, end;
   item_range(rt.nd * blocks, it, end);
   if (it >= end) return;
   constexpr int CB = FMT == 2 ? 8 : 12;
+  constexpr int kGroups = kUpThreads / 256;  // four waves (16 rows) per item
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15;
-  const int rsub = wave * 4 + (lane >> 4);
-  RowChunks<FMT, MC> gu[2];  // (gate row, up row); four waves per SIMD hide the load latency
-  auto load_item = [&](int item) {
+  const int grp = wave >> 2, rsub = (wave & 3) * 4 + (lane >> 4);
+  // (gate row, up row) of one item in flight per wave: a second batch of loads would only queue
+  // behind the first (the load pipeline is already full), and costs registers
+  constexpr bool kTwo = false;
+  RowChunks<FMT, MC> gu[kTwo ? 2 : 1][2];
+  auto load_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
     const int d = item / blocks, n = (item % blocks) * kUpRows + rsub;
     const size_t row = (size_t)rt.dexp[d] * I + n;
-    load_row_chunks<FMT, MC>(gu[0], gate_codes + row * nb * CB, gate_scales + row * nb, nchunk, c, 16);
-    load_row_chunks<FMT, MC>(gu[1], up_codes + row * nb * CB, up_scales + row * nb, nchunk, c, 16);
+    load_row_chunks<FMT, MC>(rr[0], gate_codes + row * nb * CB, gate_scales + row * nb, nchunk, c, 16);
+    load_row_chunks<FMT, MC>(rr[1], up_codes + row * nb * CB, up_scales + row * nb, nchunk, c, 16);
   };
-  load_item(it);
-  // stage x (the routing table's scratch is dead now)
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int b = tid + p * kDecThreads;
-    if (b < nblk) stage_block<FMT>(xv[p], pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
-  }
-  for (int b = tid + 2 * kDecThreads; b < nblk; b += kDecThreads) {
-    u32x4_t v[4];
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)b * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = src[i];
-    stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
-  }
-  __syncthreads();
-  for (; it < end; ++it) {
-    const int d = it / blocks, n = (it % blocks) * kUpRows + rsub;
+  auto compute_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
+    const int d = item / blocks, n = (item % blocks) * kUpRows + rsub;
     const int Tp = rt.dtp[d];
     for (int tt = 0; tt < Tp; ++tt) {
       const int t = rt.dtok[d][tt];
       float acc[2];
-      row_dots<FMT, MC, 2>(gu, nchunk, c, 16, pairs + t * rs, cs + t * nb, acc);
+      row_dots<FMT, MC, 2>(rr, nchunk, c, 16, pairs + t * rs, cs + t * nb, acc);
       const float gs = sum16(acc[0]), us = sum16(acc[1]);
       if (c == 0) {
         const float a = gs / (1.0f + expf(-gs)) * us;
         a16[(size_t)rt.dslot[d][tt] * I + n] = f32_to_bf16(a);
       }
     }
-    if (it + 1 < end) load_item(it + 1);
+  };
+  it += grp;
+  if (it < end) load_item(it, gu[0]);
+  // stage x (the routing table's scratch is dead now); then the second item's loads
+  if (tid < nblk) stage_block<FMT>(xv, pairs + (tid / nb) * rs, cs + (tid / nb) * nb, tid % nb);
+  if constexpr (kTwo) {
+    if (it + kGroups < end) load_item(it + kGroups, gu[kTwo ? 1 : 0]);
+    __syncthreads();
+    for (; it < end; it += 2 * kGroups) {
+      compute_item(it, gu[0]);
+      if (it + 2 * kGroups < end) load_item(it + 2 * kGroups, gu[0]);
+      if (it + kGroups >= end) break;
+      compute_item(it + kGroups, gu[kTwo ? 1 : 0]);
+      if (it + 3 * kGroups < end) load_item(it + 3 * kGroups, gu[kTwo ? 1 : 0]);
+    }
+  } else {
+    __syncthreads();
+    for (; it < end; it += kGroups) {
+      compute_item(it, gu[0]);
+      if (it + kGroups < end) load_item(it + kGroups, gu[0]);
+    }
   }
 }
 
@@ -468,50 +547,94 @@ __global__ __launch_bounds__(kDecThreads) void decode_up_kernel(
 
 template <int FMT, int MC, int LPU>
 __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
-    const uint16_t* __restrict__ a16, const int* __restrict__ ids_ws, const float* __restrict__ w_ws,
+    const uint16_t* __restrict__ a16, const GlobalTable* __restrict__ gt, const float* __restrict__ w_ws,
     int T, int E, int k, int H, int I, const uint8_t* __restrict__ down_codes,
     const uint16_t* __restrict__ down_scales, float* __restrict__ y, int accumulate) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ RouteTable rt;
   __shared__ float outs[kDecMaxS * kDecMaxR];  // [slot][r]
   const int tid = threadIdx.x, S = T * k;
-  const int R = H / gridDim.x, h0 = blockIdx.x * R;
+  const int R = H / kGrid, h0 = blockIdx.x * R;
   const int nb = I / 32, nchunk = I / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)S * rs * 4);
-  if (tid < S) { rt.ids[tid] = ids_ws[tid]; rt.w[tid] = w_ws[tid]; }
+  // the routing table as K1 built it, then every slot's intermediate a: both loads are in flight
+  // together, and the weight loads below wait only for the table
+  int nd_v = 0, dexp_v = 0, dtp_v = 0;
+  float w_v = 0.0f;
+  uint2 dslot_v = {0u, 0u};
+  if (tid == 0) nd_v = gt->nd;
+  if (tid < S) {
+    w_v = w_ws[tid];
+    dexp_v = gt->dexp[tid];
+    dtp_v = gt->dtp[tid];
+    dslot_v = *reinterpret_cast<const uint2*>(gt->dslot[tid]);
+  }
+  const int nsb = S * nb;
+  u32x4_t av[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int b = min(tid + p * kDnThreads, nsb - 1);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[p][i] = src[i];
+  }
+  if (tid == 0) rt.nd = nd_v;
+  if (tid < S) {
+    rt.w[tid] = w_v;
+    rt.dexp[tid] = dexp_v;
+    rt.dtp[tid] = dtp_v;
+    *reinterpret_cast<uint2*>(rt.dslot[tid]) = dslot_v;
+  }
   __syncthreads();
-  build_table(rt, T, k, E, reinterpret_cast<int*>(smem));
   constexpr int CB = FMT == 2 ? 8 : 12;
   constexpr int kGroups = kDnThreads / LPU;
-  const int U = rt.nd * R, g = tid / LPU, j = tid % LPU;
-  RowChunks<FMT, MC> wr[2][1];
-  auto load_unit = [&](int u, RowChunks<FMT, MC> (&rr)[1]) {
-    const int d = u / R, r = u % R;
-    const size_t row = (size_t)rt.dexp[d] * H + h0 + r;
-    load_row_chunks<FMT, MC>(rr[0], down_codes + row * nb * CB, down_scales + row * nb, nchunk, j, LPU);
+  // units (distinct expert d, row pair r < RH): rows r and r + RH (the second repeats r when it
+  // falls outside the R rows), so that each activation read from LDS serves two rows
+  const int RH = (R + 1) / 2, U = rt.nd * RH, g = tid / LPU, j = tid % LPU;
+  RowChunks<FMT, MC> wr[2][2];
+  auto unit_rows = [&](int u, int& r0, int& r1) {
+    r0 = u % RH;
+    r1 = r0 + RH < R ? r0 + RH : r0;
+  };
+  auto load_unit = [&](int u, RowChunks<FMT, MC> (&rr)[2]) {
+    int r0, r1;
+    unit_rows(u, r0, r1);
+    const size_t base = (size_t)rt.dexp[u / RH] * H + h0;
+    load_row_chunks<FMT, MC>(rr[0], down_codes + (base + r0) * nb * CB, down_scales + (base + r0) * nb, nchunk, j, LPU);
+    load_row_chunks<FMT, MC>(rr[1], down_codes + (base + r1) * nb * CB, down_scales + (base + r1) * nb, nchunk, j, LPU);
   };
   if (g < U) load_unit(g, wr[0]);
   if (g + kGroups < U) load_unit(g + kGroups, wr[1]);
-  // stage every slot's intermediate a (the routing table's scratch is dead now)
-  for (int b = tid; b < S * nb; b += kDnThreads) {
-    const int s = b / nb, blk = b % nb;
+  // stage a (the routing table's scratch is dead now)
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int b = tid + p * kDnThreads;
+    if (b < nsb) stage_block<FMT>(av[p], pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+  }
+  for (int b = tid + 2 * kDnThreads; b < nsb; b += kDnThreads) {
     u32x4_t v[4];
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)s * I + blk * 32);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = src[i];
-    stage_block<FMT>(v, pairs + s * rs, cs + s * nb, blk);
+    stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
   }
   __syncthreads();
-  auto compute_unit = [&](int u, const RowChunks<FMT, MC> (&rr)[1]) {
-    const int d = u / R, r = u % R;
+  auto compute_unit = [&](int u, RowChunks<FMT, MC> (&rr)[2]) {
+    const int d = u / RH;
+    int r0, r1;
+    unit_rows(u, r0, r1);
     const int Tp = rt.dtp[d];  // uniform over the unit's lanes
     for (int tt = 0; tt < Tp; ++tt) {
       const int slot = rt.dslot[d][tt];
-      float acc[1];
-      row_dots<FMT, MC, 1>(rr, nchunk, j, LPU, pairs + slot * rs, cs + slot * nb, acc);
-      const float v = LPU == 4 ? sum4(acc[0]) : sum16(acc[0]);
-      if (j == 0) outs[slot * R + r] = v;
+      float acc[2];
+      row_dots<FMT, MC, 2>(rr, nchunk, j, LPU, pairs + slot * rs, cs + slot * nb, acc);
+      const float v0 = LPU == 4 ? sum4(acc[0]) : sum16(acc[0]);
+      const float v1 = LPU == 4 ? sum4(acc[1]) : sum16(acc[1]);
+      if (j == 0) {
+        outs[slot * R + r0] = v0;
+        outs[slot * R + r1] = v1;  // r1 == r0 rewrites the same value
+      }
     }
   };
   for (int u = g; u < U; u += 2 * kGroups) {
@@ -536,11 +659,11 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
 // Host side
 
 static size_t up_lds_bytes(int T, int E, int H) {
-  const size_t st = (size_t)T * staged_row_bytes(H), sc = (size_t)2 * E * 4;
+  const size_t st = (size_t)T * staged_row_bytes(H), sc = (size_t)E * 4;
   return st > sc ? st : sc;
 }
 static size_t dn_lds_bytes(int T, int E, int k, int I) {
-  const size_t st = (size_t)T * k * staged_row_bytes(I), sc = (size_t)2 * E * 4;
+  const size_t st = (size_t)T * k * staged_row_bytes(I), sc = (size_t)E * 4;
   return st > sc ? st : sc;
 }
 constexpr size_t kDecLdsLimit = 160 * 1024 - 16 * 1024;  // dynamic LDS beside the static tables
@@ -551,12 +674,12 @@ bool decode_fits(int T, int E, int k, int H, int I) {
   return up_lds_bytes(T, E, H) <= kDecLdsLimit && dn_lds_bytes(T, E, k, I) <= kDecLdsLimit;
 }
 
-// Workspace: ids [S] int32 | w [S] fp32 | a [S][I] bf16
+// Workspace: ids [S] int32 | w [S] fp32 | routing table | a [S][I] bf16
 size_t decode_workspace_bytes(int T, int E, int k, int H, int I) {
   (void)E; (void)H;
   const size_t S = (size_t)T * k;
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  return up(S * 4) + up(S * 4) + up(S * I * 2);
+  return up(S * 4) + up(S * 4) + up(sizeof(GlobalTable)) + up(S * I * 2);
 }
 
 template <typename K>
@@ -590,21 +713,22 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T,
   p += up(S * 4);
   float* w = w_out ? w_out : reinterpret_cast<float*>(p);
   p += up(S * 4);
+  GlobalTable* gt = reinterpret_cast<GlobalTable*>(p);
+  p += up(sizeof(GlobalTable));
   uint16_t* a16 = reinterpret_cast<uint16_t*>(p);
   const uint8_t* gc = static_cast<const uint8_t*>(gate_codes);
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
   const size_t lds_up = up_lds_bytes(T, E, H), lds_dn = dn_lds_bytes(T, E, k, I);
-  const int grid_up = 1024;  // four 4-wave workgroups per CU
   const int mc_up = (H / 64 + 15) / 16;                 // 1..4 chunks per lane (16 lanes per row)
   const int nch_dn = I / 64;
   const int lpu = nch_dn <= 16 ? 4 : 16;                 // lanes per down row
   const int mc_dn = (nch_dn + lpu - 1) / lpu;            // 1..4
 #define STRATA_UP(F, M)                                                                          \
-  decode_up_kernel<F, M><<<grid_up, kDecThreads, lds_up, s>>>(x, logits, T, E, k, H, I, gc, uc,   \
-                                                              gate_scales, up_scales, a16, ids, w)
+  decode_up_kernel<F, M><<<kGrid, kUpThreads, lds_up, s>>>(x, logits, T, E, k, H, I, gc, uc,   \
+                                                              gate_scales, up_scales, a16, ids, w, gt)
 #define STRATA_DN(F, M, L)                                                                       \
-  decode_down_kernel<F, M, L><<<kDnGrid, kDnThreads, lds_dn, s>>>(a16, ids, w, T, E, k, H, I, dc, \
+  decode_down_kernel<F, M, L><<<kGrid, kDnThreads, lds_dn, s>>>(a16, gt, w, T, E, k, H, I, dc,  \
                                                                    down_scales, y, accumulate)
 #define STRATA_DEC(F)                                                                            \
   switch (mc_up) { case 1: STRATA_UP(F, 1); break; case 2: STRATA_UP(F, 2); break;              \

@@ -187,9 +187,8 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
  * One-call layer: y (=, or += with accumulate) MoE(x).  T <= 8 runs strata_moe_decode's path
  * when the shape is within its limits; otherwise route -> permute -> expert_ffn -> combine.
  * Each opt_* pointer may be NULL; when given it receives that intermediate (same layout as the
- * staged calls).  opt_counts,
- * opt_offsets and opt_sorted_slot are only produced on the T > 8 path and must be NULL for
- * T <= 8 (STRATA_ERR_INVALID_ARGUMENT otherwise).
+ * staged calls).  opt_counts, opt_offsets and opt_sorted_slot are only produced on the T > 8
+ * path and must be NULL for T <= 8 (STRATA_ERR_INVALID_ARGUMENT otherwise).
  */
 strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, const float* logits,
                                int32_t T, int32_t k, float* y, int32_t accumulate,
