@@ -181,29 +181,22 @@ STRATA_DEVICE void select_token_wave(TokenKeys<NPL>& tk, int E, int k, int* ids_
   }
 }
 
-// Routes all T tokens into LDS, one wave per token (T <= NWAVES).  `prefetch` runs first: its
-// loads and the logit loads are in flight together.
-template <int NPL, int NWAVES, typename F>
-STRATA_DEVICE void route_tokens_npl(const float* __restrict__ logits, int T, int E, int k,
-                                    int* ids_s, float* w_s, F&& prefetch) {
-  static_assert(NWAVES >= kDecMaxT, "one wave per token");
-  const int t = threadIdx.x >> 6;
-  prefetch();
-  if (t < T) {
-    TokenKeys<NPL> tk;
-    load_token_logits<NPL>(logits + (size_t)t * E, E, tk);
-    select_token_wave<NPL>(tk, E, k, ids_s + t * k, w_s + t * k);
-  }
+// Routes token t (this wave) into LDS.
+template <int NPL>
+STRATA_DEVICE void route_token_npl(const float* __restrict__ logits, int t, int E, int k,
+                                   int* ids_s, float* w_s) {
+  TokenKeys<NPL> tk;
+  load_token_logits<NPL>(logits + (size_t)t * E, E, tk);
+  select_token_wave<NPL>(tk, E, k, ids_s + t * k, w_s + t * k);
 }
 
-template <int NWAVES, typename F>
-STRATA_DEVICE void route_tokens(const float* __restrict__ logits, int T, int E, int k, int* ids_s,
-                                float* w_s, F&& prefetch) {
-  if (E <= 64) route_tokens_npl<1, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
-  else if (E <= 128) route_tokens_npl<2, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
-  else if (E <= 256) route_tokens_npl<4, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
-  else if (E <= 512) route_tokens_npl<8, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
-  else route_tokens_npl<16, NWAVES>(logits, T, E, k, ids_s, w_s, prefetch);
+STRATA_DEVICE void route_token(const float* __restrict__ logits, int t, int E, int k, int* ids_s,
+                               float* w_s) {
+  if (E <= 64) route_token_npl<1>(logits, t, E, k, ids_s, w_s);
+  else if (E <= 128) route_token_npl<2>(logits, t, E, k, ids_s, w_s);
+  else if (E <= 256) route_token_npl<4>(logits, t, E, k, ids_s, w_s);
+  else if (E <= 512) route_token_npl<8>(logits, t, E, k, ids_s, w_s);
+  else route_token_npl<16>(logits, t, E, k, ids_s, w_s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -299,7 +292,7 @@ STRATA_DEVICE void stage_block(const u32x4_t (&v)[4], uint32_t* prow, float* cro
   crow[blk] = c;
 }
 
-inline size_t staged_row_bytes(int K) { return (size_t)(K / 64) * kChunkDwords * 4 + (size_t)(K / 32) * 4; }
+__host__ __device__ inline size_t staged_row_bytes(int K) { return (size_t)(K / 64) * kChunkDwords * 4 + (size_t)(K / 32) * 4; }
 
 // ---------------------------------------------------------------------------------------------
 // Weight rows: a lane holds chunks c0, c0 + cstep, ... (< nchunk) of a packed row, at most MC.
@@ -467,17 +460,24 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   const int nb = H / 32, nblk = T * nb, nchunk = H / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)T * rs * 4);
-  table_clear<kUpThreads>(rt, S, E, reinterpret_cast<int*>(smem));  // visible after the routing
-  // x (one 32-value block per thread: T * H / 32 <= 1024) is loaded while the routing runs
-  u32x4_t xv[4];
-  route_tokens<kUpThreads / 64>(logits, T, E, k, rt.ids, rt.w, [&] {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)min(tid, nblk - 1) * 32);
+  int* scratch = reinterpret_cast<int*>(smem + (size_t)T * staged_row_bytes(H));
+  table_clear<kUpThreads>(rt, S, E, scratch);  // visible after the barrier below
+  // waves 0 .. T-1 route one token each while the other waves stage x
+  const int nr = T * 64;
+  if (tid < nr) {
+    route_token(logits, tid >> 6, E, k, rt.ids, rt.w);
+  } else {
+    for (int b = tid - nr; b < nblk; b += kUpThreads - nr) {
+      u32x4_t v[4];
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)b * 32);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xv[v] = src[v];
-  });
+      for (int i = 0; i < 4; ++i) v[i] = src[i];
+      stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+    }
+  }
   __syncthreads();
   if (blockIdx.x == 0 && tid < S) { ids_ws[tid] = rt.ids[tid]; w_ws[tid] = rt.w[tid]; }
-  build_table(rt, T, k, reinterpret_cast<int*>(smem));
+  build_table(rt, T, k, scratch);
   if (blockIdx.x == 0) {  // the table for K2
     if (tid == 0) gt->nd = rt.nd;
     if (tid < rt.nd) {
@@ -518,13 +518,12 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
       }
     }
   };
+  // (no barrier after the first weight loads: they are accepted only as fast as data returns, so
+  // a barrier would hold every wave until the whole first batch had been issued)
   it += grp;
   if (it < end) load_item(it, gu[0]);
-  // stage x (the routing table's scratch is dead now); then the second item's loads
-  if (tid < nblk) stage_block<FMT>(xv, pairs + (tid / nb) * rs, cs + (tid / nb) * nb, tid % nb);
   if constexpr (kTwo) {
     if (it + kGroups < end) load_item(it + kGroups, gu[kTwo ? 1 : 0]);
-    __syncthreads();
     for (; it < end; it += 2 * kGroups) {
       compute_item(it, gu[0]);
       if (it + 2 * kGroups < end) load_item(it + 2 * kGroups, gu[0]);
@@ -533,7 +532,6 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
       if (it + 3 * kGroups < end) load_item(it + 3 * kGroups, gu[kTwo ? 1 : 0]);
     }
   } else {
-    __syncthreads();
     for (; it < end; it += kGroups) {
       compute_item(it, gu[0]);
       if (it + kGroups < end) load_item(it + kGroups, gu[0]);
@@ -558,33 +556,30 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
   const int nb = I / 32, nchunk = I / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)S * rs * 4);
-  // the routing table as K1 built it, then every slot's intermediate a: both loads are in flight
-  // together, and the weight loads below wait only for the table
-  int nd_v = 0, dexp_v = 0, dtp_v = 0;
-  float w_v = 0.0f;
-  uint2 dslot_v = {0u, 0u};
-  if (tid == 0) nd_v = gt->nd;
-  if (tid < S) {
-    w_v = w_ws[tid];
-    dexp_v = gt->dexp[tid];
-    dtp_v = gt->dtp[tid];
-    dslot_v = *reinterpret_cast<const uint2*>(gt->dslot[tid]);
-  }
+  // Waves 0-7 stage every slot's intermediate a while waves 8-15 fetch the routing table, then
+  // start their weight loads at once; an LDS counter (not a barrier, which would hold everyone
+  // behind the throttled weight loads) tells the waves when the staged a is complete.
+  constexpr int kStage = 512;
+  __shared__ int staged_waves;
   const int nsb = S * nb;
-  u32x4_t av[2][4];
+  u32x4_t av[4][4];
+  if (tid < kStage) {
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int b = min(tid + p * kDnThreads, nsb - 1);
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
+    for (int i = 0; i < 4; ++i) {
+      const int b = min(tid + kStage * i, nsb - 1);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[p][i] = src[i];
-  }
-  if (tid == 0) rt.nd = nd_v;
-  if (tid < S) {
-    rt.w[tid] = w_v;
-    rt.dexp[tid] = dexp_v;
-    rt.dtp[tid] = dtp_v;
-    *reinterpret_cast<uint2*>(rt.dslot[tid]) = dslot_v;
+      for (int v = 0; v < 4; ++v) av[i][v] = src[v];
+    }
+  } else {
+    const int q = tid - kStage;
+    if (q == 0) { rt.nd = gt->nd; staged_waves = 0; }
+    if (q < S) {
+      rt.w[q] = w_ws[q];
+      rt.dexp[q] = gt->dexp[q];
+      rt.dtp[q] = gt->dtp[q];
+      *reinterpret_cast<uint2*>(rt.dslot[q]) = *reinterpret_cast<const uint2*>(gt->dslot[q]);
+    }
   }
   __syncthreads();
   constexpr int CB = FMT == 2 ? 8 : 12;
@@ -604,22 +599,26 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
     load_row_chunks<FMT, MC>(rr[0], down_codes + (base + r0) * nb * CB, down_scales + (base + r0) * nb, nchunk, j, LPU);
     load_row_chunks<FMT, MC>(rr[1], down_codes + (base + r1) * nb * CB, down_scales + (base + r1) * nb, nchunk, j, LPU);
   };
+  if (tid < kStage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid + kStage * i;
+      if (b < nsb) stage_block<FMT>(av[i], pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+    }
+    for (int b = tid + 4 * kStage; b < nsb; b += kStage) {
+      u32x4_t v[4];
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = src[i];
+      stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if ((tid & 63) == 0) atomicAdd(&staged_waves, 1);
+  }
   if (g < U) load_unit(g, wr[0]);
   if (g + kGroups < U) load_unit(g + kGroups, wr[1]);
-  // stage a (the routing table's scratch is dead now)
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int b = tid + p * kDnThreads;
-    if (b < nsb) stage_block<FMT>(av[p], pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
-  }
-  for (int b = tid + 2 * kDnThreads; b < nsb; b += kDnThreads) {
-    u32x4_t v[4];
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = src[i];
-    stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
-  }
-  __syncthreads();
+  while (__hip_atomic_load(&staged_waves, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kStage / 64)
+    __builtin_amdgcn_s_sleep(1);
   auto compute_unit = [&](int u, RowChunks<FMT, MC> (&rr)[2]) {
     const int d = u / RH;
     int r0, r1;
@@ -659,8 +658,7 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
 // Host side
 
 static size_t up_lds_bytes(int T, int E, int H) {
-  const size_t st = (size_t)T * staged_row_bytes(H), sc = (size_t)E * 4;
-  return st > sc ? st : sc;
+  return (size_t)T * staged_row_bytes(H) + (size_t)E * 4;
 }
 static size_t dn_lds_bytes(int T, int E, int k, int I) {
   const size_t st = (size_t)T * k * staged_row_bytes(I), sc = (size_t)E * 4;
