@@ -54,6 +54,47 @@ def event_time_ms(fn, steps, stream):
     return start.elapsed_time(end)
 
 
+def source_sha256(name):
+    import hashlib
+
+    path = os.path.join(ROOT, "bit_expert_ffn_fp32_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(summary, source):
+    """HBM bytes per call from a committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's counters), or None when the summary is missing or was taken on other
+    kernel source."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != source_sha256(source):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mb, stream):
+    """A plain device-to-device copy of known size, for scaling the memory counters."""
+    import torch
+
+    n = mb * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {n} bytes")
+
+
 def bench_decode(args, stream):
     import torch
 
@@ -77,23 +118,60 @@ def bench_decode(args, stream):
         touched.append(len(np.unique(ids)))
     bytes_per_layer = [n * s.expert_bytes for n in touched]
 
-    def step(i):
+    def step(i, strm):
         L = layers[i % n_layers]
-        sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=stream)
+        sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=strm)
 
+    # Eager launches: each call costs ~20 us of host time (Python + ctypes + two kernel launches),
+    # which is of the order of the GPU time, so the timed loop replays a HIP graph of one pass over
+    # the resident layers instead; the eager rate is reported beside it.
     for i in range(args.warmup):
-        step(i)
-    ms = event_time_ms(step, args.steps, stream)
-    ms_per_step = ms / args.steps
-    algo_bytes = float(np.mean([bytes_per_layer[i % n_layers] for i in range(args.steps)]))
+        step(i, stream)
+    eager_ms = event_time_ms(lambda i: step(i, stream), args.steps, stream) / args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(n_layers):
+            step(i, side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+
+    def capture(first, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for i in range(first, first + count):
+                step(i, cap)
+        return g
+
+    # exactly args.steps steps: full passes over the layers, then the remainder
+    full, rem = divmod(args.steps, n_layers)
+    graph = capture(0, n_layers)
+    tail = capture(0, rem) if rem else None
+    for _ in range(2):
+        graph.replay()
+    steps = args.steps
+
+    def timed(r):
+        if r < full:
+            graph.replay()
+        else:
+            tail.replay()
+
+    ms = event_time_ms(timed, full + (1 if rem else 0), stream)
+    ms_per_step = ms / steps
+    algo_bytes = (full * sum(bytes_per_layer) + sum(bytes_per_layer[:rem])) / steps
     achieved_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
     return {
         "ms_per_step": ms_per_step,
+        "steps": steps,
+        "eager_ms_per_step": eager_ms,
         "value": s.T / (ms_per_step * 1e-3),
         "touched_experts_mean": float(np.mean(touched)),
         "bytes_per_layer": algo_bytes,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("decode_t4_traffic.txt", "decode.hip"),
                      "kernel": "strata_moe_decode (route, gate/up GEMV, down GEMV, combine)",
                      "unit_of_work": "touched experts' packed bytes (2,211,840 B each) per layer"},
         "layers": layers,
@@ -153,7 +231,8 @@ def bench_prefill(args, stream):
         "layer_tflops": tflops_layer,
         "layer_frac": tflops_layer / MFMA_F16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": tflops_ffn, "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops_ffn / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": tflops_ffn / MFMA_F16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("prefill_t8192_traffic.txt", "prefill.hip"),
                      "kernel": "strata_moe_expert_ffn (x to fp16, gate/up GEMM, down GEMM)",
                      "ms_per_call": ms_ffn, "unit_of_work": "6*T*k*H*I FLOP per call"},
         "dtype": "f16 MFMA, fp32 accumulate",
@@ -172,6 +251,8 @@ def main():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="also run a plain copy of this many MiB (for scaling memory counters)")
     args = p.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every layer's "
@@ -188,7 +269,8 @@ def main():
     torch.cuda.init()
     stream = torch.cuda.current_stream()
     dec = bench_decode(args, stream)
-    log(f"decode: {dec['ms_per_step'] * 1e3:.2f} us/layer, {dec['value']:.4g} layer-tokens/s, "
+    log(f"decode: {dec['ms_per_step'] * 1e3:.2f} us/layer (graph replay; eager "
+        f"{dec['eager_ms_per_step'] * 1e3:.2f} us), {dec['value']:.4g} layer-tokens/s, "
         f"{dec['roofline']['achieved']:.0f} GB/s ({dec['roofline']['frac'] * 100:.1f}% of HBM peak)")
     layers = dec.pop("layers")
     pre = None
@@ -200,6 +282,8 @@ def main():
         log(f"prefill: {pre['ms_per_step']:.3f} ms/layer, {pre['value']:.4g} tokens/s, layer "
             f"{pre['layer_tflops']:.0f} TFLOP/s; expert FFN {pre['roofline']['achieved']:.0f} TFLOP/s "
             f"({pre['roofline']['frac'] * 100:.1f}% of MFMA peak)")
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb, stream)
     cpu = None
     if not args.no_cpu:
         s = mi.DECODE
@@ -224,9 +308,10 @@ def main():
         "value": dec["value"],
         "unit": "layer-tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": dec["steps"],
         "warmup": args.warmup,
         "ms_per_step": dec["ms_per_step"],
+        "eager_ms_per_step": dec["eager_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -1,0 +1,40 @@
+"""Graph capture of the layer entry point: a captured decode-path call and a captured prefill-path
+call, each replayed several times with other GPU work and synchronizations in between, give
+exactly the eager result on every replay (the benchmark times graph replays)."""
+import pytest
+import torch
+
+import bit_expert_ffn_fp32_amd as sm
+import moe_inputs as mi
+from gpu_helpers import Layer, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_graph_replay_matches_eager(T):
+    s = mi.TINY
+    L = Layer(s, T=T)
+    ws = L.workspace()
+    y_eager = torch.empty((T, s.H), dtype=torch.float32, device=dev())
+    sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y_eager, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.zeros_like(y_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws,
+                            stream=torch.cuda.current_stream())
+    for rep in range(3):
+        y.fill_(float("nan"))
+        scratch = torch.randn(1 << 16, device=dev()).sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {rep} differs from the eager result"
+        del scratch
