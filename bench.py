@@ -178,18 +178,20 @@ def bench_decode(args, stream):
     }
 
 
-def bench_prefill(args, stream):
+def bench_prefill(args, stream, name):
     import torch
 
     import bit_expert_ffn_fp32_amd as sm
     import moe_inputs as mi
     from gpu_helpers import Layer
 
-    s = mi.SHAPES[args.prefill_workload]
+    s = mi.SHAPES[name]
     t0 = time.time()
     L = Layer(s, seed=args.seed)
     del L.w_np
-    log(f"prefill: layer generated and uploaded in {time.time() - t0:.1f}s")
+    log(f"{name}: layer generated and uploaded in {time.time() - t0:.1f}s")
+    ids_host = np.argsort(-L.l_np.astype(np.float64), axis=1, kind="stable")[:, :s.k]
+    touched = len(np.unique(ids_host))
     ws = L.workspace()
     y = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
     S = s.T * s.k
@@ -221,9 +223,12 @@ def bench_prefill(args, stream):
     ms_ffn = event_time_ms(ffn, steps, stream) / steps
     tflops_ffn = flops / (ms_ffn * 1e-3) / 1e12
     tflops_layer = flops / (ms_per_step * 1e-3) / 1e12
+    traffic = measured_traffic("prefill_t8192_traffic.txt", "prefill.hip") if name == "prefill" else None
     return {
         "workload": f"{s.name} T={s.T} H={s.H} E={s.E} k={s.k} I={s.I} "
-                    f"{'Q3' if s.fmt == 3 else 'Q2'}-block experts",
+                    f"{'Q3' if s.fmt == 3 else 'Q2'}-block experts"
+                    + (", Zipf(1.1)-skewed routing" if s.zipf else ""),
+        "touched_experts": touched,
         "value": s.T / (ms_per_step * 1e-3),
         "unit": "layer-tokens/s",
         "ms_per_step": ms_per_step,
@@ -232,11 +237,74 @@ def bench_prefill(args, stream):
         "layer_frac": tflops_layer / MFMA_F16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": tflops_ffn, "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops_ffn / MFMA_F16_PEAK_TFLOPS,
-                     "traffic": measured_traffic("prefill_t8192_traffic.txt", "prefill.hip"),
+                     "traffic": traffic,
                      "kernel": "strata_moe_expert_ffn (x to fp16, gate/up GEMM, down GEMM)",
                      "ms_per_call": ms_ffn, "unit_of_work": "6*T*k*H*I FLOP per call"},
         "dtype": "f16 MFMA, fp32 accumulate",
     }
+
+
+def bench_stack(args, stream):
+    """48-layer expert stack, all experts resident: h <- h + MoE(RMSNorm(h)) per layer with fresh
+    seeded logits, one T=4 decode step and one T=8192 prefill chunk through all layers."""
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import to_dev
+
+    sd, sp = mi.STACK_DECODE, mi.STACK_PREFILL
+    n = args.stack_layers
+    t0 = time.time()
+    weights, lg_dec, lg_pre, touched = [], [], [], []
+    for l in range(n):
+        w_np = mi.make_weights(sp, args.seed, l)
+        weights.append(sm.Weights.from_numpy(w_np, "cuda"))
+        del w_np
+        ld = mi.make_logits(sd, args.seed, l)
+        ids = np.argsort(-ld.astype(np.float64), axis=1, kind="stable")[:, :sd.k]
+        touched.append(len(np.unique(ids)))
+        lg_dec.append(to_dev(ld))
+        lg_pre.append(to_dev(mi.make_logits(sp, args.seed, l)))
+    log(f"stack: {n} layers generated and uploaded in {time.time() - t0:.1f}s")
+    out = {"layers": n}
+    for s, lg, tag in ((sd, lg_dec, "decode"), (sp, lg_pre, "prefill")):
+        h = to_dev(mi.make_h0(s, args.seed))
+        x = torch.empty((s.T, s.H), dtype=torch.int16, device="cuda")
+        ws = sm.alloc_workspace(sm.workspace_bytes(s.T, s.E, s.k, s.H, s.I), "cuda")
+
+        def step(strm):
+            for l in range(n):
+                sm.strata_moe_rmsnorm(h, x, 1e-6, stream=strm)
+                sm.strata_moe_layer(weights[l], x, lg[l], s.k, h, accumulate=True, workspace=ws,
+                                    stream=strm)
+
+        step(stream)
+        steps = args.stack_steps if tag == "decode" else max(1, args.stack_steps // 10)
+        if tag == "decode":  # replay a graph of the 48-layer step (launch-bound otherwise)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                step(side)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(torch.cuda.current_stream())
+            g.replay()
+            ms = event_time_ms(lambda i: g.replay(), steps, stream) / steps
+            gbs = sum(touched) * s.expert_bytes / (ms * 1e-3) / 1e9
+            out[tag] = {"T": s.T, "ms_per_step": ms, "stack_tokens_per_s": s.T / (ms * 1e-3),
+                        "steps": steps, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                        "touched_experts_total": sum(touched)}
+        else:
+            ms = event_time_ms(lambda i: step(stream), steps, stream) / steps
+            tf = n * 6.0 * s.T * s.k * s.H * s.I / (ms * 1e-3) / 1e12
+            out[tag] = {"T": s.T, "ms_per_step": ms, "stack_tokens_per_s": s.T / (ms * 1e-3),
+                        "steps": steps, "achieved_TFLOPs": tf, "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
+        log(f"stack {tag}: {ms:.3f} ms per {n}-layer step, {s.T / (ms * 1e-3):.4g} stack-tokens/s")
+        del h, x, ws
+    return out
 
 
 def main():
@@ -247,7 +315,10 @@ def main():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--decode-layers", type=int, default=16)
     p.add_argument("--prefill-steps", type=int, default=10)
-    p.add_argument("--prefill-workload", default="prefill", choices=["prefill", "skewed"])
+    p.add_argument("--no-skewed", action="store_true")
+    p.add_argument("--no-stack", action="store_true")
+    p.add_argument("--stack-layers", type=int, default=48)
+    p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
@@ -273,15 +344,24 @@ def main():
         f"{dec['eager_ms_per_step'] * 1e3:.2f} us), {dec['value']:.4g} layer-tokens/s, "
         f"{dec['roofline']['achieved']:.0f} GB/s ({dec['roofline']['frac'] * 100:.1f}% of HBM peak)")
     layers = dec.pop("layers")
-    pre = None
+    pre = skw = None
     if not args.no_prefill:
         for L in layers:
             del L.w
         torch.cuda.empty_cache()
-        pre = bench_prefill(args, stream)
+        pre = bench_prefill(args, stream, "prefill")
         log(f"prefill: {pre['ms_per_step']:.3f} ms/layer, {pre['value']:.4g} tokens/s, layer "
             f"{pre['layer_tflops']:.0f} TFLOP/s; expert FFN {pre['roofline']['achieved']:.0f} TFLOP/s "
             f"({pre['roofline']['frac'] * 100:.1f}% of MFMA peak)")
+        if not args.no_skewed:
+            skw = bench_prefill(args, stream, "skewed")
+            log(f"skewed: {skw['ms_per_step']:.3f} ms/layer, {skw['touched_experts']} experts touched, "
+                f"expert FFN {skw['roofline']['achieved']:.0f} TFLOP/s")
+            torch.cuda.empty_cache()
+    stack = None
+    if not args.no_stack:
+        stack = bench_stack(args, stream)
+        torch.cuda.empty_cache()
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb, stream)
     cpu = None
@@ -328,6 +408,10 @@ def main():
     }
     if pre is not None:
         line["prefill"] = pre
+    if skw is not None:
+        line["skewed"] = skw
+    if stack is not None:
+        line["stack"] = stack
     print(json.dumps(line), flush=True)
 
 
