@@ -22,7 +22,7 @@ Q2, Q3 = 2, 3
 CODE_BYTES = {Q2: 8, Q3: 12}
 
 EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "strata_moe_combine",
-           "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm",
+           "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
            "strata_status_string"]
 
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "strata_moe_decode": [W, vp, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp],
             "strata_moe_layer": [W, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "strata_moe_rmsnorm": [vp, i32, i32, ctypes.c_float, vp, vp],
+            "strata_moe_pack_matrix": [i32, i32, i32, i32, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -122,11 +123,21 @@ class Weights:
 
     @staticmethod
     def from_numpy(w: dict, device="cuda") -> "Weights":
-        def t(a):
-            return torch.from_numpy(a).to(device)
-        return Weights(w["fmt"], w["E"], w["H"], w["I"], t(w["gate_codes"]), t(w["up_codes"]),
-                       t(w["down_codes"]), t(w["gate_scales"].view("int16")),
-                       t(w["up_scales"].view("int16")), t(w["down_scales"].view("int16")))
+        """Uploads row-major arrays ([E][rows][K/32][cb] codes, [E][rows][K/32] fp16 scales) and
+        repacks them on the device into the tiled layout the kernels read."""
+        fmt, E, H, I = w["fmt"], w["E"], w["H"], w["I"]
+
+        def packed(codes, scales, rows, K):
+            c = torch.from_numpy(codes).to(device)
+            s_ = torch.from_numpy(scales.view("int16")).to(device)
+            tc, ts = torch.empty_like(c), torch.empty_like(s_)
+            strata_moe_pack_matrix(fmt, E, rows, K, c, s_, tc, ts)
+            return tc, ts
+
+        gc, gs = packed(w["gate_codes"], w["gate_scales"], I, H)
+        uc, us = packed(w["up_codes"], w["up_scales"], I, H)
+        dc, ds = packed(w["down_codes"], w["down_scales"], H, I)
+        return Weights(fmt, E, H, I, gc, uc, dc, gs, us, ds)
 
 
 def permute_workspace_bytes(T: int, E: int, k: int) -> int:
@@ -186,6 +197,13 @@ def strata_moe_layer(w: Weights, x, logits, k, y, accumulate=False, topk_ids=Non
         ctypes.byref(cw), _p(x), _p(logits), x.shape[0], k, _p(y), int(accumulate), _p(topk_ids),
         _p(topk_w), _p(counts), _p(offsets), _p(sorted_slot), _p(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+
+
+def strata_moe_pack_matrix(fmt, n_mat, rows, K, codes, scales, tiled_codes, tiled_scales,
+                           stream=None) -> None:
+    _check("strata_moe_pack_matrix", lib().strata_moe_pack_matrix(
+        fmt, n_mat, rows, K, _p(codes), _p(scales), _p(tiled_codes), _p(tiled_scales),
+        _stream(stream)))
 
 
 def strata_moe_rmsnorm(h, x, eps=1e-6, stream=None) -> None:

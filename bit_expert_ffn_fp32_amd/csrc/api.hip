@@ -299,6 +299,28 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   return from_hip(e);
 }
 
+strata_status strata_moe_pack_matrix(int32_t fmt, int32_t n_mat, int32_t rows, int32_t K,
+                                    const void* codes, const uint16_t* scales, void* tiled_codes,
+                                    uint16_t* tiled_scales, hipStream_t stream) {
+  if (fmt != STRATA_Q2_B32 && fmt != STRATA_Q3_B32) return STRATA_ERR_INVALID_ARGUMENT;
+  if (n_mat < 1 || rows < 1 || K < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if (rows % 4 || K % 64) return STRATA_ERR_UNSUPPORTED;
+  if ((int64_t)n_mat * rows * (K / 64) > (int64_t)INT32_MAX * 64) return STRATA_ERR_UNSUPPORTED;
+  const void* ptrs[4] = {codes, scales, tiled_codes, tiled_scales};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  const size_t cb = fmt == STRATA_Q2_B32 ? 8 : 12;
+  const size_t nblk = (size_t)n_mat * rows * (K / 32);
+  const uintptr_t c0 = (uintptr_t)codes, c1 = c0 + nblk * cb, t0 = (uintptr_t)tiled_codes,
+                  t1 = t0 + nblk * cb;
+  const uintptr_t s0 = (uintptr_t)scales, s1 = s0 + nblk * 2, u0 = (uintptr_t)tiled_scales,
+                  u1 = u0 + nblk * 2;
+  if ((c0 < t1 && t0 < c1) || (s0 < u1 && u0 < s1) || (c0 < u1 && u0 < c1) || (s0 < t1 && t0 < s1))
+    return STRATA_ERR_INVALID_ARGUMENT;  // overlapping source and destination
+  return from_hip(strata::launch_pack(fmt, n_mat, rows, K, codes, scales, tiled_codes,
+                                      tiled_scales, stream));
+}
+
 strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
                                  hipStream_t stream) {
   if (T < 0 || H < 1 || !(eps >= 0.0f)) return STRATA_ERR_INVALID_ARGUMENT;

@@ -295,7 +295,20 @@ STRATA_DEVICE void stage_block(const u32x4_t (&v)[4], uint32_t* prow, float* cro
 __host__ __device__ inline size_t staged_row_bytes(int K) { return (size_t)(K / 64) * kChunkDwords * 4 + (size_t)(K / 32) * 4; }
 
 // ---------------------------------------------------------------------------------------------
-// Weight rows: a lane holds chunks c0, c0 + cstep, ... (< nchunk) of a packed row, at most MC.
+// Weight rows in the tiled layout: a row's chunk ch (reduction indices 64 ch .. 64 ch + 63, two
+// blocks) sits in stage ch of its 4-row group, the stages of one group being consecutive
+// (4 rows x 2 cb code bytes and 4 x 2 fp16 scales each).  A lane holds chunks c0, c0 + cstep, ...
+// (< nchunk) of one row, at most MC.
+
+template <int FMT>
+STRATA_DEVICE const uint8_t* tiled_row_codes(const uint8_t* codes, size_t row, int nchunk) {
+  constexpr int CB = FMT == 2 ? 8 : 12;
+  return codes + (row >> 2) * nchunk * (8 * CB) + (row & 3) * (2 * CB);
+}
+
+STRATA_DEVICE const uint16_t* tiled_row_scales(const uint16_t* scales, size_t row, int nchunk) {
+  return scales + (row >> 2) * nchunk * 8 + (row & 3) * 2;
+}
 
 template <int FMT, int MC>
 struct RowChunks {
@@ -304,23 +317,26 @@ struct RowChunks {
   uint32_t sc[MC];                                 // the chunk's two fp16 block scales
 };
 
+// row_codes / row_scales: the row's chunk 0 (tiled_row_codes / tiled_row_scales).
 template <int FMT, int MC>
 STRATA_DEVICE void load_row_chunks(RowChunks<FMT, MC>& rc, const uint8_t* row_codes,
                                    const uint16_t* row_scales, int nchunk, int c0, int cstep) {
+  constexpr int CB = FMT == 2 ? 8 : 12;
 #pragma unroll
   for (int i = 0; i < MC; ++i) {
     const int ch = c0 + cstep * i;
     if (ch < nchunk) {
+      const uint8_t* cp = row_codes + (size_t)ch * (8 * CB);
       if constexpr (FMT == 2) {
-        const u32x4_t v = reinterpret_cast<const u32x4_t*>(row_codes)[ch];
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cp);
         rc.w[i][0] = v[0]; rc.w[i][1] = v[1]; rc.w[i][2] = v[2]; rc.w[i][3] = v[3];
       } else {
-        const uint2* p = reinterpret_cast<const uint2*>(row_codes + (size_t)ch * 24);
+        const uint2* p = reinterpret_cast<const uint2*>(cp);
         const uint2 a = p[0], b = p[1], d = p[2];
         rc.w[i][0] = a.x; rc.w[i][1] = a.y; rc.w[i][2] = b.x; rc.w[i][3] = b.y;
         rc.w[i][4] = d.x; rc.w[i][5] = d.y;
       }
-      rc.sc[i] = reinterpret_cast<const uint32_t*>(row_scales)[ch];
+      rc.sc[i] = *reinterpret_cast<const uint32_t*>(row_scales + (size_t)ch * 8);
     }
   }
 }
@@ -501,8 +517,10 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   auto load_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
     const int d = item / blocks, n = (item % blocks) * kUpRows + rsub;
     const size_t row = (size_t)rt.dexp[d] * I + n;
-    load_row_chunks<FMT, MC>(rr[0], gate_codes + row * nb * CB, gate_scales + row * nb, nchunk, c, 16);
-    load_row_chunks<FMT, MC>(rr[1], up_codes + row * nb * CB, up_scales + row * nb, nchunk, c, 16);
+    load_row_chunks<FMT, MC>(rr[0], tiled_row_codes<FMT>(gate_codes, row, nchunk),
+                             tiled_row_scales(gate_scales, row, nchunk), nchunk, c, 16);
+    load_row_chunks<FMT, MC>(rr[1], tiled_row_codes<FMT>(up_codes, row, nchunk),
+                             tiled_row_scales(up_scales, row, nchunk), nchunk, c, 16);
   };
   auto compute_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
     const int d = item / blocks, n = (item % blocks) * kUpRows + rsub;
@@ -596,8 +614,10 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
     int r0, r1;
     unit_rows(u, r0, r1);
     const size_t base = (size_t)rt.dexp[u / RH] * H + h0;
-    load_row_chunks<FMT, MC>(rr[0], down_codes + (base + r0) * nb * CB, down_scales + (base + r0) * nb, nchunk, j, LPU);
-    load_row_chunks<FMT, MC>(rr[1], down_codes + (base + r1) * nb * CB, down_scales + (base + r1) * nb, nchunk, j, LPU);
+    load_row_chunks<FMT, MC>(rr[0], tiled_row_codes<FMT>(down_codes, base + r0, nchunk),
+                             tiled_row_scales(down_scales, base + r0, nchunk), nchunk, j, LPU);
+    load_row_chunks<FMT, MC>(rr[1], tiled_row_codes<FMT>(down_codes, base + r1, nchunk),
+                             tiled_row_scales(down_scales, base + r1, nchunk), nchunk, j, LPU);
   };
   if (tid < kStage) {
 #pragma unroll

@@ -24,6 +24,10 @@ inline int64_t max_chunks(int64_t S, int64_t E) {
   return S / kChunkRows + (E < S ? E : S) + 1;
 }
 
+// Row-major -> tiled weight layout for n_mat matrices of R x K (R a multiple of 4, K of 64).
+hipError_t launch_pack(int fmt, int n_mat, int R, int K, const void* codes, const uint16_t* scales,
+                       void* tcodes, uint16_t* tscales, hipStream_t s);
+
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
                         hipStream_t s);
 

@@ -44,9 +44,9 @@ template <int FMT, int NF>
 struct Pipe {
   static constexpr int kCB = FMT == 2 ? 8 : 12;
   static constexpr int kXBytes = NF * 32 * kKS * 2;         // activation tile
-  static constexpr int kWCodeBytes = 256 * 2 * kCB;          // 256 weight rows x 2 blocks
+  static constexpr int kWCodeBytes = 4 * 128 * kCB;          // 4 weight tiles x 64 rows x 2 blocks
   static constexpr int kStage = kXBytes + kWCodeBytes + kWScaleBytes;
-  static constexpr int kPer = NF + (FMT == 2 ? 1 : 6) + 1;   // copy instructions per wave per stage
+  static constexpr int kPer = NF + (FMT == 2 ? 1 : 2) + 1;   // copy instructions per wave per stage
   static constexpr int kByLds = kLdsBudget / kStage;
   static constexpr int kByCnt = 63 / kPer + 1;               // (buffers - 2) * kPer <= 63, with margin
   static constexpr int kNBuf = kByLds < kByCnt ? (kByLds < 8 ? kByLds : 8) : (kByCnt < 8 ? kByCnt : 8);
@@ -93,15 +93,26 @@ STRATA_DEVICE Q2Tab q2_table(uint16_t dbits) {
   return Q2Tab{__builtin_amdgcn_perm(u23, u01, 0x06040200u), __builtin_amdgcn_perm(u23, u01, 0x07050301u)};
 }
 
+// The selector constants of q2_decode, held in VGPRs so that each selector is one v_and_or_b32
+// (gfx9 VOP3 takes no literal operand and reads at most one scalar register).
+struct Q2Sel {
+  uint32_t mask, base;
+};
+
+STRATA_DEVICE Q2Sel q2_sel() {
+  Q2Sel k{0x03030303u, 0x04000400u};
+  asm volatile("" : "+v"(k.mask), "+v"(k.base));
+  return k;
+}
+
 // code: the block's 8 code bytes; bytes 2s, 2s+1 hold the codes of step s.
-STRATA_DEVICE half8_t q2_decode(uint32_t w0, uint32_t w1, int s, const Q2Tab& tab) {
+STRATA_DEVICE half8_t q2_decode(uint32_t w0, uint32_t w1, int s, const Q2Tab& tab, const Q2Sel& k) {
   const uint32_t word = (s >> 1) ? w1 : w0;
   const uint32_t X = __builtin_amdgcn_perm(word, word, (s & 1) ? 0x03030202u : 0x01010000u);
-  const uint32_t mask = 0x03030303u, base = 0x04000400u;
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t sel = ((X >> (2 * i)) & mask) | (base & ~mask);
+    const uint32_t sel = ((X >> (2 * i)) & k.mask) | k.base;
     r[i] = __builtin_amdgcn_perm(tab.hi, tab.lo, sel);
   }
   return __builtin_bit_cast(half8_t, r);
@@ -157,60 +168,149 @@ STRATA_DEVICE bool pick_unit(const Chunk* chunks, const int* n_chunks, int n_sli
 //  * activation tile: NF*32 rows x 64 fp16 = 8 pieces of 16 B per row; piece c of row r sits in
 //    slot c ^ (r % 8) so that a fragment read (8 consecutive rows, one piece each, per LDS cycle)
 //    hits distinct banks; wave w copies the 8-row groups q = w, w+4, ...;
-//  * weights: the 64 rows of each wave (32 of stream 0, 32 of stream 1), both blocks' codes and
-//    scales of the stage.
+//  * weights: the unit's 256 rows are four 64-row weight tiles, one per wave; per stage a wave
+//    copies its tile's codes (64 rows x 2 blocks, 1 or 1.5 KB) and scales (256 B) into the
+//    tile's LDS slot as [64 rows][2 blocks][cb] and [64 rows][2] fp16.  In the tiled weight
+//    layout those bytes are 16 contiguous pieces (one per 4-row group) of 64 / 96 bytes of codes
+//    and 16 bytes of scales.
 // Stages are issued kPD ahead into a ring of kNBuf buffers; each stage waits on the vector-memory
 // counter for its own copies and a barrier makes them visible to all waves.
 
-// The weight row this lane copies: lane l of a wave copies row l % 32 of stream l / 32.
-struct WeightRows {
-  const uint8_t* code_row;
-  const uint16_t* scale_row;
+// This lane's stage-0 source addresses for the 64-row weight tile its wave copies.  Codes: lane l
+// copies bytes 16 l .. 16 l + 15 of the tile's [64][2][cb] bytes (and, for 3-bit, l < 32 also
+// 1024 + 16 l ..); scales: bytes 4 l .. 4 l + 3 of its [64][2] fp16.  Byte b of a tile-stage sits
+// in 4-row group b / (8 cb) at offset b % (8 cb); successive stages of a group are 8 cb bytes
+// (16 bytes of scales) apart.
+struct WeightTile {
+  const uint8_t* codes0;
+  const uint8_t* codes1;
+  const uint16_t* scales;
 };
 
 template <int FMT>
-STRATA_DEVICE WeightRows weight_rows(const uint8_t* codes0, const uint8_t* codes1,
-                                     const uint16_t* scales0, const uint16_t* scales1, int nb) {
-  constexpr int CB = FMT == 2 ? 8 : 12;
-  const int lane = threadIdx.x & 63, row = lane & 31;
-  const bool second = lane >= 32;
-  WeightRows wr;
-  wr.code_row = (second ? codes1 : codes0) + (size_t)row * nb * CB;
-  wr.scale_row = (second ? scales1 : scales0) + (size_t)row * nb;
-  return wr;
+STRATA_DEVICE WeightTile weight_tile(const uint8_t* codes, const uint16_t* scales, size_t row0, int nkt) {
+  constexpr int GB = 8 * (FMT == 2 ? 8 : 12);  // code bytes of one 4-row group stage
+  const int lane = threadIdx.x & 63;
+  const size_t g0 = row0 >> 2;
+  const int b0 = lane * 16, b1 = 1024 + lane * 16;
+  WeightTile wt;
+  wt.codes0 = codes + (g0 + b0 / GB) * nkt * GB + b0 % GB;
+  wt.codes1 = codes + (g0 + (FMT == 3 && lane < 32 ? b1 / GB : 0)) * nkt * GB + (FMT == 3 && lane < 32 ? b1 % GB : 0);
+  wt.scales = scales + (g0 + (lane >> 2)) * nkt * 8 + (lane & 3) * 2;
+  return wt;
 }
 
+// Copies c0 .. c1 - 1 of this wave's kPer copies of stage j: the NF activation groups, then the
+// weight tile's codes (one or two), then its scales.
 template <int FMT, int NF>
-STRATA_DEVICE void issue_stage(uint8_t* stage, const uint16_t* __restrict__ src, const int (&xoff)[NF],
-                               const WeightRows& wr, int j) {
-  constexpr int CB = FMT == 2 ? 8 : 12;
+STRATA_DEVICE void issue_copies(uint8_t* stage, const uint16_t* __restrict__ src, const int (&xoff)[NF],
+                                const WeightTile& wt, int j, int c0, int c1) {
+  constexpr int TB = 128 * (FMT == 2 ? 8 : 12);  // code bytes of one 64-row tile-stage
+  constexpr int GB = TB / 16;                     // code bytes of one 4-row group stage
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k0 = j * kKS;
 #pragma unroll
   for (int g = 0; g < NF; ++g) {
+    if (g < c0 || g >= c1) continue;
     const int q = wave + 4 * g;
     __builtin_amdgcn_global_load_lds(src + xoff[g] + k0, stage + q * 1024, 16, 0, 0);
   }
-  const uint8_t* crow = wr.code_row + 2 * j * CB;
-  uint8_t* carea = stage + Pipe<FMT, NF>::kXBytes + wave * 64 * 2 * CB;
-  if constexpr (FMT == 2) {
-    __builtin_amdgcn_global_load_lds(crow, carea, 16, 0, 0);  // [64 rows][2 blocks][8 B]
-  } else {
-    // [2 blocks][3 words][64 rows] dwords
-#pragma unroll
-    for (int w = 0; w < 6; ++w)
-      __builtin_amdgcn_global_load_lds(crow + 4 * w, carea + w * 256, 4, 0, 0);
+  uint8_t* carea = stage + Pipe<FMT, NF>::kXBytes + wave * TB;
+  if (NF >= c0 && NF < c1) __builtin_amdgcn_global_load_lds(wt.codes0 + (size_t)j * GB, carea, 16, 0, 0);
+  constexpr int kS = NF + (FMT == 2 ? 1 : 2);  // index of the scale copy
+  if constexpr (FMT == 3) {
+    if (NF + 1 >= c0 && NF + 1 < c1 && lane < 32)
+      __builtin_amdgcn_global_load_lds(wt.codes1 + (size_t)j * GB, carea + 1024, 16, 0, 0);
   }
-  const uint16_t* srow = wr.scale_row + 2 * j;
-  __builtin_amdgcn_global_load_lds(srow, stage + Pipe<FMT, NF>::kXBytes + Pipe<FMT, NF>::kWCodeBytes + wave * 256, 4, 0, 0);
+  if (kS >= c0 && kS < c1)
+    __builtin_amdgcn_global_load_lds(wt.scales + (size_t)j * 8,
+                                     stage + Pipe<FMT, NF>::kXBytes + Pipe<FMT, NF>::kWCodeBytes + wave * 256, 4, 0, 0);
 }
 
 template <int FMT, int NF>
-STRATA_DEVICE void gemm_core(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const uint16_t* __restrict__ src,
-                             int ld, int K, const int* rows_lds, const WeightRows& wr,
-                             uint8_t* lds) {
+STRATA_DEVICE void issue_stage(uint8_t* stage, const uint16_t* __restrict__ src, const int (&xoff)[NF],
+                               const WeightTile& wt, int j) {
+  issue_copies<FMT, NF>(stage, src, xoff, wt, j, 0, Pipe<FMT, NF>::kPer);
+}
+
+// Per-lane weight state of one stage: the lane's block (hh) of its row in each stream (row ri of
+// LDS weight tile ti) and what the decoder derives from the block scale.
+template <int FMT>
+struct StageWeights {
+  uint32_t cw0[3], cw1[3];
+  Q2Tab t0, t1;
+  float f0, f1;
+};
+
+template <int FMT, int NF>
+STRATA_DEVICE void load_stage_weights(StageWeights<FMT>& sw, const uint8_t* stage, int ti0, int ti1,
+                                      int ri0, int ri1, int hh) {
   using P = Pipe<FMT, NF>;
   constexpr int CB = P::kCB;
+  const uint8_t* carea = stage + P::kXBytes;
+  const uint16_t* sarea = reinterpret_cast<const uint16_t*>(stage + P::kXBytes + P::kWCodeBytes);
+  const uint32_t* p0 = reinterpret_cast<const uint32_t*>(carea + ti0 * 128 * CB + ri0 * 2 * CB + hh * CB);
+  const uint32_t* p1 = reinterpret_cast<const uint32_t*>(carea + ti1 * 128 * CB + ri1 * 2 * CB + hh * CB);
+  if constexpr (FMT == 2) {
+    const uint2 v0 = *reinterpret_cast<const uint2*>(p0), v1 = *reinterpret_cast<const uint2*>(p1);
+    sw.cw0[0] = v0.x; sw.cw0[1] = v0.y; sw.cw1[0] = v1.x; sw.cw1[1] = v1.y;
+    sw.cw0[2] = sw.cw1[2] = 0;
+  } else {
+    sw.cw0[0] = p0[0]; sw.cw0[1] = p0[1]; sw.cw0[2] = p0[2];
+    sw.cw1[0] = p1[0]; sw.cw1[1] = p1[1]; sw.cw1[2] = p1[2];
+  }
+  const uint16_t d0 = sarea[ti0 * 128 + ri0 * 2 + hh], d1 = sarea[ti1 * 128 + ri1 * 2 + hh];
+  if constexpr (FMT == 2) {
+    sw.t0 = q2_table(d0);
+    sw.t1 = q2_table(d1);
+  } else {
+    sw.f0 = f16_to_f32(d0);
+    sw.f1 = f16_to_f32(d1);
+  }
+}
+
+// The B operands (both streams) of step s of the stage.
+template <int FMT>
+STRATA_DEVICE void decode_step(const StageWeights<FMT>& sw, int s, half8_t (&b)[2], const Q2Sel& k) {
+  if constexpr (FMT == 2) {
+    b[0] = q2_decode(sw.cw0[0], sw.cw0[1], s, sw.t0, k);
+    b[1] = q2_decode(sw.cw1[0], sw.cw1[1], s, sw.t1, k);
+  } else {
+    b[0] = q3_decode(sw.cw0[0], sw.cw0[1], sw.cw0[2], s, sw.f0);
+    b[1] = q3_decode(sw.cw1[0], sw.cw1[1], sw.cw1[2], s, sw.f1);
+  }
+}
+
+// The A fragments of step s: row f*32 + m, 8 fp16 at piece (hh*4 + s) of the row.
+template <int NF>
+STRATA_DEVICE void read_frags(const uint8_t* xt, int m, int hh, int s, half8_t (&a)[NF]) {
+  const int slot = ((hh << 2) + s) ^ ((m >> 1) & 7);
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    a[f] = *reinterpret_cast<const half8_t*>(xt + (f * 32 + m) * 128 + slot * 16);
+}
+
+template <int NF>
+STRATA_DEVICE void mfma_step(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const half8_t (&a)[NF],
+                             const half8_t (&b)[2], int f0, int f1) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f < f0 || f >= f1) continue;
+    acc0[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[f], b[0], acc0[f], 0, 0, 0);
+    acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[f], b[1], acc1[f], 0, 0, 0);
+  }
+}
+
+// Software pipeline over the 4 steps of a stage: scheduling region s holds the matrix ops of step
+// s together with the fragment reads and the weight decode of step s+1, so the decode's VALU work
+// issues between the matrix ops.  The next stage's set-up (its barrier, weight words, decode
+// tables, step-0 fragments and weights) runs inside step 3, behind the last matrix ops of this
+// stage, so the matrix core does not wait for it at the stage boundary.
+template <int FMT, int NF>
+STRATA_DEVICE void gemm_core(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const uint16_t* __restrict__ src,
+                             int ld, int K, const int* rows_lds, const WeightTile& wt,
+                             int ti0, int ti1, int ri0, int ri1, uint8_t* lds) {
+  using P = Pipe<FMT, NF>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, hh = lane >> 5;
 #pragma unroll
@@ -222,85 +322,66 @@ STRATA_DEVICE void gemm_core(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const u
 #pragma unroll
   for (int g = 0; g < NF; ++g) {
     const int r = 8 * (wave + 4 * g) + (lane >> 3);
-    xoff[g] = rows_lds[r] * ld + (((lane & 7) ^ (lane >> 3)) << 3);
+    xoff[g] = rows_lds[r] * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 3);
   }
   const int NK = K / kKS;
 #pragma unroll
   for (int j = 0; j < P::kPD; ++j)
-    if (j < NK) issue_stage<FMT, NF>(lds + j * P::kStage, src, xoff, wr, j);
+    if (j < NK) issue_stage<FMT, NF>(lds + j * P::kStage, src, xoff, wt, j);
+  // stage 0 landed for this wave (later stages may be outstanding), then for every wave.  Bare
+  // s_barriers: __syncthreads() would also drain the copies in flight for the later stages.
+  {
+    const int later = NK - 1;
+    wait_pending<P::kPer, P::kPD - 1>(later < P::kPD - 1 ? later : P::kPD - 1);
+  }
+  __builtin_amdgcn_s_barrier();
+  const Q2Sel ksel = q2_sel();
+  StageWeights<FMT> sw;
+  half8_t a[2][NF];
+  half8_t b[2][2];
+  load_stage_weights<FMT, NF>(sw, lds, ti0, ti1, ri0, ri1, hh);
+  read_frags<NF>(lds, m, hh, 0, a[0]);
+  decode_step<FMT>(sw, 0, b[0], ksel);
   for (int j = 0; j < NK; ++j) {
-    // this wave's copies of stage j have landed (at most the later stages are outstanding) ...
-    {
-      const int later = NK - 1 - j;
-      wait_pending<P::kPer, P::kPD - 1>(later < P::kPD - 1 ? later : P::kPD - 1);
-    }
-    // ... and so have every other wave's.  A bare s_barrier: __syncthreads() would also drain the
-    // copies still in flight for the later stages.
-    __builtin_amdgcn_s_barrier();
-    if (j + P::kPD < NK) issue_stage<FMT, NF>(lds + ((j + P::kPD) % P::kNBuf) * P::kStage, src, xoff, wr, j + P::kPD);
-    const uint8_t* stage = lds + (j % P::kNBuf) * P::kStage;
-    const uint8_t* carea = stage + P::kXBytes + wave * 64 * 2 * CB;
-    const uint16_t* sarea = reinterpret_cast<const uint16_t*>(stage + P::kXBytes + P::kWCodeBytes + wave * 256);
-    // this lane's block (hh) of its row in each stream
-    uint32_t cw0[3], cw1[3];
-    if constexpr (FMT == 2) {
-      const uint2 v0 = *reinterpret_cast<const uint2*>(carea + m * 16 + hh * 8);
-      const uint2 v1 = *reinterpret_cast<const uint2*>(carea + (32 + m) * 16 + hh * 8);
-      cw0[0] = v0.x; cw0[1] = v0.y; cw1[0] = v1.x; cw1[1] = v1.y;
-      cw0[2] = cw1[2] = 0;
-    } else {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(carea) + hh * 3 * 64;
-      cw0[0] = p[m]; cw0[1] = p[64 + m]; cw0[2] = p[128 + m];
-      cw1[0] = p[32 + m]; cw1[1] = p[96 + m]; cw1[2] = p[160 + m];
-    }
-    const uint16_t d0 = sarea[m * 2 + hh], d1 = sarea[(32 + m) * 2 + hh];
-    Q2Tab t0, t1;
-    float f0 = 0.0f, f1 = 0.0f;
-    if constexpr (FMT == 2) {
-      t0 = q2_table(d0);
-      t1 = q2_table(d1);
-    } else {
-      f0 = f16_to_f32(d0);
-      f1 = f16_to_f32(d1);
-    }
-    const uint8_t* xt = stage;
-    // Software pipeline over the 4 steps of the stage: scheduling region s holds the matrix ops
-    // of step s together with the fragment reads and the weight decode of step s+1, so the
-    // decode's VALU work issues between the matrix ops and the reads have a full step to land.
-    half8_t a[2][NF];
-    half8_t b[2][2];
+    // stage j + kPD goes into the buffer of stage j - 1, which every wave finished reading before
+    // the barrier that opened stage j.  Its copies are spread over steps 0-2, between the matrix
+    // ops: a wave waits at a copy while the address unit still serves earlier ones, and the matrix
+    // core keeps running meanwhile.  (All are issued before the wait in step 3, which counts them.)
+    // Past the last stage the copies repeat stage NK - 1 into that free buffer, so that they stay
+    // unconditional (no branch splits the step); the waits do not count them, which only makes
+    // them stricter.
+    const int jc = j + P::kPD < NK ? j + P::kPD : NK - 1;
+    uint8_t* dst = lds + ((j + P::kPD) % P::kNBuf) * P::kStage;
+    const uint8_t* xt = lds + (j % P::kNBuf) * P::kStage;
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      a[0][f] = *reinterpret_cast<const half8_t*>(xt + (f * 32 + m) * 128 + ((hh << 2) ^ (m & 7)) * 16);
-    if constexpr (FMT == 2) {
-      b[0][0] = q2_decode(cw0[0], cw0[1], 0, t0);
-      b[0][1] = q2_decode(cw1[0], cw1[1], 0, t1);
-    } else {
-      b[0][0] = q3_decode(cw0[0], cw0[1], cw0[2], 0, f0);
-      b[0][1] = q3_decode(cw1[0], cw1[1], cw1[2], 0, f1);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 3; ++s) {
       __builtin_amdgcn_sched_barrier(0);
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s < 3) {
-        const int slot = ((hh << 2) + s + 1) ^ (m & 7);
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          a[nxt][f] = *reinterpret_cast<const half8_t*>(xt + (f * 32 + m) * 128 + slot * 16);
-        if constexpr (FMT == 2) {
-          b[nxt][0] = q2_decode(cw0[0], cw0[1], s + 1, t0);
-          b[nxt][1] = q2_decode(cw1[0], cw1[1], s + 1, t1);
-        } else {
-          b[nxt][0] = q3_decode(cw0[0], cw0[1], cw0[2], s + 1, f0);
-          b[nxt][1] = q3_decode(cw1[0], cw1[1], cw1[2], s + 1, f1);
-        }
+      issue_copies<FMT, NF>(dst, src, xoff, wt, jc, s * P::kPer / 3, (s + 1) * P::kPer / 3);
+      read_frags<NF>(xt, m, hh, s + 1, a[(s + 1) & 1]);
+      decode_step<FMT>(sw, s + 1, b[(s + 1) & 1], ksel);
+      mfma_step<NF>(acc0, acc1, a[s & 1], b[s & 1], 0, NF);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (on the last stage the set-up below reads a stale buffer; its results are not used.  It is
+    // not skipped so that the step-3 matrix ops stay in one block with it.)
+    {
+      // the first matrix ops of step 3 keep the matrix core busy through the barrier
+      constexpr int kPre = (NF + 1) / 2;
+      mfma_step<NF>(acc0, acc1, a[1], b[1], 0, kPre);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int later = NK - 2 - j;  // stages issued after stage j + 1
+        wait_pending<P::kPer, P::kPD - 1>(later < 0 ? 0 : later < P::kPD - 1 ? later : P::kPD - 1);
       }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        acc0[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][f], b[cur][0], acc0[f], 0, 0, 0);
-        acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur][f], b[cur][1], acc1[f], 0, 0, 0);
-      }
+      // this wave's reads of stage j are complete before any wave may overwrite its buffer
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt / expcnt unconstrained
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* nt = lds + ((j + 1) % P::kNBuf) * P::kStage;
+      load_stage_weights<FMT, NF>(sw, nt, ti0, ti1, ri0, ri1, hh);
+      read_frags<NF>(nt, m, hh, 0, a[0]);
+      decode_step<FMT>(sw, 0, b[0], ksel);
+      mfma_step<NF>(acc0, acc1, a[1], b[1], kPre, NF);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -322,11 +403,13 @@ constexpr int kUpOutRow = 128 + 8;   // halfs per LDS row of the staged output t
 constexpr int kDownOutRow = 256;     // 224 rows x 256 halfs fit in the stage ring
 
 template <int FMT, int NF>
-STRATA_DEVICE void up_unit(const UnitInfo& u, const uint16_t* __restrict__ x16, const WeightRows& wr,
+STRATA_DEVICE void up_unit(const UnitInfo& u, const uint16_t* __restrict__ x16, const WeightTile& wt,
                            int H, int I, uint16_t* __restrict__ a16, uint8_t* lds_bytes,
                            const int* rows_lds) {
   f32x16_t accg[NF], accu[NF];
-  gemm_core<FMT, NF>(accg, accu, x16, H, H, rows_lds, wr, lds_bytes);
+  // LDS weight tiles 0, 1 = gate rows 0-63, 64-127 of the slice; 2, 3 = the same up rows
+  const int w = threadIdx.x >> 6, ri = (w & 1) * 32 + (threadIdx.x & 31);
+  gemm_core<FMT, NF>(accg, accu, x16, H, H, rows_lds, wt, w >> 1, 2 + (w >> 1), ri, ri, lds_bytes);
   uint16_t* lds = reinterpret_cast<uint16_t*>(lds_bytes);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 31, hh = lane >> 5;
@@ -362,23 +445,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
   int* rows_lds = reinterpret_cast<int*>(smem + kLdsBudget);
   UnitInfo u;
   if (!pick_unit(chunks, n_chunks, I / 128, u)) return;
-  constexpr int CB = FMT == 2 ? 8 : 12;
   const int wave = threadIdx.x >> 6;
-  const int nbh = H / 32;
-  const size_t row0 = (size_t)u.expert * I + u.slice * 128 + wave * 32;
-  const WeightRows wr = weight_rows<FMT>(gate_codes + row0 * nbh * CB, up_codes + row0 * nbh * CB,
-                                         gate_scales + row0 * nbh, up_scales + row0 * nbh, nbh);
+  // wave w copies gate (w < 2) or up rows 128 slice + 64 (w & 1) .. + 63 of the expert
+  const size_t row0 = (size_t)u.expert * I + 128 * u.slice + 64 * (wave & 1);
+  const WeightTile wt = weight_tile<FMT>(wave < 2 ? gate_codes : up_codes,
+                                         wave < 2 ? gate_scales : up_scales, row0, H / 64);
   for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads)
     rows_lds[r] = sorted_slot[u.row_start + (r < u.nrows ? r : 0)] / k;
   __syncthreads();
   switch (u.nfrag) {
-    case 1: up_unit<FMT, 1>(u, x16, wr, H, I, a16, smem, rows_lds); break;
-    case 2: up_unit<FMT, 2>(u, x16, wr, H, I, a16, smem, rows_lds); break;
-    case 3: up_unit<FMT, 3>(u, x16, wr, H, I, a16, smem, rows_lds); break;
-    case 4: up_unit<FMT, 4>(u, x16, wr, H, I, a16, smem, rows_lds); break;
-    case 5: up_unit<FMT, 5>(u, x16, wr, H, I, a16, smem, rows_lds); break;
-    case 6: up_unit<FMT, 6>(u, x16, wr, H, I, a16, smem, rows_lds); break;
-    default: up_unit<FMT, 7>(u, x16, wr, H, I, a16, smem, rows_lds); break;
+    case 1: up_unit<FMT, 1>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+    case 2: up_unit<FMT, 2>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+    case 3: up_unit<FMT, 3>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+    case 4: up_unit<FMT, 4>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+    case 5: up_unit<FMT, 5>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+    case 6: up_unit<FMT, 6>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+    default: up_unit<FMT, 7>(u, x16, wt, H, I, a16, smem, rows_lds); break;
   }
 }
 
@@ -388,11 +470,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
 
 template <int FMT, int NF>
 STRATA_DEVICE void down_unit(const UnitInfo& u, const uint16_t* __restrict__ a16,
-                             const int* __restrict__ sorted_slot, const WeightRows& wr, int H,
+                             const int* __restrict__ sorted_slot, const WeightTile& wt, int H,
                              int I, uint16_t* __restrict__ expert_out, uint8_t* lds_bytes,
                              const int* rows_lds) {
   f32x16_t acc0[NF], acc1[NF];
-  gemm_core<FMT, NF>(acc0, acc1, a16, I, I, rows_lds, wr, lds_bytes);
+  // LDS weight tile w = rows 64 w .. 64 w + 63 of the slice
+  const int w = threadIdx.x >> 6, ri = threadIdx.x & 31;
+  gemm_core<FMT, NF>(acc0, acc1, a16, I, I, rows_lds, wt, w, w, ri, 32 + ri, lds_bytes);
   uint16_t* lds = reinterpret_cast<uint16_t*>(lds_bytes);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 31, hh = lane >> 5;
@@ -427,23 +511,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
   int* rows_lds = reinterpret_cast<int*>(smem + kLdsBudget);
   UnitInfo u;
   if (!pick_unit(chunks, n_chunks, H / 256, u)) return;
-  constexpr int CB = FMT == 2 ? 8 : 12;
   const int wave = threadIdx.x >> 6;
-  const int nbi = I / 32;
-  const size_t row0 = (size_t)u.expert * H + u.slice * 256 + wave * 64;
-  const WeightRows wr = weight_rows<FMT>(down_codes + row0 * nbi * CB, down_codes + (row0 + 32) * nbi * CB,
-                                         down_scales + row0 * nbi, down_scales + (row0 + 32) * nbi, nbi);
+  // wave w copies rows 256 slice + 64 w .. + 63 of the expert
+  const size_t row0 = (size_t)u.expert * H + 256 * u.slice + 64 * wave;
+  const WeightTile wt = weight_tile<FMT>(down_codes, down_scales, row0, I / 64);
   for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads)
     rows_lds[r] = u.row_start + (r < u.nrows ? r : 0);
   __syncthreads();
   switch (u.nfrag) {
-    case 1: down_unit<FMT, 1>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
-    case 2: down_unit<FMT, 2>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
-    case 3: down_unit<FMT, 3>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
-    case 4: down_unit<FMT, 4>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
-    case 5: down_unit<FMT, 5>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
-    case 6: down_unit<FMT, 6>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
-    default: down_unit<FMT, 7>(u, a16, sorted_slot, wr, H, I, expert_out, smem, rows_lds); break;
+    case 1: down_unit<FMT, 1>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+    case 2: down_unit<FMT, 2>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+    case 3: down_unit<FMT, 3>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+    case 4: down_unit<FMT, 4>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+    case 5: down_unit<FMT, 5>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+    case 6: down_unit<FMT, 6>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+    default: down_unit<FMT, 7>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
   }
 }
 

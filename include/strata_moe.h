@@ -62,11 +62,21 @@ typedef enum {
  *   read as one 96-bit little-endian integer; weight i sits in bits [3*i, 3*i+2] (codes may
  *   straddle byte and word edges).
  *
- * A matrix with R rows and reduction length K (K a multiple of 32) is stored as two arrays
- * (structure of arrays, row-major):
- *   codes  [R][K/32][8 or 12 bytes]
+ * Row-major layout.  A matrix with R rows and reduction length K (K a multiple of 32) is two
+ * arrays (structure of arrays):
+ *   codes  [R][K/32][cb bytes]      (cb = 8 for Q2, 12 for Q3)
  *   scales [R][K/32] fp16
  * so w[r][c] = scale[r][c/32] * (code of weight c%32 in block [r][c/32] - offset).
+ *
+ * Tiled layout (what the compute entry points read).  R a multiple of 4 and K of 64; the matrix
+ * is cut into tiles of 4 rows x 64 reduction indices (two blocks per row), ordered row-group
+ * major:
+ *   codes  [R/4][K/64][4][2][cb bytes]
+ *   scales [R/4][K/64][4][2] fp16
+ * i.e. block b of row r sits at tile (r/4, b/2), tile row r%4, slot b%2.  The same bytes as the
+ * row-major arrays, reordered so that a 4-row group's consecutive 64-index stages are contiguous
+ * and one stage of 64 rows is 16 contiguous pieces.
+ * strata_moe_pack_matrix converts row-major -> tiled on the device.
  */
 typedef enum {
   STRATA_Q2_B32 = 2,
@@ -74,12 +84,13 @@ typedef enum {
 } strata_qformat;
 
 /*
- * One layer's expert weights, all device pointers, expert-major:
+ * One layer's expert weights, all device pointers, expert-major, each matrix in the tiled layout:
  *   gate W_g and up W_u: per expert an [I][H] matrix (rows = intermediate features, reduction
- *     along H): codes [E][I][H/32][cb], scales [E][I][H/32];
+ *     along H): codes [E][I/4][H/64][4][2][cb], scales [E][I/4][H/64][4][2];
  *   down W_d: per expert an [H][I] matrix (rows = hidden features, reduction along I):
- *     codes [E][H][I/32][cb], scales [E][H][I/32];
- * with cb = 8 (Q2) or 12 (Q3).  Expert e's arrays start at e times the per-expert size.
+ *     codes [E][H/4][I/64][4][2][cb], scales [E][H/4][I/64][4][2];
+ * with cb = 8 (Q2) or 12 (Q3).  Expert e's arrays start at e times the per-expert size (the E
+ * matrices of one kind are also one tiled matrix of E*R rows).
  */
 typedef struct strata_moe_weights {
   int32_t fmt;          /* strata_qformat */
@@ -195,6 +206,18 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
                                int32_t* opt_topk_ids, float* opt_topk_w, int32_t* opt_counts,
                                int32_t* opt_offsets, int32_t* opt_sorted_slot, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Weight repack, row-major -> tiled (see the layouts above), for n_mat matrices of rows x K
+ * stored back to back (e.g. all E gate matrices: n_mat = E, rows = I, K = H).  A one-time
+ * load step; the compute entry points read only the tiled layout.
+ *   codes, scales              row-major arrays (read)
+ *   tiled_codes, tiled_scales  same sizes, tiled (written); must not overlap the inputs
+ * Limits: rows a multiple of 4 and K a multiple of 64 (STRATA_ERR_UNSUPPORTED otherwise).
+ */
+strata_status strata_moe_pack_matrix(int32_t fmt, int32_t n_mat, int32_t rows, int32_t K,
+                                    const void* codes, const uint16_t* scales, void* tiled_codes,
+                                    uint16_t* tiled_scales, hipStream_t stream);
 
 /*
  * RMSNorm for a layer stack: x[t] = bf16_RNE(h[t] / sqrt(mean_i h[t][i]^2 + eps)), unit gain.

@@ -99,6 +99,20 @@ def test_combine_and_rmsnorm_validation(L):
     assert L.strata_moe_rmsnorm(MIS, 4, 3072, ctypes.c_float(1e-6), A, None) == INVAL
 
 
+def test_pack_matrix_validation(L):
+    B = A + (1 << 30)  # a second fake buffer, far from A
+    assert L.strata_moe_pack_matrix(4, 1, 64, 64, A, A + 4096, B, B + 4096, None) == INVAL
+    assert L.strata_moe_pack_matrix(2, 1, 66, 64, A, A + 4096, B, B + 4096, None) == UNSUP
+    assert L.strata_moe_pack_matrix(2, 1, 64, 96, A, A + 4096, B, B + 4096, None) == UNSUP
+    assert L.strata_moe_pack_matrix(2, 0, 64, 64, A, A + 4096, B, B + 4096, None) == INVAL
+    assert L.strata_moe_pack_matrix(2, 1, 64, 64, MIS, A + 4096, B, B + 4096, None) == INVAL
+    assert L.strata_moe_pack_matrix(2, 1, 64, 64, A, A + 4096, None, B + 4096, None) == INVAL
+    # 64 x 64 Q2 is 1 KB of codes and 256 B of scales: overlapping source and destination
+    assert L.strata_moe_pack_matrix(2, 1, 64, 64, A, A + 4096, A + 512, B + 4096, None) == INVAL
+    assert L.strata_moe_pack_matrix(2, 1, 64, 64, A, A + 4096, B, A + 4096 + 128, None) == INVAL
+    assert L.strata_moe_pack_matrix(3, 1, 64, 64, A, A + 4096, A + 1024, B + 4096, None) == INVAL
+
+
 def test_workspace_sizes(L):
     assert L.strata_moe_workspace_bytes(-1, 512, 10, 3072, 768) == 0
     small = L.strata_moe_workspace_bytes(16, 64, 4, 256, 128)

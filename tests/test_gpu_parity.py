@@ -251,3 +251,28 @@ def test_rmsnorm_against_oracle():
     diff = np.abs(got - ref)
     assert diff.max() <= 1              # at most one bf16 ulp (rounding of a near-tie)
     assert np.mean(diff == 0) > 0.999
+
+
+# ---------------------------------------------------------------------------------------------
+# Weight repack (row-major -> tiled): a pure byte permutation, so bit-exact against the index
+# arithmetic written out with numpy.
+
+
+@pytest.mark.parametrize("fmt,n_mat,rows,K", [(2, 3, 128, 256), (3, 2, 196, 128), (2, 1, 4, 64)])
+def test_pack_matrix_bit_exact(fmt, n_mat, rows, K):
+    cb = sm.CODE_BYTES[fmt]
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(n_mat, rows, K // 32, cb), dtype=np.uint8)
+    scales = rng.integers(0, 1 << 16, size=(n_mat, rows, K // 32), dtype=np.uint16)
+    c = torch.from_numpy(codes).to(dev())
+    s = torch.from_numpy(scales.view(np.int16)).to(dev())
+    tc, ts = torch.empty_like(c), torch.empty_like(s)
+    sm.strata_moe_pack_matrix(fmt, n_mat, rows, K, c, s, tc, ts)
+    torch.cuda.synchronize()
+    # block b of row r -> tile (r // 4, b // 2), tile row r % 4, slot b % 2
+    want_c = codes.reshape(n_mat, rows // 4, 4, K // 64, 2, cb).transpose(0, 1, 3, 2, 4, 5)
+    want_s = scales.reshape(n_mat, rows // 4, 4, K // 64, 2).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(tc.cpu().numpy().reshape(-1), np.ascontiguousarray(want_c).reshape(-1))
+    assert np.array_equal(ts.cpu().numpy().view(np.uint16).reshape(-1),
+                          np.ascontiguousarray(want_s).reshape(-1))
+
