@@ -34,25 +34,36 @@ constexpr int kGemmThreads = 256;                 // 4 waves, one per SIMD
 constexpr int kKS = 64;                           // reduction indices per pipeline stage (2 blocks)
 constexpr int kFrags = kChunkRows / 32;           // 32-row fragments per chunk
 constexpr int kWScaleBytes = 256 * 2 * 2;         // 256 weight rows x 2 fp16 scales per stage
-constexpr int kLdsBudget = 150 * 1024;            // ring of stage buffers
-constexpr size_t kGemmLds = kLdsBudget + kChunkRows * sizeof(int);
+constexpr int kGemmLds = 160 * 1024;              // the whole LDS of a CU
+constexpr int kRowsBytes = 2 * kChunkRows * 4;    // a unit's source and destination rows
+// Output staging: two 32-row buffers (one fragment each) with padded rows.
+constexpr int kUpOutRow = 128 + 8;                // halfs per row: 128 outputs
+constexpr int kDownOutRow = 256 + 8;              // halfs per row: 256 outputs
+constexpr int kUpEpiBytes = 2 * 32 * kUpOutRow * 2;
+constexpr int kDownEpiBytes = 2 * 32 * kDownOutRow * 2;
 
-// Stage geometry of a unit with NF fragments: as many stage buffers as fit in the ring (the
-// copies of all but the computed stage are in flight, hiding the ~2-3 us copy latency), capped
-// so that the vector-memory counter can express the waits (at most 63 outstanding operations).
+// Byte layout of one stage buffer of a unit with NF fragments.
 template <int FMT, int NF>
-struct Pipe {
+struct Geom {
   static constexpr int kCB = FMT == 2 ? 8 : 12;
   static constexpr int kXBytes = NF * 32 * kKS * 2;         // activation tile
   static constexpr int kWCodeBytes = 4 * 128 * kCB;          // 4 weight tiles x 64 rows x 2 blocks
   static constexpr int kStage = kXBytes + kWCodeBytes + kWScaleBytes;
   static constexpr int kPer = NF + (FMT == 2 ? 1 : 2) + 1;   // copy instructions per wave per stage
-  static constexpr int kByLds = kLdsBudget / kStage;
-  static constexpr int kByCnt = 63 / kPer + 1;               // (buffers - 2) * kPer <= 63, with margin
+};
+
+// The stage ring in RING bytes: as many buffers as fit (the copies of all but the computed stage
+// are in flight, hiding the ~2-3 us copy latency), capped so that the vector-memory counter can
+// express the waits (at most 63 outstanding).
+template <int FMT, int NF, int RING>
+struct Pipe : Geom<FMT, NF> {
+  using G = Geom<FMT, NF>;
+  static constexpr int kByLds = RING / G::kStage;
+  static constexpr int kByCnt = 63 / G::kPer + 1;            // (buffers - 2) * kPer <= 63, with margin
   static constexpr int kNBuf = kByLds < kByCnt ? (kByLds < 8 ? kByLds : 8) : (kByCnt < 8 ? kByCnt : 8);
   static constexpr int kPD = kNBuf - 1;
   static_assert(kNBuf >= 2, "ring too small");
-  static_assert((kPD - 1) * kPer <= 63, "vmcnt range");
+  static_assert((kPD - 1) * G::kPer <= 63, "vmcnt range");
 };
 
 STRATA_DEVICE int p8inv(int m) { return ((m & 3) << 1) | (m >> 2); }  // position of index m
@@ -63,6 +74,21 @@ STRATA_DEVICE void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
+
+// s_waitcnt vmcnt(n) for a runtime n in [LO, HI] (a binary tree of uniform branches).
+template <int LO, int HI>
+STRATA_DEVICE void wait_vmcnt_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vmcnt_range<MID, HI>(n);
+    else wait_vmcnt_range<LO, MID - 1>(n);
+  }
+}
+
+// Waits until at most n vector-memory operations are outstanding (n clamped to [0, 63]).
+STRATA_DEVICE void wait_vmcnt_dyn(int n) { wait_vmcnt_range<0, 63>(n < 0 ? 0 : n > 63 ? 63 : n); }
 
 // Waits until at most P later stages' copies are outstanding, for a runtime P in [0, PMAX].
 template <int PER, int PMAX>
@@ -140,23 +166,27 @@ STRATA_DEVICE half8_t q3_decode(uint32_t w0, uint32_t w1, uint32_t w2, int s, fl
 // Work units.
 
 struct UnitInfo {
-  int expert, row_start, nrows, nfrag, slice;
+  int expert, row_start, nrows, nfrag, slice0, nsl;
 };
 
-// Maps blockIdx to a unit; false if this workgroup has no unit.
-STRATA_DEVICE bool pick_unit(const Chunk* chunks, const int* n_chunks, int n_slices, UnitInfo& u) {
-  const int U = *n_chunks * n_slices;
+// Maps blockIdx to a unit (a chunk and G consecutive column slices of it); false if this
+// workgroup has none.  The units of XCD x (blockIdx % 8, with the usual round-robin dispatch) are
+// a contiguous range, so the slice groups of one chunk run side by side on one L2.
+STRATA_DEVICE bool pick_unit(const Chunk* chunks, const int* n_chunks, int n_groups, int G,
+                             UnitInfo& u) {
+  const int U = *n_chunks * n_groups;
   const int per = (U + 7) >> 3;
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
   if (i >= per) return false;
   const int unit = xcd * per + i;
   if (unit >= U) return false;
-  const Chunk ch = chunks[unit / n_slices];
+  const Chunk ch = chunks[unit / n_groups];
   u.expert = ch.expert;
   u.row_start = ch.row_start;
   u.nrows = ch.nrows;
   u.nfrag = (ch.nrows + 31) >> 5;
-  u.slice = unit % n_slices;
+  u.slice0 = (unit % n_groups) * G;
+  u.nsl = G;
   return true;
 }
 
@@ -200,37 +230,31 @@ STRATA_DEVICE WeightTile weight_tile(const uint8_t* codes, const uint16_t* scale
   return wt;
 }
 
-// Copies c0 .. c1 - 1 of this wave's kPer copies of stage j: the NF activation groups, then the
-// weight tile's codes (one or two), then its scales.
+// Copies c0 .. c1 - 1 of this wave's kPer copies of one stage: the NF activation groups (columns
+// 64 ks .. 64 ks + 63 of the rows xoff), then the weight tile's codes (one or two), then its
+// scales; woff / soff: byte / fp16 offsets of the stage's weight pieces from stage 0 of slice 0.
 template <int FMT, int NF>
-STRATA_DEVICE void issue_copies(uint8_t* stage, const uint16_t* __restrict__ src, const int (&xoff)[NF],
-                                const WeightTile& wt, int j, int c0, int c1) {
-  constexpr int TB = 128 * (FMT == 2 ? 8 : 12);  // code bytes of one 64-row tile-stage
-  constexpr int GB = TB / 16;                     // code bytes of one 4-row group stage
+STRATA_DEVICE void issue_copies(uint8_t* stage, const uint16_t* __restrict__ src, const int* xoff,
+                                const WeightTile& wt, int ks, size_t woff, size_t soff, int c0, int c1) {
+  using GM = Geom<FMT, NF>;
+  constexpr int TB = 128 * GM::kCB;  // code bytes of one 64-row tile-stage
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int k0 = j * kKS;
+  const int k0 = ks * kKS;
 #pragma unroll
   for (int g = 0; g < NF; ++g) {
     if (g < c0 || g >= c1) continue;
     const int q = wave + 4 * g;
     __builtin_amdgcn_global_load_lds(src + xoff[g] + k0, stage + q * 1024, 16, 0, 0);
   }
-  uint8_t* carea = stage + Pipe<FMT, NF>::kXBytes + wave * TB;
-  if (NF >= c0 && NF < c1) __builtin_amdgcn_global_load_lds(wt.codes0 + (size_t)j * GB, carea, 16, 0, 0);
+  uint8_t* carea = stage + GM::kXBytes + wave * TB;
+  if (NF >= c0 && NF < c1) __builtin_amdgcn_global_load_lds(wt.codes0 + woff, carea, 16, 0, 0);
   constexpr int kS = NF + (FMT == 2 ? 1 : 2);  // index of the scale copy
   if constexpr (FMT == 3) {
     if (NF + 1 >= c0 && NF + 1 < c1 && lane < 32)
-      __builtin_amdgcn_global_load_lds(wt.codes1 + (size_t)j * GB, carea + 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(wt.codes1 + woff, carea + 1024, 16, 0, 0);
   }
   if (kS >= c0 && kS < c1)
-    __builtin_amdgcn_global_load_lds(wt.scales + (size_t)j * 8,
-                                     stage + Pipe<FMT, NF>::kXBytes + Pipe<FMT, NF>::kWCodeBytes + wave * 256, 4, 0, 0);
-}
-
-template <int FMT, int NF>
-STRATA_DEVICE void issue_stage(uint8_t* stage, const uint16_t* __restrict__ src, const int (&xoff)[NF],
-                               const WeightTile& wt, int j) {
-  issue_copies<FMT, NF>(stage, src, xoff, wt, j, 0, Pipe<FMT, NF>::kPer);
+    __builtin_amdgcn_global_load_lds(wt.scales + soff, stage + GM::kXBytes + GM::kWCodeBytes + wave * 256, 4, 0, 0);
 }
 
 // Per-lane weight state of one stage: the lane's block (hh) of its row in each stream (row ri of
@@ -245,10 +269,10 @@ struct StageWeights {
 template <int FMT, int NF>
 STRATA_DEVICE void load_stage_weights(StageWeights<FMT>& sw, const uint8_t* stage, int ti0, int ti1,
                                       int ri0, int ri1, int hh) {
-  using P = Pipe<FMT, NF>;
-  constexpr int CB = P::kCB;
-  const uint8_t* carea = stage + P::kXBytes;
-  const uint16_t* sarea = reinterpret_cast<const uint16_t*>(stage + P::kXBytes + P::kWCodeBytes);
+  using GM = Geom<FMT, NF>;
+  constexpr int CB = GM::kCB;
+  const uint8_t* carea = stage + GM::kXBytes;
+  const uint16_t* sarea = reinterpret_cast<const uint16_t*>(stage + GM::kXBytes + GM::kWCodeBytes);
   const uint32_t* p0 = reinterpret_cast<const uint32_t*>(carea + ti0 * 128 * CB + ri0 * 2 * CB + hh * CB);
   const uint32_t* p1 = reinterpret_cast<const uint32_t*>(carea + ti1 * 128 * CB + ri1 * 2 * CB + hh * CB);
   if constexpr (FMT == 2) {
@@ -301,93 +325,6 @@ STRATA_DEVICE void mfma_step(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const h
   }
 }
 
-// Software pipeline over the 4 steps of a stage: scheduling region s holds the matrix ops of step
-// s together with the fragment reads and the weight decode of step s+1, so the decode's VALU work
-// issues between the matrix ops.  The next stage's set-up (its barrier, weight words, decode
-// tables, step-0 fragments and weights) runs inside step 3, behind the last matrix ops of this
-// stage, so the matrix core does not wait for it at the stage boundary.
-template <int FMT, int NF>
-STRATA_DEVICE void gemm_core(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const uint16_t* __restrict__ src,
-                             int ld, int K, const int* rows_lds, const WeightTile& wt,
-                             int ti0, int ti1, int ri0, int ri1, uint8_t* lds) {
-  using P = Pipe<FMT, NF>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    acc0[f] = f32x16_t{};
-    acc1[f] = f32x16_t{};
-  }
-  int xoff[NF];
-#pragma unroll
-  for (int g = 0; g < NF; ++g) {
-    const int r = 8 * (wave + 4 * g) + (lane >> 3);
-    xoff[g] = rows_lds[r] * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 3);
-  }
-  const int NK = K / kKS;
-#pragma unroll
-  for (int j = 0; j < P::kPD; ++j)
-    if (j < NK) issue_stage<FMT, NF>(lds + j * P::kStage, src, xoff, wt, j);
-  // stage 0 landed for this wave (later stages may be outstanding), then for every wave.  Bare
-  // s_barriers: __syncthreads() would also drain the copies in flight for the later stages.
-  {
-    const int later = NK - 1;
-    wait_pending<P::kPer, P::kPD - 1>(later < P::kPD - 1 ? later : P::kPD - 1);
-  }
-  __builtin_amdgcn_s_barrier();
-  const Q2Sel ksel = q2_sel();
-  StageWeights<FMT> sw;
-  half8_t a[2][NF];
-  half8_t b[2][2];
-  load_stage_weights<FMT, NF>(sw, lds, ti0, ti1, ri0, ri1, hh);
-  read_frags<NF>(lds, m, hh, 0, a[0]);
-  decode_step<FMT>(sw, 0, b[0], ksel);
-  for (int j = 0; j < NK; ++j) {
-    // stage j + kPD goes into the buffer of stage j - 1, which every wave finished reading before
-    // the barrier that opened stage j.  Its copies are spread over steps 0-2, between the matrix
-    // ops: a wave waits at a copy while the address unit still serves earlier ones, and the matrix
-    // core keeps running meanwhile.  (All are issued before the wait in step 3, which counts them.)
-    // Past the last stage the copies repeat stage NK - 1 into that free buffer, so that they stay
-    // unconditional (no branch splits the step); the waits do not count them, which only makes
-    // them stricter.
-    const int jc = j + P::kPD < NK ? j + P::kPD : NK - 1;
-    uint8_t* dst = lds + ((j + P::kPD) % P::kNBuf) * P::kStage;
-    const uint8_t* xt = lds + (j % P::kNBuf) * P::kStage;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      issue_copies<FMT, NF>(dst, src, xoff, wt, jc, s * P::kPer / 3, (s + 1) * P::kPer / 3);
-      read_frags<NF>(xt, m, hh, s + 1, a[(s + 1) & 1]);
-      decode_step<FMT>(sw, s + 1, b[(s + 1) & 1], ksel);
-      mfma_step<NF>(acc0, acc1, a[s & 1], b[s & 1], 0, NF);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // (on the last stage the set-up below reads a stale buffer; its results are not used.  It is
-    // not skipped so that the step-3 matrix ops stay in one block with it.)
-    {
-      // the first matrix ops of step 3 keep the matrix core busy through the barrier
-      constexpr int kPre = (NF + 1) / 2;
-      mfma_step<NF>(acc0, acc1, a[1], b[1], 0, kPre);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const int later = NK - 2 - j;  // stages issued after stage j + 1
-        wait_pending<P::kPer, P::kPD - 1>(later < 0 ? 0 : later < P::kPD - 1 ? later : P::kPD - 1);
-      }
-      // this wave's reads of stage j are complete before any wave may overwrite its buffer
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt / expcnt unconstrained
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* nt = lds + ((j + 1) % P::kNBuf) * P::kStage;
-      load_stage_weights<FMT, NF>(sw, nt, ti0, ti1, ri0, ri1, hh);
-      read_frags<NF>(nt, m, hh, 0, a[0]);
-      decode_step<FMT>(sw, 0, b[0], ksel);
-      mfma_step<NF>(acc0, acc1, a[1], b[1], kPre, NF);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();  // every wave is done with the stage buffers before the epilogue reuses them
-}
-
 // Row of a 32x32 accumulator tile held in register r of this lane.
 STRATA_DEVICE int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
@@ -395,44 +332,240 @@ STRATA_DEVICE float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Writes one slice's outputs, fragment by fragment, through two LDS staging buffers, with 16-byte
+// stores.  Up: out = A (fp16, [rows][I], columns in P8 order within groups of 8), 128 outputs per
+// slice, lane c < 16 of a tile holding the gate and lane c + 16 the up value of output 16 w + c ...
+// (acc0 = gate, acc1 = up columns); down: out = expert outputs (bf16, [slots][H]), 256 per slice.
+// dst_lds[r]: the destination row of unit row r (rows past the chunk repeat row 0, whose values
+// they equal, so every lane stores).  Each wave issues kStores stores per fragment.
+template <int NF, bool UP>
+struct Epilogue {
+  static constexpr int kRow = UP ? kUpOutRow : kDownOutRow;        // halfs per staged row
+  static constexpr int kPieces = UP ? 16 : 32;                     // 16-byte pieces per row
+  static constexpr int kStores = 32 * kPieces / kGemmThreads;      // per thread per fragment
+  static constexpr int kBuf = 32 * kRow;                           // halfs per staging buffer
+};
+
+template <int NF, bool UP>
+STRATA_DEVICE void write_slice(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], uint16_t* epi,
+                               const int* dst_lds, uint16_t* __restrict__ out, int out_ld, int col0) {
+  using EP = Epilogue<NF, UP>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 31, hh = lane >> 5;
+  // this lane's first staged element (tile row 4 hh, its column); register r of a tile adds
+  // rows 8 (r >> 2) + (r & 3), a constant offset
+  const int lcol = UP ? wave * 32 + (nl & ~7) + p8inv(nl & 7) : wave * 64 + nl;
+  uint16_t* const e0 = epi + 4 * hh * EP::kRow + lcol;
+  // (opaque to the optimizer, so that the store addresses are not computed once for every slice
+  // and held in registers across the main loop)
+  asm volatile("" : "+s"(out_ld));
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    // One fragment at a time: the empty asm re-defines this fragment's sums in the accumulation
+    // registers here, so their copies into VGPRs cannot be hoisted above it (all fragments'
+    // copies at once would need 32 NF VGPRs).
+    asm volatile("" : "+a"(acc0[f]), "+a"(acc1[f]));
+    uint16_t* eb = e0 + (f & 1) * EP::kBuf;
+    if constexpr (UP) {
+      // acc0 columns: gate of outputs w*32 + n; acc1: up of the same outputs
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] =
+            __builtin_bit_cast(uint16_t, f32_to_f16_sat(silu_mul(acc0[f][r], acc1[f][r])));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] = f32_to_bf16(acc0[f][r]);
+        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow + 32] = f32_to_bf16(acc1[f][r]);
+      }
+    }
+    // the buffer is complete for every wave; (the other buffer's previous reads finished before
+    // each wave's own barrier here, so the next fragment may overwrite it)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    const uint16_t* rb = epi + (f & 1) * EP::kBuf;
+#pragma unroll
+    for (int i = 0; i < EP::kStores; ++i) {
+      const int p = threadIdx.x + i * kGemmThreads;
+      const int r = p / EP::kPieces, c = p % EP::kPieces;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rb + r * EP::kRow + c * 8);
+      *reinterpret_cast<u32x4_t*>(out + (size_t)dst_lds[f * 32 + r] * out_ld + col0 + c * 8) = v;
+    }
+  }
+}
+
+// Pipeline state carried from one stage to the next: the lane's weight words and decode tables of
+// the current stage, and the step-0 (even) / step-1.. operands.
+template <int FMT, int NF>
+struct StageState {
+  StageWeights<FMT> sw;
+  half8_t a[2][NF];
+  half8_t b[2][2];
+};
+
+// Stage set-up: weight words and tables, step-0 fragments and weights of the stage in buffer st.
+template <int FMT, int NF>
+STRATA_DEVICE void stage_setup(StageState<FMT, NF>& ss, const uint8_t* st, int ti0, int ti1, int ri0,
+                               int ri1, const Q2Sel& ksel) {
+  const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
+  load_stage_weights<FMT, NF>(ss.sw, st, ti0, ti1, ri0, ri1, hh);
+  read_frags<NF>(st, m, hh, 0, ss.a[0]);
+  decode_step<FMT>(ss.sw, 0, ss.b[0], ksel);
+}
+
+// Copy cursor of a unit: the next stage to copy as (reduction stage ks, weight offsets woff /
+// soff from slice 0 stage 0), moving through the unit's NT stages, NKs per slice, and staying on
+// the last one (whose copies then repeat).
+struct CopyCursor {
+  int j, ks, NT, NKs;
+  size_t woff, soff, wslice, sslice;
+};
+
+template <int FMT>
+STRATA_DEVICE void cursor_advance(CopyCursor& c) {
+  constexpr int GB = 8 * (FMT == 2 ? 8 : 12);  // code bytes of a 4-row group stage
+  if (c.j + 1 >= c.NT) return;
+  ++c.j;
+  if (++c.ks == c.NKs) {
+    c.ks = 0;
+    c.woff += c.wslice - (size_t)(c.NKs - 1) * GB;
+    c.soff += c.sslice - (size_t)(c.NKs - 1) * 8;
+  } else {
+    c.woff += GB;
+    c.soff += 8;
+  }
+}
+
+// Steps 0-2 of the stage in buffer xt (set up by stage_setup), with the copies of the cursor's
+// stage into dst spread between them, and the first PRE fragments of step 3.
+template <int FMT, int NF, int PER, int PRE>
+STRATA_DEVICE void stage_steps(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], StageState<FMT, NF>& ss,
+                               const uint8_t* xt, const Q2Sel& ksel, uint8_t* dst,
+                               const uint16_t* __restrict__ src, const int (&xoff)[NF],
+                               const WeightTile& wt, const CopyCursor& cc) {
+  const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_copies<FMT, NF>(dst, src, xoff, wt, cc.ks, cc.woff, cc.soff, s * PER / 3, (s + 1) * PER / 3);
+    read_frags<NF>(xt, m, hh, s + 1, ss.a[(s + 1) & 1]);
+    decode_step<FMT>(ss.sw, s + 1, ss.b[(s + 1) & 1], ksel);
+    mfma_step<NF>(acc0, acc1, ss.a[s & 1], ss.b[s & 1], 0, NF);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step<NF>(acc0, acc1, ss.a[1], ss.b[1], 0, PRE);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Vector-memory operations a wave issued after the copies of stage m, up to the wait for it: the
+// copies of the later stages that exist (PER each, at most PD - 1 stages ahead) and the ST stores
+// of each slice that ended at iterations m - PD .. e0 (e0: the latest slice end before the wait,
+// -1 if none; slice ends are NKs apart).
+template <int PER, int PD>
+STRATA_DEVICE int ops_after(int m, int e0, int NT, int NKs, int ST) {
+  int n = PER * max(0, min(PD - 1, NT - 1 - m));
+  for (int e = e0; e >= 0 && e >= m - PD; e -= NKs) n += ST;
+  return n;
+}
+
+// Stage-boundary wait: this wave's copies of the next stage have landed (n operations issued
+// after them may still be outstanding) and its own LDS reads are complete; then every wave's.
+// A bare s_barrier: __syncthreads() would also drain the copies in flight for later stages.
+// STEADY: the usual n (kPD - 1 later stages, no stores), waited for without the branch tree.
+template <int STEADY>
+STRATA_DEVICE void stage_barrier(int n) {
+  if (n == STEADY) wait_vmcnt<STEADY>();
+  else wait_vmcnt_dyn(n);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt / expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One unit: rows of a chunk times G consecutive column slices, as one pipeline of G * K/64
+// stages (stage js: slice js / (K/64), reduction stage js % (K/64)).  A slice's outputs are
+// written when its last stage is done, while the next slice's copies are already in flight.
+//
+// Software pipeline over the 4 steps of a stage: scheduling region s holds the matrix ops of step
+// s together with the fragment reads and the weight decode of step s+1, so the decode's VALU work
+// issues between the matrix ops.  Within a slice the next stage's set-up (its barrier, weight
+// words, decode tables, step-0 fragments and weights) runs inside step 3, behind the last matrix
+// ops of the stage, so the matrix core does not wait for it at the stage boundary.
+//
+// Copies: stage j + kPD goes into the buffer of stage j - 1, which every wave finished reading
+// before the barrier that opened stage j; its copies are spread over steps 0-2, between the
+// matrix ops (a wave waits at a copy while the address unit still serves earlier ones, and the
+// matrix core keeps running meanwhile).  Past the last stage the copies repeat stage NT - 1 into
+// that free buffer, so that they stay unconditional (no branch splits the step).  The waits count
+// the copies and stores issued after the awaited stage's copies, except those repeats, which only
+// makes them stricter.
+//
+// src/ld: the activation rows (rows_lds[r]: row of unit row r); wt: this lane's weight pieces of
+// slice 0, stage 0; wslice / sslice: byte / fp16 distance between slices in the tiled weights;
+// (ti, ri): this lane's B rows in the LDS weight tiles; out/out_ld/ocols: destination and the
+// columns per slice.
+template <int FMT, int NF, bool UP>
+STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src, int ld, int K,
+                            const int* rows_lds, const int* dst_lds, const WeightTile& wt,
+                            size_t wslice, size_t sslice, int ti0, int ti1, int ri0, int ri1,
+                            uint16_t* __restrict__ out, int out_ld, int ocols, uint8_t* lds) {
+  constexpr int kEpi = UP ? kUpEpiBytes : kDownEpiBytes;
+  using P = Pipe<FMT, NF, kGemmLds - kRowsBytes - kEpi>;
+  using EP = Epilogue<NF, UP>;
+  constexpr int kSt = EP::kStores * NF;  // stores per wave per slice
+  constexpr int kPre = (NF + 1) / 2;     // step-3 fragments issued before the stage barrier
+  uint16_t* epi = reinterpret_cast<uint16_t*>(lds + P::kNBuf * P::kStage);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x16_t acc0[NF], acc1[NF];
+  int xoff[NF];
+#pragma unroll
+  for (int g = 0; g < NF; ++g) {
+    const int r = 8 * (wave + 4 * g) + (lane >> 3);
+    xoff[g] = rows_lds[r] * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 3);
+  }
+  const int NKs = K / kKS, NT = u.nsl * NKs;
+  CopyCursor cc{0, 0, NT, NKs, 0, 0, wslice, sslice};
+#pragma unroll
+  for (int j = 0; j < P::kPD; ++j)
+    if (j < NT) {
+      issue_copies<FMT, NF>(lds + j * P::kStage, src, xoff, wt, cc.ks, cc.woff, cc.soff, 0, P::kPer);
+      cursor_advance<FMT>(cc);
+    }
+  stage_barrier<P::kPer * (P::kPD - 1)>(ops_after<P::kPer, P::kPD>(0, -1, NT, NKs, kSt));
+  const Q2Sel ksel = q2_sel();
+  StageState<FMT, NF> ss;
+  stage_setup<FMT, NF>(ss, lds, ti0, ti1, ri0, ri1, ksel);
+  int j = 0, rb = 0;  // stage and its ring buffer
+  int last_end = -1;  // iteration of the latest slice end
+  for (int sl = 0; sl < u.nsl; ++sl) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      acc0[f] = f32x16_t{};
+      acc1[f] = f32x16_t{};
+    }
+    // the slice's stages; each sets up the next one (on the unit's last stage: a stale buffer,
+    // whose results are not used) inside its step 3
+    for (int ks = 0; ks < NKs; ++ks, ++j) {
+      const int nb = rb + 1 == P::kNBuf ? 0 : rb + 1;                    // buffer of stage j + 1
+      uint8_t* dst = lds + (rb == 0 ? P::kNBuf - 1 : rb - 1) * P::kStage;  // of stage j - 1
+      stage_steps<FMT, NF, P::kPer, kPre>(acc0, acc1, ss, lds + rb * P::kStage, ksel, dst, src, xoff,
+                                          wt, cc);
+      cursor_advance<FMT>(cc);
+      stage_barrier<P::kPer * (P::kPD - 1)>(ops_after<P::kPer, P::kPD>(j + 1, last_end, NT, NKs, kSt));
+      // (the set-up writes the even operands; step 3 uses the odd ones)
+      stage_setup<FMT, NF>(ss, lds + nb * P::kStage, ti0, ti1, ri0, ri1, ksel);
+      mfma_step<NF>(acc0, acc1, ss.a[1], ss.b[1], kPre, NF);
+      __builtin_amdgcn_sched_barrier(0);
+      rb = nb;
+    }
+    // (the staging area is separate from the stage ring, which the next slice's copies fill)
+    write_slice<NF, UP>(acc0, acc1, epi, dst_lds, out, out_ld, (u.slice0 + sl) * ocols);
+    last_end = j - 1;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Up projection: A[p][n] = SiLU(x_t . W_g[n]) * (x_t . W_u[n]) for the chunk's rows p.
 // Slice = 128 outputs; wave w owns outputs slice*128 + w*32 + (lane % 32), gate and up.
-
-constexpr int kUpOutRow = 128 + 8;   // halfs per LDS row of the staged output tile
-constexpr int kDownOutRow = 256;     // 224 rows x 256 halfs fit in the stage ring
-
-template <int FMT, int NF>
-STRATA_DEVICE void up_unit(const UnitInfo& u, const uint16_t* __restrict__ x16, const WeightTile& wt,
-                           int H, int I, uint16_t* __restrict__ a16, uint8_t* lds_bytes,
-                           const int* rows_lds) {
-  f32x16_t accg[NF], accu[NF];
-  // LDS weight tiles 0, 1 = gate rows 0-63, 64-127 of the slice; 2, 3 = the same up rows
-  const int w = threadIdx.x >> 6, ri = (w & 1) * 32 + (threadIdx.x & 31);
-  gemm_core<FMT, NF>(accg, accu, x16, H, H, rows_lds, wt, w >> 1, 2 + (w >> 1), ri, ri, lds_bytes);
-  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_bytes);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 31, hh = lane >> 5;
-  // stage SiLU(g)*u as fp16 in LDS (columns in P8 order within groups of 8), then 16-byte stores
-  const int lcol = wave * 32 + (nl & ~7) + p8inv(nl & 7);
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = f * 32 + acc_row(r, hh);
-      lds[row * kUpOutRow + lcol] =
-          __builtin_bit_cast(uint16_t, f32_to_f16_sat(silu_mul(accg[f][r], accu[f][r])));
-    }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2 * NF; ++i) {
-    const int p = threadIdx.x + i * kGemmThreads;  // 16 pieces per row
-    const int r = p >> 4, c = p & 15;
-    if (r < u.nrows)
-      *reinterpret_cast<u32x4_t*>(a16 + (size_t)(u.row_start + r) * I + u.slice * 128 + c * 8) =
-          *reinterpret_cast<const u32x4_t*>(lds + r * kUpOutRow + c * 8);
-  }
-}
 
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
@@ -440,93 +573,86 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
     const Chunk* __restrict__ chunks, const int* __restrict__ n_chunks,
     const uint8_t* __restrict__ gate_codes, const uint8_t* __restrict__ up_codes,
     const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales, int H, int I,
-    uint16_t* __restrict__ a16) {
+    int G, uint16_t* __restrict__ a16) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int* rows_lds = reinterpret_cast<int*>(smem + kLdsBudget);
+  int* rows_lds = reinterpret_cast<int*>(smem + kGemmLds - kRowsBytes);
+  int* dst_lds = rows_lds + kChunkRows;
   UnitInfo u;
-  if (!pick_unit(chunks, n_chunks, I / 128, u)) return;
-  const int wave = threadIdx.x >> 6;
+  if (!pick_unit(chunks, n_chunks, I / 128 / G, G, u)) return;
+  constexpr int GB = 8 * (FMT == 2 ? 8 : 12);
+  const int wave = threadIdx.x >> 6, nkt = H / 64;
   // wave w copies gate (w < 2) or up rows 128 slice + 64 (w & 1) .. + 63 of the expert
-  const size_t row0 = (size_t)u.expert * I + 128 * u.slice + 64 * (wave & 1);
+  const size_t row0 = (size_t)u.expert * I + 128 * u.slice0 + 64 * (wave & 1);
   const WeightTile wt = weight_tile<FMT>(wave < 2 ? gate_codes : up_codes,
-                                         wave < 2 ? gate_scales : up_scales, row0, H / 64);
-  for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads)
-    rows_lds[r] = sorted_slot[u.row_start + (r < u.nrows ? r : 0)] / k;
-  __syncthreads();
-  switch (u.nfrag) {
-    case 1: up_unit<FMT, 1>(u, x16, wt, H, I, a16, smem, rows_lds); break;
-    case 2: up_unit<FMT, 2>(u, x16, wt, H, I, a16, smem, rows_lds); break;
-    case 3: up_unit<FMT, 3>(u, x16, wt, H, I, a16, smem, rows_lds); break;
-    case 4: up_unit<FMT, 4>(u, x16, wt, H, I, a16, smem, rows_lds); break;
-    case 5: up_unit<FMT, 5>(u, x16, wt, H, I, a16, smem, rows_lds); break;
-    case 6: up_unit<FMT, 6>(u, x16, wt, H, I, a16, smem, rows_lds); break;
-    default: up_unit<FMT, 7>(u, x16, wt, H, I, a16, smem, rows_lds); break;
+                                         wave < 2 ? gate_scales : up_scales, row0, nkt);
+  for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads) {
+    const int rr = r < u.nrows ? r : 0;
+    rows_lds[r] = sorted_slot[u.row_start + rr] / k;
+    dst_lds[r] = u.row_start + rr;
   }
+  __syncthreads();
+  // a slice is 128 gate (and up) rows = 32 groups of 4
+  const size_t wsl = (size_t)32 * nkt * GB, ssl = (size_t)32 * nkt * 8;
+  // LDS weight tiles 0, 1 = gate rows 0-63, 64-127 of the slice; 2, 3 = the same up rows
+  const int ri = (wave & 1) * 32 + (threadIdx.x & 31);
+#define STRATA_UP_UNIT(NF)                                                                        \
+  run_unit<FMT, NF, true>(u, x16, H, H, rows_lds, dst_lds, wt, wsl, ssl, wave >> 1, 2 + (wave >> 1), \
+                          ri, ri, a16, I, 128, smem)
+  switch (u.nfrag) {
+    case 1: STRATA_UP_UNIT(1); break;
+    case 2: STRATA_UP_UNIT(2); break;
+    case 3: STRATA_UP_UNIT(3); break;
+    case 4: STRATA_UP_UNIT(4); break;
+    case 5: STRATA_UP_UNIT(5); break;
+    case 6: STRATA_UP_UNIT(6); break;
+    default: STRATA_UP_UNIT(7); break;
+  }
+#undef STRATA_UP_UNIT
 }
 
 // ---------------------------------------------------------------------------------------------
 // Down projection: out[slot(p)][h] = A[p] . W_d[h] for the chunk's rows p, written as bf16 in
 // slot order.  Slice = 256 outputs; wave w owns h = slice*256 + w*64 + nf*32 + (lane % 32).
 
-template <int FMT, int NF>
-STRATA_DEVICE void down_unit(const UnitInfo& u, const uint16_t* __restrict__ a16,
-                             const int* __restrict__ sorted_slot, const WeightTile& wt, int H,
-                             int I, uint16_t* __restrict__ expert_out, uint8_t* lds_bytes,
-                             const int* rows_lds) {
-  f32x16_t acc0[NF], acc1[NF];
-  // LDS weight tile w = rows 64 w .. 64 w + 63 of the slice
-  const int w = threadIdx.x >> 6, ri = threadIdx.x & 31;
-  gemm_core<FMT, NF>(acc0, acc1, a16, I, I, rows_lds, wt, w, w, ri, 32 + ri, lds_bytes);
-  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_bytes);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = f * 32 + acc_row(r, hh);
-      lds[row * kDownOutRow + wave * 64 + nl] = f32_to_bf16(acc0[f][r]);
-      lds[row * kDownOutRow + wave * 64 + 32 + nl] = f32_to_bf16(acc1[f][r]);
-    }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4 * NF; ++i) {
-    const int p = threadIdx.x + i * kGemmThreads;  // 32 pieces per row
-    const int r = p >> 5, c = p & 31;
-    if (r < u.nrows) {
-      const size_t slot = (size_t)sorted_slot[u.row_start + r];
-      *reinterpret_cast<u32x4_t*>(expert_out + slot * H + u.slice * 256 + c * 8) =
-          *reinterpret_cast<const u32x4_t*>(lds + r * kDownOutRow + c * 8);
-    }
-  }
-}
-
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
     const uint16_t* __restrict__ a16, const int* __restrict__ sorted_slot,
     const Chunk* __restrict__ chunks, const int* __restrict__ n_chunks,
     const uint8_t* __restrict__ down_codes, const uint16_t* __restrict__ down_scales, int H, int I,
-    uint16_t* __restrict__ expert_out) {
+    int G, uint16_t* __restrict__ expert_out) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int* rows_lds = reinterpret_cast<int*>(smem + kLdsBudget);
+  int* rows_lds = reinterpret_cast<int*>(smem + kGemmLds - kRowsBytes);
+  int* dst_lds = rows_lds + kChunkRows;
   UnitInfo u;
-  if (!pick_unit(chunks, n_chunks, H / 256, u)) return;
-  const int wave = threadIdx.x >> 6;
+  if (!pick_unit(chunks, n_chunks, H / 256 / G, G, u)) return;
+  constexpr int GB = 8 * (FMT == 2 ? 8 : 12);
+  const int wave = threadIdx.x >> 6, nkt = I / 64;
   // wave w copies rows 256 slice + 64 w .. + 63 of the expert
-  const size_t row0 = (size_t)u.expert * H + 256 * u.slice + 64 * wave;
-  const WeightTile wt = weight_tile<FMT>(down_codes, down_scales, row0, I / 64);
-  for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads)
-    rows_lds[r] = u.row_start + (r < u.nrows ? r : 0);
-  __syncthreads();
-  switch (u.nfrag) {
-    case 1: down_unit<FMT, 1>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
-    case 2: down_unit<FMT, 2>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
-    case 3: down_unit<FMT, 3>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
-    case 4: down_unit<FMT, 4>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
-    case 5: down_unit<FMT, 5>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
-    case 6: down_unit<FMT, 6>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
-    default: down_unit<FMT, 7>(u, a16, sorted_slot, wt, H, I, expert_out, smem, rows_lds); break;
+  const size_t row0 = (size_t)u.expert * H + 256 * u.slice0 + 64 * wave;
+  const WeightTile wt = weight_tile<FMT>(down_codes, down_scales, row0, nkt);
+  for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads) {
+    const int rr = r < u.nrows ? r : 0;
+    rows_lds[r] = u.row_start + rr;
+    dst_lds[r] = sorted_slot[u.row_start + rr];
   }
+  __syncthreads();
+  // a slice is 256 rows = 64 groups of 4
+  const size_t wsl = (size_t)64 * nkt * GB, ssl = (size_t)64 * nkt * 8;
+  // LDS weight tile w = rows 64 w .. 64 w + 63 of the slice
+  const int ri = threadIdx.x & 31;
+#define STRATA_DOWN_UNIT(NF)                                                                      \
+  run_unit<FMT, NF, false>(u, a16, I, I, rows_lds, dst_lds, wt, wsl, ssl, wave, wave, ri, 32 + ri, \
+                           expert_out, H, 256, smem)
+  switch (u.nfrag) {
+    case 1: STRATA_DOWN_UNIT(1); break;
+    case 2: STRATA_DOWN_UNIT(2); break;
+    case 3: STRATA_DOWN_UNIT(3); break;
+    case 4: STRATA_DOWN_UNIT(4); break;
+    case 5: STRATA_DOWN_UNIT(5); break;
+    case 6: STRATA_DOWN_UNIT(6); break;
+    default: STRATA_DOWN_UNIT(7); break;
+  }
+#undef STRATA_DOWN_UNIT
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -623,6 +749,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 static int grid_for_units(int64_t max_units) { return (int)(8 * ((max_units + 7) / 8)); }
 
+// Slices per unit: the largest divisor of n_slices not above gmax.  More slices per unit pay the
+// unit's fixed costs (launch, row tables, pipeline fill) once for several slices; fewer keep
+// enough units to balance the CUs.
+static int slices_per_unit(int n_slices, int gmax) {
+  for (int g = gmax; g > 1; --g)
+    if (n_slices % g == 0) return g;
+  return 1;
+}
+
 // The GEMM kernels use more than 64 KB of dynamic LDS; allow it once per process.
 static void allow_big_lds() {
   static std::once_flag once;
@@ -648,18 +783,17 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, i
                          const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
                          hipStream_t s) {
   (void)E;
-  const int grid = grid_for_units((int64_t)max_chunks_ * (I / 128));
+  const int G = slices_per_unit(I / 128, 3);
+  const int grid = grid_for_units((int64_t)max_chunks_ * (I / 128 / G));
   const uint8_t* gc = static_cast<const uint8_t*>(gate_codes);
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
-  if (fmt == 2) {
-    allow_big_lds();
+  allow_big_lds();
+  if (fmt == 2)
     ffn_up_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(x16, sorted_slot, k, chunks, n_chunks, gc,
-                                                          uc, gate_scales, up_scales, H, I, a16);
-  } else {
-    allow_big_lds();
+                                                          uc, gate_scales, up_scales, H, I, G, a16);
+  else
     ffn_up_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(x16, sorted_slot, k, chunks, n_chunks, gc,
-                                                          uc, gate_scales, up_scales, H, I, a16);
-  }
+                                                          uc, gate_scales, up_scales, H, I, G, a16);
   return hipGetLastError();
 }
 
@@ -668,17 +802,16 @@ hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot,
                            const void* down_codes, const uint16_t* down_scales, int E, int H,
                            int I, uint16_t* expert_out, hipStream_t s) {
   (void)E;
-  const int grid = grid_for_units((int64_t)max_chunks_ * (H / 256));
+  const int G = slices_per_unit(H / 256, 4);
+  const int grid = grid_for_units((int64_t)max_chunks_ * (H / 256 / G));
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
-  if (fmt == 2) {
-    allow_big_lds();
+  allow_big_lds();
+  if (fmt == 2)
     ffn_down_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(a16, sorted_slot, chunks, n_chunks, dc,
-                                                            down_scales, H, I, expert_out);
-  } else {
-    allow_big_lds();
+                                                            down_scales, H, I, G, expert_out);
+  else
     ffn_down_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(a16, sorted_slot, chunks, n_chunks, dc,
-                                                            down_scales, H, I, expert_out);
-  }
+                                                            down_scales, H, I, G, expert_out);
   return hipGetLastError();
 }
 
