@@ -210,11 +210,13 @@ strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t*
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_up(w->fmt, p.x16, sorted_slot, k, p.chunks, p.n_chunks, p.max_chunks,
+    e = strata::launch_ffn_up(w->fmt, p.x16, sorted_slot, k, (int64_t)T * k, p.chunks, p.n_chunks,
+                              p.max_chunks,
                               w->gate_codes, w->up_codes, w->gate_scales, w->up_scales, E, H, I,
                               p.a16, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_down(w->fmt, p.a16, sorted_slot, p.chunks, p.n_chunks, p.max_chunks,
+    e = strata::launch_ffn_down(w->fmt, p.a16, sorted_slot, (int64_t)T * k, p.chunks, p.n_chunks,
+                                p.max_chunks,
                                 w->down_codes, w->down_scales, E, H, I, expert_out, stream);
   return from_hip(e);
 }
@@ -289,11 +291,13 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
                                p.tile_base, p.chunks, p.n_chunks, stream);
   if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_up(w->fmt, p.x16, sorted, k, p.chunks, p.n_chunks, p.max_chunks,
+    e = strata::launch_ffn_up(w->fmt, p.x16, sorted, k, (int64_t)T * k, p.chunks, p.n_chunks,
+                              p.max_chunks,
                               w->gate_codes, w->up_codes, w->gate_scales, w->up_scales, E, H, I,
                               p.a16, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_down(w->fmt, p.a16, sorted, p.chunks, p.n_chunks, p.max_chunks,
+    e = strata::launch_ffn_down(w->fmt, p.a16, sorted, (int64_t)T * k, p.chunks, p.n_chunks,
+                                p.max_chunks,
                                 w->down_codes, w->down_scales, E, H, I, p.expert_out, stream);
   if (e == hipSuccess) e = strata::launch_combine(p.expert_out, rw, T, k, H, y, accumulate, stream);
   return from_hip(e);

@@ -39,13 +39,14 @@ hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int*
 // x bf16 [T][H] -> fp16 in the fragment order of the grouped GEMM (see prefill.hip).
 hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, hipStream_t s);
 
-hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k,
+// S: the number of slots (sizes the work units; the chunk list itself is read on the device).
+hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k, int64_t S,
                          const Chunk* chunks, const int* n_chunks, int max_chunks,
                          const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
                          hipStream_t s);
 
-hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot,
+hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot, int64_t S,
                            const Chunk* chunks, const int* n_chunks, int max_chunks,
                            const void* down_codes, const uint16_t* down_scales, int E, int H,
                            int I, uint16_t* expert_out, hipStream_t s);

@@ -749,12 +749,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 static int grid_for_units(int64_t max_units) { return (int)(8 * ((max_units + 7) / 8)); }
 
-// Slices per unit: the largest divisor of n_slices not above gmax.  More slices per unit pay the
-// unit's fixed costs (launch, row tables, pipeline fill) once for several slices; fewer keep
-// enough units to balance the CUs.
-static int slices_per_unit(int n_slices, int gmax) {
+// Slices per unit: the largest divisor of n_slices not above gmax that still leaves about two
+// units per CU for the fewest chunks S slots can make.  More slices per unit pay the unit's fixed
+// costs (launch, row tables, pipeline fill) once for several slices; fewer keep enough units to
+// fill and balance the CUs (a skewed routing concentrates the slots in few chunks).
+static int slices_per_unit(int n_slices, int gmax, int64_t S) {
+  const int64_t min_chunks = (S + kChunkRows - 1) / kChunkRows;
   for (int g = gmax; g > 1; --g)
-    if (n_slices % g == 0) return g;
+    if (n_slices % g == 0 && min_chunks * (n_slices / g) >= 2 * 256) return g;
   return 1;
 }
 
@@ -777,13 +779,13 @@ hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k,
+hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k, int64_t S,
                          const Chunk* chunks, const int* n_chunks, int max_chunks_,
                          const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
                          hipStream_t s) {
   (void)E;
-  const int G = slices_per_unit(I / 128, 3);
+  const int G = slices_per_unit(I / 128, 3, S);
   const int grid = grid_for_units((int64_t)max_chunks_ * (I / 128 / G));
   const uint8_t* gc = static_cast<const uint8_t*>(gate_codes);
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
@@ -797,12 +799,12 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, i
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot,
+hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot, int64_t S,
                            const Chunk* chunks, const int* n_chunks, int max_chunks_,
                            const void* down_codes, const uint16_t* down_scales, int E, int H,
                            int I, uint16_t* expert_out, hipStream_t s) {
   (void)E;
-  const int G = slices_per_unit(H / 256, 4);
+  const int G = slices_per_unit(H / 256, 4, S);
   const int grid = grid_for_units((int64_t)max_chunks_ * (H / 256 / G));
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
   allow_big_lds();
