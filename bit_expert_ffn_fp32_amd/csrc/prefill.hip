@@ -785,7 +785,7 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, i
                          const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
                          hipStream_t s) {
   (void)E;
-  const int G = slices_per_unit(I / 128, 3, S);
+  const int G = slices_per_unit(I / 128, 1, S);
   const int grid = grid_for_units((int64_t)max_chunks_ * (I / 128 / G));
   const uint8_t* gc = static_cast<const uint8_t*>(gate_codes);
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
@@ -804,7 +804,7 @@ hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot,
                            const void* down_codes, const uint16_t* down_scales, int E, int H,
                            int I, uint16_t* expert_out, hipStream_t s) {
   (void)E;
-  const int G = slices_per_unit(H / 256, 4, S);
+  const int G = slices_per_unit(H / 256, 2, S);
   const int grid = grid_for_units((int64_t)max_chunks_ * (H / 256 / G));
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
   allow_big_lds();
