@@ -37,6 +37,7 @@ _lib = None
 # tensor tags of the stream id: stream = (layer << 8) | tag
 TAG_X, TAG_LOGITS, TAG_GATE_CODES, TAG_UP_CODES, TAG_DOWN_CODES = 1, 2, 3, 4, 5
 TAG_GATE_SCALES, TAG_UP_SCALES, TAG_DOWN_SCALES, TAG_ZIPF_RANK = 6, 7, 8, 9
+TAG_ROUTER_W, TAG_SHARED_GATE, TAG_SHARED_UP, TAG_SHARED_DOWN = 10, 11, 12, 13
 
 Q2, Q3 = 2, 3
 CODE_BYTES = {Q2: 8, Q3: 12}
@@ -220,6 +221,27 @@ def make_logits(shape: Shape, seed: int = 0, layer: int = 0, T: int | None = Non
     T = shape.T if T is None else T
     bias = zipf_bias(seed, layer, shape.E) if shape.zipf else None
     return normal_f32(seed, stream_id(layer, TAG_LOGITS), T * shape.E, bias=bias).reshape(T, shape.E)
+
+
+def dense_bf16(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """bf16 bits [rows][cols] of N(0, 1/cols): a dense layer that keeps unit-variance inputs at
+    unit variance."""
+    return f32_to_bf16_bits(normal_f32(seed, stream, rows * cols, scale=cols ** -0.5)).reshape(rows, cols)
+
+
+def make_router(shape: Shape, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """Router projection W_r, bf16 bits [E][H] (logits of unit-variance x are ~N(0,1))."""
+    return dense_bf16(seed, stream_id(layer, TAG_ROUTER_W), shape.E, shape.H)
+
+
+def make_shared(shape: Shape, seed: int = 0, layer: int = 0) -> dict:
+    """Shared expert, bf16 bits: W_sg, W_su [I][H] and W_sd [H][I] (intermediate size I, the
+    same as a routed expert's)."""
+    H, I = shape.H, shape.I
+    return {"H": H, "I": I,
+            "gate": dense_bf16(seed, stream_id(layer, TAG_SHARED_GATE), I, H),
+            "up": dense_bf16(seed, stream_id(layer, TAG_SHARED_UP), I, H),
+            "down": dense_bf16(seed, stream_id(layer, TAG_SHARED_DOWN), H, I)}
 
 
 def make_h0(shape: Shape, seed: int = 0, T: int | None = None) -> np.ndarray:

@@ -70,7 +70,11 @@ def lib():
         L.oracle_layer_rows.argtypes = [ctypes.POINTER(_Weights), vp, vp, i32, i32, vp, i32, vp]
         L.oracle_layer_rows.restype = i32
         L.oracle_rmsnorm.argtypes = [vp, i32, i32, dbl, vp]
+        L.oracle_router_logits.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.oracle_shared_expert.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
         L.oracle_rmsnorm.restype = None
+        L.oracle_router_logits.restype = None
+        L.oracle_shared_expert.restype = None
         _lib = L
     return _lib
 
@@ -207,3 +211,28 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     x = np.empty((T, H), dtype=np.uint16)
     lib().oracle_rmsnorm(ph, T, H, eps, x.ctypes.data)
     return x
+
+
+def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
+    """logits fp64 [T][E] = x W_r^T (x bf16 bits [T][H], W_r bf16 bits [E][H])."""
+    xx, px = _c(x, np.uint16)
+    ww, pw = _c(wr, np.uint16)
+    T, H = xx.shape
+    E = ww.shape[0]
+    out = np.empty((T, E), dtype=np.float64)
+    lib().oracle_router_logits(px, pw, T, H, E, out.ctypes.data)
+    return out
+
+
+def shared_expert(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """Shared expert output fp64 [T][H] (all arguments bf16 bits: x [T][H], W_sg and W_su
+    [Is][H], W_sd [H][Is])."""
+    xx, px = _c(x, np.uint16)
+    g, pg = _c(wg, np.uint16)
+    u, pu = _c(wu, np.uint16)
+    d, pd = _c(wd, np.uint16)
+    T, H = xx.shape
+    Is = g.shape[0]
+    out = np.empty((T, H), dtype=np.float64)
+    lib().oracle_shared_expert(px, pg, pu, pd, T, H, Is, out.ctypes.data)
+    return out

@@ -268,3 +268,48 @@ void oracle_rmsnorm(const float* h, int32_t T, int32_t H, double eps, uint16_t* 
     }
   }
 }
+
+/*
+ * Router projection: logits[t][e] = sum over h (ascending) of x[t][h] * W_r[e][h], with x (the
+ * layer input after RMSNorm) and W_r [E][H] in bf16, widened exactly.  The pages place the
+ * routers on the GPU beside the experts ("Strata - the details", How it works / memory tiers;
+ * "Strata vs Llama.cpp vs vLLM", transcript at 09:28) and give no formula; a dense linear map
+ * from the hidden state to one logit per expert is this library's definition.
+ */
+void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int32_t H, int32_t E,
+                          double* logits) {
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int32_t h = 0; h < H; ++h)
+        acc += oracle_bf16_to_f64(x[(int64_t)t * H + h]) * oracle_bf16_to_f64(wr[(int64_t)e * H + h]);
+      logits[(int64_t)t * E + e] = acc;
+    }
+}
+
+/*
+ * Shared expert on every token: g = W_sg x, u = W_su x, a = SiLU(g) * u, out = W_sd a, with dense
+ * bf16 weights W_sg, W_su [Is][H] and W_sd [H][Is] widened exactly.  The pages list shared experts
+ * among what stays on the GPU ("Strata - the details", How it works / memory tiers; "Strata vs
+ * Llama.cpp vs vLLM", transcript at 09:28); the SwiGLU form, the same as a routed expert's but
+ * dense and unscaled, is this library's definition.  out [T][H].
+ */
+void oracle_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                          const uint16_t* wd, int32_t T, int32_t H, int32_t Is, double* out) {
+  double* a = (double*)malloc(sizeof(double) * (size_t)Is);
+  for (int32_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + (int64_t)t * H;
+    for (int32_t n = 0; n < Is; ++n) {
+      double g = 0.0, u = 0.0;
+      for (int32_t h = 0; h < H; ++h) g += oracle_bf16_to_f64(wg[(int64_t)n * H + h]) * oracle_bf16_to_f64(xr[h]);
+      for (int32_t h = 0; h < H; ++h) u += oracle_bf16_to_f64(wu[(int64_t)n * H + h]) * oracle_bf16_to_f64(xr[h]);
+      a[n] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int32_t h = 0; h < H; ++h) {
+      double o = 0.0;
+      for (int32_t n = 0; n < Is; ++n) o += oracle_bf16_to_f64(wd[(int64_t)h * Is + n]) * a[n];
+      out[(int64_t)t * H + h] = o;
+    }
+  }
+  free(a);
+}

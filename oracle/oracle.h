@@ -46,6 +46,10 @@ int32_t oracle_layer(const oracle_weights* w, const uint16_t* x, const float* lo
 int32_t oracle_layer_rows(const oracle_weights* w, const uint16_t* x, const float* logits,
                           int32_t T, int32_t k, const int32_t* rows, int32_t n_rows, double* y_rows);
 void oracle_rmsnorm(const float* h, int32_t T, int32_t H, double eps, uint16_t* x);
+void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int32_t H, int32_t E,
+                          double* logits);
+void oracle_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                          const uint16_t* wd, int32_t T, int32_t H, int32_t Is, double* out);
 
 #ifdef __cplusplus
 }

@@ -352,6 +352,91 @@ def test_rmsnorm_unit_rms_and_scale_invariance(oracle_lib):
 
 
 # ---------------------------------------------------------------------------------------------
+# ---------------------------------------------------------------------------------------------
+# Router projection and shared expert (dense bf16 layers on either side of the routed experts)
+
+
+def test_router_logits_one_hot_rows_pick_weight_columns(oracle_lib):
+    """x = rows of the identity: logits[t][e] must be W_r[e][t] exactly (E != H, so a transposed
+    weight index or a dropped term fails)."""
+    H, E = 64, 24
+    wr = mi.dense_bf16(5, 77, E, H)
+    x = mi.f32_to_bf16_bits(np.eye(H, dtype=np.float32)[:10])
+    l = oracle.router_logits(x, wr)
+    assert l.shape == (10, E)
+    assert np.array_equal(l, mi.bf16_bits_to_f32(wr).astype(np.float64)[:, :10].T)
+
+
+def test_router_logits_matches_float64_matmul(oracle_lib):
+    shape = small_shape(T=7, H=256, E=48)
+    x = mi.make_x(shape, seed=2)
+    wr = mi.make_router(shape, seed=2)
+    ref = mi.bf16_bits_to_f32(x).astype(np.float64) @ mi.bf16_bits_to_f32(wr).astype(np.float64).T
+    l = oracle.router_logits(x, wr)
+    np.testing.assert_allclose(l, ref, rtol=1e-13, atol=1e-14 * np.abs(ref).max())
+    # products of bf16 values are exact in fp64 and the sums of 256 of them lose at most a few
+    # ulps: the unit-variance generator gives logits of about unit spread
+    assert 0.7 < l.std() < 1.4
+
+
+def shared_reference(x, wg, wu, wd):
+    f = lambda b: torch.from_numpy(mi.bf16_bits_to_f32(b).astype(np.float64))
+    xx = f(x)
+    a = torch.nn.functional.silu(xx @ f(wg).T) * (xx @ f(wu).T)
+    return (a @ f(wd).T).numpy()
+
+
+def test_shared_expert_matches_torch_swiglu(oracle_lib):
+    shape = small_shape(T=9, H=256, I=128)
+    sh = mi.make_shared(shape, seed=4)
+    x = mi.make_x(shape, seed=4)
+    out = oracle.shared_expert(x, sh["gate"], sh["up"], sh["down"])
+    ref = shared_reference(x, sh["gate"], sh["up"], sh["down"])
+    assert out.shape == (9, 256)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13 * np.abs(ref).max())
+    # gate and up are not interchangeable: SiLU acts on the gate projection only
+    swapped = oracle.shared_expert(x, sh["up"], sh["gate"], sh["down"])
+    assert np.abs(swapped - out).max() > 1e-3 * np.abs(out).max()
+
+
+def test_shared_expert_equals_routed_expert_with_exact_weights(oracle_lib):
+    """A shared expert whose bf16 weights equal a routed expert's dequantized weights computes
+    the same SwiGLU FFN as that expert: with every block scale 2^-6 the weights d(q - 1.5) are
+    exact in bf16, so the two oracle paths (quantized-block and dense) must agree to rounding."""
+    shape = small_shape(T=4, H=128, E=2, k=1, I=64)
+    w = mi.make_weights(shape, seed=6)
+    for name in ("gate", "up", "down"):
+        w[name + "_scales"] = np.full_like(w[name + "_scales"], 0x2400)   # fp16 2^-6
+    e = 1
+    dense = {}
+    for name in ("gate", "up", "down"):
+        m = dequant_np(2, w[name + "_codes"][e], w[name + "_scales"][e])
+        bits = mi.f32_to_bf16_bits(m.astype(np.float32))
+        assert np.array_equal(mi.bf16_bits_to_f32(bits).astype(np.float64), m)
+        dense[name] = bits
+    x = mi.make_x(shape, seed=6)
+    out = oracle.shared_expert(x, dense["gate"], dense["up"], dense["down"])
+    for t in range(shape.T):
+        o, _ = oracle.expert_ffn(w, e, x[t])
+        np.testing.assert_allclose(out[t], o, rtol=1e-12, atol=1e-14 * np.abs(o).max())
+
+
+def test_shared_expert_zero_and_scaling(oracle_lib):
+    shape = small_shape(T=3, H=128, I=64)
+    sh = mi.make_shared(shape, seed=8)
+    x = mi.make_x(shape, seed=8)
+    out = oracle.shared_expert(x, sh["gate"], sh["up"], sh["down"])
+    zero = np.zeros_like(sh["gate"])
+    assert np.array_equal(oracle.shared_expert(x, zero, sh["up"], sh["down"]), np.zeros((3, 128)))
+    assert np.array_equal(oracle.shared_expert(x, sh["gate"], zero, sh["down"]), np.zeros((3, 128)))
+    # doubling W_sd (exact in bf16) doubles the output exactly; the output is linear in W_su
+    d2 = mi.f32_to_bf16_bits(2 * mi.bf16_bits_to_f32(sh["down"]))
+    assert np.array_equal(oracle.shared_expert(x, sh["gate"], sh["up"], d2), 2 * out)
+    u2 = mi.f32_to_bf16_bits(-2 * mi.bf16_bits_to_f32(sh["up"]))
+    np.testing.assert_allclose(oracle.shared_expert(x, sh["gate"], u2, sh["down"]), -2 * out,
+                               rtol=1e-13, atol=1e-15)
+
+
 # Golden regression values (written by tests/golden/make_golden.py from the oracle only)
 
 
