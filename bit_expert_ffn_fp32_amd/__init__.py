@@ -23,8 +23,9 @@ CODE_BYTES = {Q2: 8, Q3: 12}
 
 EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "strata_moe_combine",
            "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
+           "strata_moe_router_logits", "strata_moe_shared_expert",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
-           "strata_status_string"]
+           "strata_moe_shared_workspace_bytes", "strata_status_string"]
 
 
 class StrataError(RuntimeError):
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
             "strata_moe_layer": [W, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "strata_moe_rmsnorm": [vp, i32, i32, ctypes.c_float, vp, vp],
             "strata_moe_pack_matrix": [i32, i32, i32, i32, vp, vp, vp, vp, vp],
+            "strata_moe_router_logits": [vp, vp, i32, i32, i32, vp, vp],
+            "strata_moe_shared_expert": [vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -71,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.strata_moe_permute_workspace_bytes.restype = sz
         L.strata_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.strata_moe_workspace_bytes.restype = sz
+        L.strata_moe_shared_workspace_bytes.argtypes = [i32, i32]
+        L.strata_moe_shared_workspace_bytes.restype = sz
         L.strata_status_string.argtypes = [ctypes.c_int]
         L.strata_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -148,6 +153,10 @@ def workspace_bytes(T: int, E: int, k: int, H: int, I: int) -> int:
     return lib().strata_moe_workspace_bytes(T, E, k, H, I)
 
 
+def shared_workspace_bytes(T: int, I: int) -> int:
+    return lib().strata_moe_shared_workspace_bytes(T, I)
+
+
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
@@ -209,3 +218,24 @@ def strata_moe_pack_matrix(fmt, n_mat, rows, K, codes, scales, tiled_codes, tile
 def strata_moe_rmsnorm(h, x, eps=1e-6, stream=None) -> None:
     T, H = h.shape
     _check("strata_moe_rmsnorm", lib().strata_moe_rmsnorm(_p(h), T, H, eps, _p(x), _stream(stream)))
+
+
+def strata_moe_router_logits(x, w_router, logits, stream=None) -> None:
+    """logits fp32 [T][E] = x W_r^T (x bf16 [T][H], w_router bf16 [E][H]; bf16 tensors or their
+    int16 bit patterns)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check("strata_moe_router_logits", lib().strata_moe_router_logits(
+        _p(x), _p(w_router), T, H, E, _p(logits), _stream(stream)))
+
+
+def strata_moe_shared_expert(x, w_gate, w_up, w_down, y, workspace, accumulate=False,
+                             stream=None) -> None:
+    """y (=, or += with accumulate) SwiGLU shared expert of x (bf16 [T][H]); w_gate, w_up
+    [I][H] and w_down [H][I] bf16; y fp32 [T][H]."""
+    T, H = x.shape
+    I = w_gate.shape[0]
+    _check("strata_moe_shared_expert", lib().strata_moe_shared_expert(
+        _p(x), _p(w_gate), _p(w_up), _p(w_down), T, H, I, _p(y), int(accumulate), _p(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))

@@ -325,6 +325,42 @@ strata_status strata_moe_pack_matrix(int32_t fmt, int32_t n_mat, int32_t rows, i
                                       tiled_scales, stream));
 }
 
+size_t strata_moe_shared_workspace_bytes(int32_t T, int32_t I) {
+  if (T < 0 || I < 1) return 0;
+  return round_up((size_t)T * I * 2);
+}
+
+strata_status strata_moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T,
+                                       int32_t H, int32_t E, float* logits, hipStream_t stream) {
+  if (T < 0 || H < 1 || E < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if (H % 64) return STRATA_ERR_UNSUPPORTED;
+  if ((int64_t)T * H > INT32_MAX || (int64_t)E * H > INT32_MAX || (int64_t)T * E > INT32_MAX)
+    return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[3] = {x, w_router, logits};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_router_logits(x, w_router, T, H, E, logits, stream));
+}
+
+strata_status strata_moe_shared_expert(const uint16_t* x, const uint16_t* w_gate,
+                                       const uint16_t* w_up, const uint16_t* w_down, int32_t T,
+                                       int32_t H, int32_t I, float* y, int32_t accumulate,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (T < 0 || H < 1 || I < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if (H % 64 || I % 64) return STRATA_ERR_UNSUPPORTED;
+  if ((int64_t)T * H > INT32_MAX || (int64_t)T * I > INT32_MAX || (int64_t)H * I > INT32_MAX)
+    return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[6] = {x, w_gate, w_up, w_down, y, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < strata_moe_shared_workspace_bytes(T, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(strata::launch_shared_expert(x, w_gate, w_up, w_down, T, H, I, y, accumulate,
+                                               static_cast<uint16_t*>(workspace), stream));
+}
+
 strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
                                  hipStream_t stream) {
   if (T < 0 || H < 1 || !(eps >= 0.0f)) return STRATA_ERR_INVALID_ARGUMENT;

@@ -1,0 +1,380 @@
+// Dense bf16 layers beside the routed experts: the router projection and the shared expert.
+//
+// The pages keep a layer's routers and its shared experts on the GPU next to the expert caches
+// ("Strata - the details", How it works / memory tiers; "Strata vs Llama.cpp vs vLLM", transcript
+// at 09:28).  Both are dense products out = x W^T with x bf16 [M][K] and W bf16 [N][K], both
+// K-contiguous:
+//  * router: logits fp32 [T][E] = x W_r^T;
+//  * shared expert: a = SiLU(x W_sg^T) * (x W_su^T) rounded to bf16 [T][I], then
+//    y (+)= a W_sd^T in fp32 [T][H].
+//
+// Two kernels per product, chosen by the number of token rows M:
+//  * M <= 8 (decode / draft verification): a bandwidth-bound GEMV.  A workgroup streams 8 weight
+//    rows with 32 lanes per row (16-byte loads, 512 contiguous bytes per row and instruction),
+//    keeps the M token rows in LDS and reduces each row's dot products across its 32 lanes.
+//  * larger M: an MFMA GEMM, v_mfma_f32_32x32x16_bf16 with fp32 accumulation, tiles of
+//    BM = 128 or 256 rows by 128 columns, 64 reduction indices per stage copied global -> LDS
+//    with global_load_lds into a ring of stages, one barrier per stage.
+//
+// The SwiGLU epilogue needs a token's gate and up sums of the same output in one lane: the GEMM's
+// 128 weight rows of a tile are [gate o..o+31, up o..o+31, gate o+32..o+63, up o+32..o+63], so a
+// wave's two 32-column fragments hold the gate and up projections of the same 32 outputs.
+#include <mutex>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+namespace strata {
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Epilogues.
+enum DenseEpi { kEpiStore = 0, kEpiAccum = 1, kEpiSwiglu = 2 };
+
+STRATA_DEVICE float silu_mul_f(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ---------------------------------------------------------------------------------------------
+// MFMA GEMM.
+
+constexpr int kDK = 64;       // reduction indices per stage (128 bytes of a row)
+constexpr int kDBN = 128;     // weight rows (output columns) per tile
+constexpr int kDLds = 160 * 1024;
+
+template <int WM>
+struct DenseCfg {
+  static constexpr int kWaves = 2 * WM;                 // WM wave rows x 2 wave columns
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBM = 64 * WM;                   // token rows per tile
+  static constexpr int kABytes = kBM * 128;
+  static constexpr int kStage = kABytes + kDBN * 128;
+  static constexpr int kCopies = (kBM + kDBN) / 8;      // 1 KB copies (8 rows) per stage
+  static constexpr int kPer = kCopies / kWaves;         // per wave
+  static constexpr int kNBuf = kDLds / kStage < 4 ? kDLds / kStage : 4;
+  static constexpr int kPD = kNBuf - 1;                 // stages in flight ahead of the computed one
+  static_assert(kCopies % kWaves == 0, "copies per wave");
+  static_assert(kNBuf >= 2 && (kPD - 1) * kPer <= 63, "ring");
+};
+
+template <int N>
+STRATA_DEVICE void dense_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Waits until at most min(p, PMAX) later stages' copies (PER each) are outstanding.
+template <int PER, int PMAX>
+STRATA_DEVICE void dense_wait_pending(int p) {
+  if constexpr (PMAX <= 0) {
+    dense_wait_vmcnt<0>();
+  } else {
+    if (p >= PMAX) dense_wait_vmcnt<PMAX * PER>();
+    else dense_wait_pending<PER, PMAX - 1>(p);
+  }
+}
+
+// LDS tile layout: row r (128 bytes = 8 pieces of 8 bf16) keeps piece c in slot c ^ ((r >> 1) & 7),
+// so the 16 lanes that one LDS cycle serves (16 consecutive rows, one piece each) hit 64 distinct
+// banks.  A 1 KB copy instruction fills 8 rows; lane i lands in row i / 8, slot i % 8.
+STRATA_DEVICE int dense_piece(int row, int slot) { return slot ^ ((row >> 1) & 7); }
+
+struct DenseArgs {
+  const uint16_t* a;     // [M][K]
+  const uint16_t* b0;    // [N][K] (SwiGLU: gate [I][K])
+  const uint16_t* b1;    // SwiGLU: up [I][K]; otherwise unused
+  void* out;
+  int M, N, K;           // N: output columns (SwiGLU: I)
+  int accumulate;
+};
+
+// Copies stage ks (this wave's kPer pieces of 1 KB) into its ring buffer.
+template <int WM>
+STRATA_DEVICE void dense_issue(uint8_t* lds, const uint16_t* const* src, int ks) {
+  using C = DenseCfg<WM>;
+  const int wave = threadIdx.x >> 6;
+  uint8_t* st = lds + (ks % C::kNBuf) * C::kStage;
+#pragma unroll
+  for (int i = 0; i < C::kPer; ++i) {
+    const int q = wave + C::kWaves * i;
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)ks * kDK, st + q * 1024, 16, 0, 0);
+  }
+}
+
+template <int WM, int EPI>
+__global__ __launch_bounds__(DenseCfg<WM>::kThreads) void dense_gemm_kernel(DenseArgs p) {
+  using C = DenseCfg<WM>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nN = EPI == kEpiSwiglu ? (p.N + 63) / 64 : (p.N + kDBN - 1) / kDBN;
+  const int nM = (p.M + C::kBM - 1) / C::kBM;
+  const int nT = nM * nN;
+  // consecutive tiles (same token rows, neighbouring columns) go to the same XCD
+  int t = blockIdx.x;
+  if ((nT & 7) == 0) t = (t & 7) * (nT >> 3) + (t >> 3);
+  const int tm = t / nN, tn = t - tm * nN;
+  const int m0 = tm * C::kBM;
+
+  // this lane's source row of each of its copies
+  const uint16_t* src[C::kPer];
+#pragma unroll
+  for (int i = 0; i < C::kPer; ++i) {
+    const int q = wave + C::kWaves * i;            // copy index: A rows first, then weight rows
+    const int r = 8 * q + (lane >> 3);             // tile row (A rows 0..BM-1, then B rows)
+    const int piece = dense_piece(r, lane & 7);
+    const uint16_t* row;
+    if (r < C::kBM) {
+      const int m = min(m0 + r, p.M - 1);
+      row = p.a + (size_t)m * p.K;
+    } else {
+      const int rb = r - C::kBM;
+      if constexpr (EPI == kEpiSwiglu) {
+        const int o = min(tn * 64 + (rb >> 6) * 32 + (rb & 31), p.N - 1);
+        row = ((rb >> 5) & 1 ? p.b1 : p.b0) + (size_t)o * p.K;
+      } else {
+        const int n = min(tn * kDBN + rb, p.N - 1);
+        row = p.b0 + (size_t)n * p.K;
+      }
+    }
+    src[i] = row + piece * 8;
+  }
+
+  const int nk = p.K / kDK;
+#pragma unroll
+  for (int s = 0; s < C::kPD; ++s)
+    if (s < nk) dense_issue<WM>(lds, src, s);
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m = lane & 31, hh = lane >> 5;
+  const int key = (m >> 1) & 7;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
+
+  for (int ks = 0; ks < nk; ++ks) {
+    dense_wait_pending<C::kPer, C::kPD - 1>(nk - 1 - ks);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read of this stage moves above the barrier
+    if (ks + C::kPD < nk) dense_issue<WM>(lds, src, ks + C::kPD);
+    const uint8_t* st = lds + (ks % C::kNBuf) * C::kStage;
+    const uint8_t* at = st + (wm * 64 + m) * 128;
+    const uint8_t* bt = st + C::kABytes + (wn * 64 + m) * 128;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int slot = ((hh << 2) + s) ^ key;
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) a[f] = *reinterpret_cast<const bf16x8_t*>(at + f * 32 * 128 + slot * 16);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) b[g] = *reinterpret_cast<const bf16x8_t*>(bt + g * 32 * 128 + slot * 16);
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], b[g], acc[f][g], 0, 0, 0);
+    }
+  }
+
+  // Epilogue from registers: register r of a 32x32 tile holds row 8 (r / 4) + 4 hh + r % 4 and
+  // column lane % 32.
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 64 + f * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (row >= p.M) continue;
+      if constexpr (EPI == kEpiSwiglu) {
+        const int o = tn * 64 + wn * 32 + m;
+        if (o < p.N) {
+          uint16_t* out = static_cast<uint16_t*>(p.out);
+          out[(size_t)row * p.N + o] = f32_to_bf16(silu_mul_f(acc[f][0][r], acc[f][1][r]));
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int n = tn * kDBN + wn * 64 + g * 32 + m;
+          if (n >= p.N) continue;
+          float* out = static_cast<float*>(p.out) + (size_t)row * p.N + n;
+          if (EPI == kEpiAccum && p.accumulate) *out += acc[f][g][r];
+          else *out = acc[f][g][r];
+        }
+      }
+    }
+  }
+}
+
+template <int WM, int EPI>
+hipError_t launch_gemm(const DenseArgs& p, hipStream_t s) {
+  using C = DenseCfg<WM>;
+  const int nN = EPI == kEpiSwiglu ? (p.N + 63) / 64 : (p.N + kDBN - 1) / kDBN;
+  const int nM = (p.M + C::kBM - 1) / C::kBM;
+  const int lds = C::kNBuf * C::kStage;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dense_gemm_kernel<WM, EPI>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              DenseCfg<WM>::kNBuf * DenseCfg<WM>::kStage);
+  });
+  hipLaunchKernelGGL((dense_gemm_kernel<WM, EPI>), dim3(nM * nN), dim3(C::kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+// Tiles of 256 rows when they still give at least one tile per CU, else 128.
+template <int EPI>
+hipError_t gemm(const DenseArgs& p, hipStream_t s) {
+  const int nN = EPI == kEpiSwiglu ? (p.N + 63) / 64 : (p.N + kDBN - 1) / kDBN;
+  if ((int64_t)((p.M + 255) / 256) * nN >= 256) return launch_gemm<4, EPI>(p, s);
+  return launch_gemm<2, EPI>(p, s);
+}
+
+// ---------------------------------------------------------------------------------------------
+// GEMV for M <= 8 token rows.  Workgroup of 256 threads = 8 weight rows x 32 lanes; lane c of a
+// row multiplies 16-byte pieces c, c + 32, ... of the row with the same pieces of every token
+// row (staged in LDS), then the row's 32 lanes sum their partial dot products.
+
+constexpr int kGemvRows = 8;
+constexpr int kGemvMaxRows = 8;       // token rows the GEMV takes
+constexpr int kGemvMaxLds = 64 * 1024;  // M * K * 2 bytes of staged token rows
+constexpr int kGemvBatch = 8;           // pieces loaded before they are used
+
+STRATA_DEVICE float dot2_bf16(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
+
+STRATA_DEVICE float dot8_bf16(const u32x4_t& w, const u32x4_t& x, float acc) {
+  acc = dot2_bf16(w.x, x.x, acc);
+  acc = dot2_bf16(w.y, x.y, acc);
+  acc = dot2_bf16(w.z, x.z, acc);
+  return dot2_bf16(w.w, x.w, acc);
+}
+
+template <int TT, int EPI>
+__global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int nk8 = p.K >> 3;  // 16-byte pieces per row
+  // stage the token rows [TT][K]
+  {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.a);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds);
+    for (int i = tid; i < TT * nk8; i += 256) dst[i] = src[i];
+  }
+  const int r = tid >> 5, c = tid & 31;
+  const uint16_t* row;
+  int col;  // output column of this row (SwiGLU: output index, gate rows 0-3, up rows 4-7)
+  if constexpr (EPI == kEpiSwiglu) {
+    col = blockIdx.x * 4 + (r & 3);
+    row = ((r >> 2) ? p.b1 : p.b0) + (size_t)min(col, p.N - 1) * p.K;
+  } else {
+    col = blockIdx.x * kGemvRows + r;
+    row = p.b0 + (size_t)min(col, p.N - 1) * p.K;
+  }
+  __syncthreads();
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+  const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(row);
+  const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(lds);
+  for (int j0 = c; j0 < nk8; j0 += 32 * kGemvBatch) {
+    u32x4_t w[kGemvBatch];
+#pragma unroll
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int j = j0 + 32 * b;
+      if (j < nk8) w[b] = __builtin_nontemporal_load(wrow + j);
+    }
+#pragma unroll
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int j = j0 + 32 * b;
+      if (j < nk8) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[t] = dot8_bf16(w[b], xs[t * nk8 + j], acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 32);
+  }
+  if constexpr (EPI == kEpiSwiglu) {
+    __syncthreads();  // the staged rows are no longer read: reuse LDS for the row sums
+    float* sums = reinterpret_cast<float*>(lds);
+    if (c == 0) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) sums[r * TT + t] = acc[t];
+    }
+    __syncthreads();
+    if (tid < 4 * TT) {
+      const int o = tid / TT, t = tid - o * TT;
+      const int n = blockIdx.x * 4 + o;
+      if (n < p.N) {
+        const float g = sums[o * TT + t], u = sums[(4 + o) * TT + t];
+        static_cast<uint16_t*>(p.out)[(size_t)t * p.N + n] = f32_to_bf16(silu_mul_f(g, u));
+      }
+    }
+  } else {
+    if (c < TT && col < p.N) {
+      float v = acc[0];
+#pragma unroll
+      for (int t = 1; t < TT; ++t)
+        if (c == t) v = acc[t];
+      float* out = static_cast<float*>(p.out) + (size_t)c * p.N + col;
+      if (EPI == kEpiAccum && p.accumulate) *out += v;
+      else *out = v;
+    }
+  }
+}
+
+template <int TT, int EPI>
+hipError_t launch_gemv_t(const DenseArgs& p, hipStream_t s) {
+  const int rows_per_wg = EPI == kEpiSwiglu ? 4 : kGemvRows;
+  const int grid = (p.N + rows_per_wg - 1) / rows_per_wg;
+  const int lds = TT * p.K * 2 > 256 ? TT * p.K * 2 : 256;
+  hipLaunchKernelGGL((dense_gemv_kernel<TT, EPI>), dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t gemv(const DenseArgs& p, hipStream_t s) {
+  switch (p.M) {
+    case 1: return launch_gemv_t<1, EPI>(p, s);
+    case 2: return launch_gemv_t<2, EPI>(p, s);
+    case 3: return launch_gemv_t<3, EPI>(p, s);
+    case 4: return launch_gemv_t<4, EPI>(p, s);
+    case 5: return launch_gemv_t<5, EPI>(p, s);
+    case 6: return launch_gemv_t<6, EPI>(p, s);
+    case 7: return launch_gemv_t<7, EPI>(p, s);
+    default: return launch_gemv_t<8, EPI>(p, s);
+  }
+}
+
+template <int EPI>
+hipError_t dense(const DenseArgs& p, hipStream_t s) {
+  if (p.M <= kGemvMaxRows && p.M * p.K * 2 <= kGemvMaxLds) return gemv<EPI>(p, s);
+  return gemm<EPI>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
+                                float* logits, hipStream_t s) {
+  DenseArgs p{x, wr, nullptr, logits, T, E, H, 0};
+  return dense<kEpiStore>(p, s);
+}
+
+hipError_t launch_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                                const uint16_t* wd, int T, int H, int I, float* y, int accumulate,
+                                uint16_t* a, hipStream_t s) {
+  DenseArgs up{x, wg, wu, a, T, I, H, 0};
+  hipError_t e = dense<kEpiSwiglu>(up, s);
+  if (e != hipSuccess) return e;
+  DenseArgs down{a, wd, nullptr, y, T, H, I, accumulate};
+  return dense<kEpiAccum>(down, s);
+}
+
+}  // namespace strata

@@ -56,6 +56,14 @@ hipError_t launch_combine(const uint16_t* expert_out, const float* w, int T, int
 
 hipError_t launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, hipStream_t s);
 
+// Dense bf16 layers.  Router: logits fp32 [T][E] = x W_r^T.  Shared expert: a = bf16(SiLU(x W_sg^T)
+// * (x W_su^T)) into a [T][I], then y (+)= a W_sd^T.  H and I multiples of 64.
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
+                                float* logits, hipStream_t s);
+hipError_t launch_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                                const uint16_t* wd, int T, int H, int I, float* y, int accumulate,
+                                uint16_t* a, hipStream_t s);
+
 // Decode path (T <= 8).
 hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T, int E, int k,
                          int H, int I, const void* gate_codes, const void* up_codes,

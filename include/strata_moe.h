@@ -226,9 +226,46 @@ strata_status strata_moe_pack_matrix(int32_t fmt, int32_t n_mat, int32_t rows, i
 strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
                                  hipStream_t stream);
 
+/*
+ * Router projection: logits[t][e] = sum_h x[t][h] * w_router[e][h], fp32.  The pages keep the
+ * routers on the GPU with the experts ("Strata - the details", How it works / memory tiers;
+ * "Strata vs Llama.cpp vs vLLM", transcript at 09:28) but give no formula; a dense linear map of
+ * the normalised hidden state to one logit per expert is this library's definition.  The
+ * logits feed strata_moe_route / strata_moe_layer.
+ *   x        bf16 [T][H] (read), the layer input after RMSNorm
+ *   w_router bf16 [E][H] (read), row-major
+ *   logits   fp32 [T][E] (written)
+ * Precision: bf16 products are exact in fp32; sums are accumulated in fp32 (matrix cores for
+ * T > 8, dot-product instructions for T <= 8), so |logits - exact| <= H * 2^-24 / (1 - H * 2^-24)
+ * * sum_h |x[t][h] w_router[e][h]|.
+ * Limits: H a multiple of 64 (STRATA_ERR_UNSUPPORTED otherwise); E >= 1.
+ */
+strata_status strata_moe_router_logits(const uint16_t* x, const uint16_t* w_router, int32_t T,
+                                       int32_t H, int32_t E, float* logits, hipStream_t stream);
+
+/*
+ * Shared expert, a dense SwiGLU FFN applied to every token: a = bf16_RNE(SiLU(x W_sg^T) *
+ * (x W_su^T)), out = a W_sd^T, y = out (or y += out with accumulate != 0).  The pages list shared
+ * experts among what stays on the GPU ("Strata - the details", How it works / memory tiers;
+ * "Strata vs Llama.cpp vs vLLM", transcript at 09:28); its form, the routed experts' SwiGLU with
+ * dense weights and no router scale, is this library's definition.
+ *   x          bf16 [T][H] (read)
+ *   w_gate     bf16 [I][H], w_up bf16 [I][H], w_down bf16 [H][I] (read), row-major
+ *   y          fp32 [T][H] (written or accumulated)
+ * Workspace: at least strata_moe_shared_workspace_bytes(T, I) (holds a).
+ * Precision: fp32 accumulation of exact bf16 products; a rounded to bf16 once.
+ * Limits: H and I multiples of 64 (STRATA_ERR_UNSUPPORTED otherwise).
+ */
+strata_status strata_moe_shared_expert(const uint16_t* x, const uint16_t* w_gate,
+                                       const uint16_t* w_up, const uint16_t* w_down, int32_t T,
+                                       int32_t H, int32_t I, float* y, int32_t accumulate,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* Workspace sizes in bytes (host functions; 0 for invalid shapes). */
 size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k);
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
+size_t strata_moe_shared_workspace_bytes(int32_t T, int32_t I);
 
 /* Static string for a status code (host function; never NULL). */
 const char* strata_status_string(strata_status status);

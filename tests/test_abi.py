@@ -113,6 +113,26 @@ def test_pack_matrix_validation(L):
     assert L.strata_moe_pack_matrix(3, 1, 64, 64, A, A + 4096, A + 1024, B + 4096, None) == INVAL
 
 
+def test_router_and_shared_validation(L):
+    assert L.strata_moe_router_logits(A, A, -1, 3072, 512, A, None) == INVAL
+    assert L.strata_moe_router_logits(A, A, 4, 3072, 0, A, None) == INVAL
+    assert L.strata_moe_router_logits(A, A, 4, 3000, 512, A, None) == UNSUP    # H % 64
+    assert L.strata_moe_router_logits(MIS, A, 4, 3072, 512, A, None) == INVAL
+    assert L.strata_moe_router_logits(A, None, 4, 3072, 512, A, None) == INVAL
+    assert L.strata_moe_router_logits(None, None, 0, 3072, 512, None, None) == OK  # T = 0
+    ws = L.strata_moe_shared_workspace_bytes(8192, 768)
+    assert ws >= 8192 * 768 * 2 and L.strata_moe_shared_workspace_bytes(-1, 768) == 0
+    call = lambda T=8192, H=3072, I=768, y=A, wsb=ws, x=A: L.strata_moe_shared_expert(
+        x, A, A, A, T, H, I, y, 0, A, wsb, None)
+    assert call(H=3000) == UNSUP
+    assert call(I=800) == UNSUP
+    assert call(I=0) == INVAL
+    assert call(y=None) == INVAL
+    assert call(x=MIS) == INVAL
+    assert call(wsb=ws - 1) == WS
+    assert call(T=0, y=None, x=None) == OK
+
+
 def test_workspace_sizes(L):
     assert L.strata_moe_workspace_bytes(-1, 512, 10, 3072, 768) == 0
     small = L.strata_moe_workspace_bytes(16, 64, 4, 256, 128)

@@ -1,0 +1,153 @@
+"""GPU parity of the dense layers beside the routed experts (router projection, shared expert)
+against the CPU oracle, through the C ABI.
+
+Bars:
+ * router logits: every element within the fp32 summation bound
+   |l - l_exact| <= gamma_H * sum_h |x_h w_h|, gamma_H = H u / (1 - H u), u = 2^-24 (the bf16
+   products are exact in fp32, so only the H - 1 additions round);
+ * shared expert: per-row relative L2 <= 5e-3 against the fp64 oracle (the GPU rounds the SwiGLU
+   intermediate to bf16, about 2^-9 relative per element);
+ * the composed block (router -> routed layer -> + shared expert) against the oracle fed the
+   GPU's own fp32 logits, so that the routing decision is taken on the same numbers.
+Shapes cover the GEMV path (T <= 8), both GEMM tile heights, ragged rows and columns, and the
+full-size decode and prefill shapes on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_expert_ffn_fp32_amd as sm
+import moe_inputs as mi
+import oracle
+from gpu_helpers import TOL_REL_L2, Layer, dev, rel_l2_rows, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def shape(T, H, E=64, I=128, k=4):
+    return mi.Shape("d", T=T, H=H, E=E, k=k, I=I)
+
+
+def f64(bits):
+    return mi.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def router_bound(x, wr, H):
+    g = H * U32 / (1 - H * U32)
+    return g * (np.abs(f64(x)) @ np.abs(f64(wr)).T)
+
+
+def gpu_router(x_np, wr_np):
+    T, E = x_np.shape[0], wr_np.shape[0]
+    logits = torch.full((T, E), float("nan"), dtype=torch.float32, device=dev())
+    sm.strata_moe_router_logits(to_dev_bf16(x_np), to_dev_bf16(wr_np), logits)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,E", [(1, 256, 64), (4, 3072, 512), (8, 256, 100), (9, 256, 100),
+                                   (16, 256, 64), (300, 512, 200), (700, 192, 384)])
+def test_router_logits(T, H, E):
+    log(f"router T={T} H={H} E={E}")
+    s = shape(T, H, E=E)
+    x = mi.make_x(s, seed=T)
+    wr = mi.make_router(s, seed=T)
+    got = gpu_router(x, wr)
+    ref = oracle.router_logits(x, wr)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= router_bound(x, wr, H))
+
+
+def test_router_logits_full_size_sampled_rows():
+    s = mi.PREFILL
+    log(f"router full size T={s.T}")
+    x = mi.make_x(s)
+    wr = mi.make_router(s)
+    got = gpu_router(x, wr)
+    rows = np.array([0, 1, 255, 256, 4095, 4096, 8000, s.T - 1])
+    ref = oracle.router_logits(x[rows], wr)
+    assert np.all(np.abs(got[rows] - ref) <= router_bound(x[rows], wr, s.H))
+    assert np.all(np.isfinite(got))
+    # unit-variance inputs and N(0, 1/H) weights: logits of about unit spread
+    assert 0.8 < got.std() < 1.2
+
+
+def gpu_shared(x_np, sh, y0=None):
+    T, H = x_np.shape
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev()) if y0 is None \
+        else to_dev(y0.astype(np.float32))
+    ws = sm.alloc_workspace(sm.shared_workspace_bytes(T, sh["I"]), dev())
+    sm.strata_moe_shared_expert(to_dev_bf16(x_np), to_dev_bf16(sh["gate"]), to_dev_bf16(sh["up"]),
+                                to_dev_bf16(sh["down"]), y, ws, accumulate=y0 is not None)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,I", [(1, 256, 64), (4, 3072, 768), (8, 256, 128), (9, 256, 128),
+                                   (16, 256, 128), (300, 512, 192), (600, 192, 320)])
+def test_shared_expert(T, H, I):
+    log(f"shared T={T} H={H} I={I}")
+    s = shape(T, H, I=I)
+    x = mi.make_x(s, seed=T + 1)
+    sh = mi.make_shared(s, seed=T + 1)
+    got = gpu_shared(x, sh)
+    ref = oracle.shared_expert(x, sh["gate"], sh["up"], sh["down"])
+    assert np.all(np.isfinite(got))
+    assert rel_l2_rows(got, ref).max() <= TOL_REL_L2
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_shared_expert_accumulates(T):
+    log(f"shared accumulate T={T}")
+    s = shape(T, 256, I=128)
+    x = mi.make_x(s, seed=5)
+    sh = mi.make_shared(s, seed=5)
+    y0 = mi.normal_f32(5, 999, T * 256).reshape(T, 256)
+    got = gpu_shared(x, sh, y0)
+    ref = y0.astype(np.float64) + oracle.shared_expert(x, sh["gate"], sh["up"], sh["down"])
+    assert rel_l2_rows(got, ref).max() <= TOL_REL_L2
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_shared_expert_full_size_sampled_rows(name):
+    s = {"decode": mi.DECODE, "prefill": mi.PREFILL}[name]
+    log(f"shared full size {name} T={s.T}")
+    x = mi.make_x(s)
+    sh = mi.make_shared(s)
+    got = gpu_shared(x, sh)
+    rows = np.arange(s.T) if s.T <= 8 else np.array([0, 255, 256, 511, 4096, s.T - 2, s.T - 1])
+    ref = oracle.shared_expert(x[rows], sh["gate"], sh["up"], sh["down"])
+    assert np.all(np.isfinite(got))
+    assert rel_l2_rows(got[rows], ref).max() <= TOL_REL_L2
+
+
+@pytest.mark.parametrize("T", [4, 16, 9])
+def test_moe_block_router_layer_shared(T):
+    """Router -> routed layer -> + shared expert, all on the GPU, against the oracle fed the
+    GPU's logits (the routing decision is compared bit-exactly on the same fp32 numbers)."""
+    log(f"block T={T}")
+    s = shape(T, 256, E=64, I=128, k=4)
+    L = Layer(s, seed=11, T=T)
+    wr = mi.make_router(s, seed=11)
+    sh = mi.make_shared(s, seed=11)
+    logits = torch.empty((T, s.E), dtype=torch.float32, device=dev())
+    sm.strata_moe_router_logits(L.x, to_dev_bf16(wr), logits)
+    y = torch.empty((T, s.H), dtype=torch.float32, device=dev())
+    ids = torch.empty((T, s.k), dtype=torch.int32, device=dev())
+    sm.strata_moe_layer(L.w, L.x, logits, s.k, y, topk_ids=ids, workspace=L.workspace())
+    ws = sm.alloc_workspace(sm.shared_workspace_bytes(T, s.I), dev())
+    sm.strata_moe_shared_expert(L.x, to_dev_bf16(sh["gate"]), to_dev_bf16(sh["up"]),
+                                to_dev_bf16(sh["down"]), y, ws, accumulate=True)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.all(np.abs(lg - oracle.router_logits(L.x_np, wr)) <= router_bound(L.x_np, wr, s.H))
+    ref_y, ref_ids, *_ = oracle.layer(L.w_np, L.x_np, lg, s.k, intermediates=True)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = ref_y + oracle.shared_expert(L.x_np, sh["gate"], sh["up"], sh["down"])
+    assert rel_l2_rows(y.cpu().numpy(), ref).max() <= TOL_REL_L2
