@@ -9,7 +9,9 @@ experts, the steps cycle over 16 resident layers (each with its own weights, act
 logits): a layer's experts are re-read only after ~1.4 GB of other layers' traffic.
 
 Secondary (same JSON line, key "prefill"): one prefill chunk of one layer, T = 8192, same
-dimensions; a step is one whole-layer call.
+dimensions; a step is one whole-layer call.  Keys "block_decode" and "prefill.block": the dense
+layers on either side of the routed experts (router projection x W_r^T, shared SwiGLU expert),
+alone and as the whole block router -> routed layer -> + shared expert.
 
 value = whole-job layer-tokens/s = T * steps / timed seconds, inputs resident in HBM.
 roofline: HBM-bound decode (touched experts' packed bytes per layer call / call duration, peak
@@ -178,6 +180,121 @@ def bench_decode(args, stream):
     }
 
 
+def bench_block_decode(args, stream, layers):
+    """The dense layers around the routed experts at T = 4: router projection (logits = x W_r^T,
+    bf16 [E][H]) and the shared SwiGLU expert (bf16 W_sg, W_su [I][H], W_sd [H][I]), each layer
+    with its own seeded weights so the 16 resident layers (~270 MB of dense weights) are not
+    served from the Infinity Cache.  Graph replays of one pass over the layers: router alone,
+    shared expert alone, and the whole block (router -> routed layer -> + shared expert)."""
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import to_dev_bf16
+
+    s = mi.DECODE
+    n = len(layers)
+    wr = [to_dev_bf16(mi.make_router(s, args.seed, l)) for l in range(n)]
+    sh = []
+    for l in range(n):
+        d = mi.make_shared(s, args.seed, l)
+        sh.append((to_dev_bf16(d["gate"]), to_dev_bf16(d["up"]), to_dev_bf16(d["down"])))
+    logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    y = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    ws = layers[0].workspace()
+    sws = sm.alloc_workspace(sm.shared_workspace_bytes(s.T, s.I), "cuda")
+
+    def router(i, strm):
+        sm.strata_moe_router_logits(layers[i].x, wr[i], logits, stream=strm)
+
+    def shared(i, strm):
+        sm.strata_moe_shared_expert(layers[i].x, *sh[i], y, sws, accumulate=True, stream=strm)
+
+    def block(i, strm):
+        router(i, strm)
+        sm.strata_moe_layer(layers[i].w, layers[i].x, logits, s.k, y, workspace=ws, stream=strm)
+        shared(i, strm)
+
+    def graph_ms(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(n):
+                fn(i, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for i in range(n):
+                fn(i, cap)
+        g.replay()
+        reps = max(1, args.steps // n)
+        return event_time_ms(lambda r: g.replay(), reps, stream) / (reps * n)
+
+    ms_r, ms_s, ms_b = graph_ms(router), graph_ms(shared), graph_ms(block)
+    r_bytes = s.E * s.H * 2 + s.T * s.H * 2
+    s_bytes = 3 * s.H * s.I * 2
+    out = {
+        "T": s.T, "layers_cycled": n,
+        "router_us": ms_r * 1e3, "router_GBs": r_bytes / (ms_r * 1e-3) / 1e9,
+        "shared_us": ms_s * 1e3, "shared_GBs": s_bytes / (ms_s * 1e-3) / 1e9,
+        "block_us": ms_b * 1e3, "block_tokens_per_s": s.T / (ms_b * 1e-3),
+        "unit_of_work": "router: E*H*2 + T*H*2 bytes; shared: 3*H*I*2 bytes of bf16 weights",
+    }
+    log(f"block decode: router {out['router_us']:.2f} us ({out['router_GBs']:.0f} GB/s), shared "
+        f"{out['shared_us']:.2f} us ({out['shared_GBs']:.0f} GB/s), router+layer+shared "
+        f"{out['block_us']:.2f} us")
+    return out
+
+
+def block_prefill(args, stream, L, ws, y):
+    """Router projection and shared expert at T = 8192 (matrix-core GEMMs), and the whole block."""
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import to_dev_bf16
+
+    s = L.shape
+    wr = to_dev_bf16(mi.make_router(s, args.seed))
+    d = mi.make_shared(s, args.seed)
+    sh = (to_dev_bf16(d["gate"]), to_dev_bf16(d["up"]), to_dev_bf16(d["down"]))
+    logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    sws = sm.alloc_workspace(sm.shared_workspace_bytes(s.T, s.I), "cuda")
+
+    def router(i):
+        sm.strata_moe_router_logits(L.x, wr, logits, stream=stream)
+
+    def shared(i):
+        sm.strata_moe_shared_expert(L.x, *sh, y, sws, accumulate=True, stream=stream)
+
+    def block(i):
+        router(i)
+        sm.strata_moe_layer(L.w, L.x, logits, s.k, y, workspace=ws, stream=stream)
+        shared(i)
+
+    steps = max(3, args.prefill_steps)
+    res = {}
+    for name, fn in (("router", router), ("shared", shared), ("block", block)):
+        fn(0)
+        res[name] = event_time_ms(fn, steps, stream) / steps
+    f_r = 2.0 * s.T * s.H * s.E
+    f_s = 6.0 * s.T * s.H * s.I
+    out = {
+        "T": s.T,
+        "router_us": res["router"] * 1e3, "router_TFLOPs": f_r / (res["router"] * 1e-3) / 1e12,
+        "shared_us": res["shared"] * 1e3, "shared_TFLOPs": f_s / (res["shared"] * 1e-3) / 1e12,
+        "block_ms": res["block"], "block_tokens_per_s": s.T / (res["block"] * 1e-3),
+        "peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
+        "unit_of_work": "router: 2*T*H*E FLOP; shared: 6*T*H*I FLOP (bf16 MFMA, fp32 accumulate)",
+    }
+    log(f"block prefill: router {out['router_us']:.1f} us ({out['router_TFLOPs']:.0f} TFLOP/s), "
+        f"shared {out['shared_us']:.1f} us ({out['shared_TFLOPs']:.0f} TFLOP/s), block "
+        f"{out['block_ms']:.3f} ms")
+    return out
+
+
 def bench_prefill(args, stream, name):
     import torch
 
@@ -224,7 +341,8 @@ def bench_prefill(args, stream, name):
     tflops_ffn = flops / (ms_ffn * 1e-3) / 1e12
     tflops_layer = flops / (ms_per_step * 1e-3) / 1e12
     traffic = measured_traffic("prefill_t8192_traffic.txt", "prefill.hip") if name == "prefill" else None
-    return {
+    block = block_prefill(args, stream, L, ws, y) if name == "prefill" and not args.no_block else None
+    res = {
         "workload": f"{s.name} T={s.T} H={s.H} E={s.E} k={s.k} I={s.I} "
                     f"{'Q3' if s.fmt == 3 else 'Q2'}-block experts"
                     + (", Zipf(1.1)-skewed routing" if s.zipf else ""),
@@ -242,6 +360,9 @@ def bench_prefill(args, stream, name):
                      "ms_per_call": ms_ffn, "unit_of_work": "6*T*k*H*I FLOP per call"},
         "dtype": "f16 MFMA, fp32 accumulate",
     }
+    if block is not None:
+        res["block"] = block
+    return res
 
 
 def bench_stack(args, stream):
@@ -322,6 +443,8 @@ def main():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-block", action="store_true",
+                   help="skip the router projection / shared expert measurements")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run a plain copy of this many MiB (for scaling memory counters)")
     args = p.parse_args()
@@ -344,6 +467,8 @@ def main():
         f"{dec['eager_ms_per_step'] * 1e3:.2f} us), {dec['value']:.4g} layer-tokens/s, "
         f"{dec['roofline']['achieved']:.0f} GB/s ({dec['roofline']['frac'] * 100:.1f}% of HBM peak)")
     layers = dec.pop("layers")
+    blk = None if args.no_block else bench_block_decode(args, stream, layers)
+    torch.cuda.empty_cache()
     pre = skw = None
     if not args.no_prefill:
         for L in layers:
@@ -406,6 +531,8 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
     }
+    if blk is not None:
+        line["block_decode"] = blk
     if pre is not None:
         line["prefill"] = pre
     if skw is not None:

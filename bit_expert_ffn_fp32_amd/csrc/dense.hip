@@ -55,6 +55,8 @@ struct DenseCfg {
   static constexpr int kPD = kNBuf - 1;                 // stages in flight ahead of the computed one
   static_assert(kCopies % kWaves == 0, "copies per wave");
   static_assert(kNBuf >= 2 && (kPD - 1) * kPer <= 63, "ring");
+  static_assert(kBM * 136 * 4 <= kNBuf * kStage, "fp32 output tile staged in the ring");
+  static_assert(kBM * 32 % kThreads == 0 && kBM * 8 % kThreads == 0, "epilogue chunks");
 };
 
 template <int N>
@@ -179,29 +181,74 @@ __global__ __launch_bounds__(DenseCfg<WM>::kThreads) void dense_gemm_kernel(Dens
     }
   }
 
-  // Epilogue from registers: register r of a 32x32 tile holds row 8 (r / 4) + 4 hh + r % 4 and
-  // column lane % 32.
+  // Epilogue through LDS, so that every global access is 16 bytes per lane along a row.  Register
+  // r of a 32x32 accumulator tile holds row 8 (r / 4) + 4 hh + r % 4 and column lane % 32.
+  // Staged rows are padded (fp32: 136 floats, bf16: 72) so that the two row groups a write
+  // instruction touches (rows R and R + 4) fall in different banks.
+  const int kChunks = C::kBM * 32 / C::kThreads;  // 16-byte fp32 chunks per thread
+  float* out = static_cast<float*>(p.out);
+  const bool vec = (p.N & 3) == 0;
+  u32x4_t yv[C::kBM * 32 / C::kThreads];
+  if constexpr (EPI == kEpiAccum) {
+    // start reading the accumulated outputs while the tile is staged
+    if (p.accumulate && vec) {
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+      for (int j = 0; j < kChunks; ++j) {
+        const int i = threadIdx.x + j * C::kThreads, R = i >> 5, n = tn * kDBN + (i & 31) * 4;
+        const int row = min(m0 + R, p.M - 1);
+        if (n < p.N) yv[j] = *reinterpret_cast<const u32x4_t*>(out + (size_t)row * p.N + n);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done reading the ring
+  if constexpr (EPI == kEpiSwiglu) {
+    constexpr int kS = 72;
+    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 64 + f * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (row >= p.M) continue;
-      if constexpr (EPI == kEpiSwiglu) {
-        const int o = tn * 64 + wn * 32 + m;
-        if (o < p.N) {
-          uint16_t* out = static_cast<uint16_t*>(p.out);
-          out[(size_t)row * p.N + o] = f32_to_bf16(silu_mul_f(acc[f][0][r], acc[f][1][r]));
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int R = wm * 64 + f * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        st[R * kS + wn * 32 + m] = f32_to_bf16(silu_mul_f(acc[f][0][r], acc[f][1][r]));
+      }
+    __syncthreads();
+    uint16_t* a_out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int j = 0; j < C::kBM * 8 / C::kThreads; ++j) {
+      const int i = threadIdx.x + j * C::kThreads, R = i >> 3, c = i & 7;
+      const int row = m0 + R, o = tn * 64 + c * 8;
+      if (row < p.M && o < p.N)  // N is a multiple of 8: a chunk is all in or all out
+        *reinterpret_cast<u32x4_t*>(a_out + (size_t)row * p.N + o) =
+            *reinterpret_cast<const u32x4_t*>(st + R * kS + c * 8);
+    }
+  } else {
+    constexpr int kS = 136;
+    float* st = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int R = wm * 64 + f * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          st[R * kS + wn * 64 + g * 32 + m] = acc[f][g][r];
         }
+    __syncthreads();
+    const bool add = EPI == kEpiAccum && p.accumulate;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int i = threadIdx.x + j * C::kThreads, R = i >> 5, c = i & 31;
+      const int row = m0 + R, n = tn * kDBN + c * 4;
+      if (row >= p.M || n >= p.N) continue;
+      f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + R * kS + c * 4);
+      float* dst = out + (size_t)row * p.N + n;
+      if (vec) {
+        if (add) v += __builtin_bit_cast(f32x4_t, yv[j]);
+        *reinterpret_cast<f32x4_t*>(dst) = v;
       } else {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int n = tn * kDBN + wn * 64 + g * 32 + m;
-          if (n >= p.N) continue;
-          float* out = static_cast<float*>(p.out) + (size_t)row * p.N + n;
-          if (EPI == kEpiAccum && p.accumulate) *out += acc[f][g][r];
-          else *out = acc[f][g][r];
-        }
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) dst[e] = add ? dst[e] + v[e] : v[e];
       }
     }
   }
@@ -232,14 +279,16 @@ hipError_t gemm(const DenseArgs& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// GEMV for M <= 8 token rows.  Workgroup of 256 threads = 8 weight rows x 32 lanes; lane c of a
-// row multiplies 16-byte pieces c, c + 32, ... of the row with the same pieces of every token
-// row (staged in LDS), then the row's 32 lanes sum their partial dot products.
+// GEMV for M <= 8 token rows.  A workgroup of 256 threads covers 256 / LPR weight rows with LPR
+// lanes each; lane c of a row multiplies 16-byte pieces c, c + LPR, ... of the row with the same
+// pieces of every token row.  The first 16 pieces of the lane's row are requested before the
+// token rows are staged in LDS, so the two latencies overlap.  The row's lanes then sum their
+// partial dot products (shuffles within a wave, LDS across the waves of a row).  LPR is chosen
+// per call so that the grid has about one workgroup per CU or more.
 
-constexpr int kGemvRows = 8;
-constexpr int kGemvMaxRows = 8;       // token rows the GEMV takes
+constexpr int kGemvMaxRows = 8;         // token rows the GEMV takes
 constexpr int kGemvMaxLds = 64 * 1024;  // M * K * 2 bytes of staged token rows
-constexpr int kGemvBatch = 8;           // pieces loaded before they are used
+constexpr int kGemvBatch = 16;          // pieces per lane requested ahead
 
 STRATA_DEVICE float dot2_bf16(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
@@ -253,109 +302,128 @@ STRATA_DEVICE float dot8_bf16(const u32x4_t& w, const u32x4_t& x, float acc) {
   return dot2_bf16(w.w, x.w, acc);
 }
 
-template <int TT, int EPI>
+// TT >= M token rows; LDS holds TT staged rows (rows M .. TT - 1 are unset, their sums are never
+// stored).
+template <int TT, int LPR, int EPI>
 __global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
+  constexpr int RW = 256 / LPR;                  // weight rows per workgroup
+  constexpr int WL = LPR < 64 ? LPR : 64;        // lanes of a row within one wave
+  constexpr int WPR = LPR / WL;                  // waves per row
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, r = tid / LPR, c = tid % LPR;
   const int nk8 = p.K >> 3;  // 16-byte pieces per row
-  // stage the token rows [TT][K]
+  const uint16_t* row;
+  if constexpr (EPI == kEpiSwiglu) {  // rows 0 .. RW/2-1: gate, RW/2 .. RW-1: up, same outputs
+    const int o = blockIdx.x * (RW / 2) + r % (RW / 2);
+    row = (r >= RW / 2 ? p.b1 : p.b0) + (size_t)min(o, p.N - 1) * p.K;
+  } else {
+    row = p.b0 + (size_t)min(blockIdx.x * RW + r, p.N - 1) * p.K;
+  }
+  const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(row);
+  u32x4_t w[kGemvBatch];
+#pragma unroll
+  for (int b = 0; b < kGemvBatch; ++b) {
+    const int j = c + LPR * b;
+    if (j < nk8) w[b] = __builtin_nontemporal_load(wrow + j);
+  }
   {
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.a);
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds);
-    for (int i = tid; i < TT * nk8; i += 256) dst[i] = src[i];
-  }
-  const int r = tid >> 5, c = tid & 31;
-  const uint16_t* row;
-  int col;  // output column of this row (SwiGLU: output index, gate rows 0-3, up rows 4-7)
-  if constexpr (EPI == kEpiSwiglu) {
-    col = blockIdx.x * 4 + (r & 3);
-    row = ((r >> 2) ? p.b1 : p.b0) + (size_t)min(col, p.N - 1) * p.K;
-  } else {
-    col = blockIdx.x * kGemvRows + r;
-    row = p.b0 + (size_t)min(col, p.N - 1) * p.K;
+    for (int i = tid; i < p.M * nk8; i += 256) dst[i] = src[i];
   }
   __syncthreads();
+  const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(lds);
   float acc[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
-  const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(row);
-  const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(lds);
-  for (int j0 = c; j0 < nk8; j0 += 32 * kGemvBatch) {
-    u32x4_t w[kGemvBatch];
+  for (int j0 = 0;; j0 += LPR * kGemvBatch) {
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
-      const int j = j0 + 32 * b;
-      if (j < nk8) w[b] = __builtin_nontemporal_load(wrow + j);
-    }
-#pragma unroll
-    for (int b = 0; b < kGemvBatch; ++b) {
-      const int j = j0 + 32 * b;
+      const int j = j0 + c + LPR * b;
       if (j < nk8) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[t] = dot8_bf16(w[b], xs[t * nk8 + j], acc[t]);
       }
     }
+    if (j0 + LPR * kGemvBatch >= nk8) break;
+#pragma unroll
+    for (int b = 0; b < kGemvBatch; ++b) {
+      const int j = j0 + LPR * kGemvBatch + c + LPR * b;
+      if (j < nk8) w[b] = __builtin_nontemporal_load(wrow + j);
+    }
   }
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 32);
+    for (int off = WL / 2; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, WL);
   }
-  if constexpr (EPI == kEpiSwiglu) {
-    __syncthreads();  // the staged rows are no longer read: reuse LDS for the row sums
-    float* sums = reinterpret_cast<float*>(lds);
-    if (c == 0) {
+  __syncthreads();  // the staged rows are no longer read: LDS now holds partial sums
+  float* part = reinterpret_cast<float*>(lds);  // [RW][WPR][TT]
+  if (c % WL == 0) {
 #pragma unroll
-      for (int t = 0; t < TT; ++t) sums[r * TT + t] = acc[t];
-    }
-    __syncthreads();
-    if (tid < 4 * TT) {
-      const int o = tid / TT, t = tid - o * TT;
-      const int n = blockIdx.x * 4 + o;
-      if (n < p.N) {
-        const float g = sums[o * TT + t], u = sums[(4 + o) * TT + t];
-        static_cast<uint16_t*>(p.out)[(size_t)t * p.N + n] = f32_to_bf16(silu_mul_f(g, u));
-      }
+    for (int t = 0; t < TT; ++t) part[(r * WPR + c / WL) * TT + t] = acc[t];
+  }
+  __syncthreads();
+  auto total = [&](int rr, int t) {
+    float v = part[rr * WPR * TT + t];
+#pragma unroll
+    for (int q = 1; q < WPR; ++q) v += part[(rr * WPR + q) * TT + t];
+    return v;
+  };
+  if constexpr (EPI == kEpiSwiglu) {
+    if (tid < (RW / 2) * TT) {
+      const int o = tid / TT, t = tid % TT;
+      const int n = blockIdx.x * (RW / 2) + o;
+      if (n < p.N && t < p.M)
+        static_cast<uint16_t*>(p.out)[(size_t)t * p.N + n] =
+            f32_to_bf16(silu_mul_f(total(o, t), total(o + RW / 2, t)));
     }
   } else {
-    if (c < TT && col < p.N) {
-      float v = acc[0];
-#pragma unroll
-      for (int t = 1; t < TT; ++t)
-        if (c == t) v = acc[t];
-      float* out = static_cast<float*>(p.out) + (size_t)c * p.N + col;
-      if (EPI == kEpiAccum && p.accumulate) *out += v;
-      else *out = v;
+    if (tid < RW * TT) {
+      const int rr = tid / TT, t = tid % TT;
+      const int n = blockIdx.x * RW + rr;
+      if (n < p.N && t < p.M) {
+        float* out = static_cast<float*>(p.out) + (size_t)t * p.N + n;
+        const float v = total(rr, t);
+        if (EPI == kEpiAccum && p.accumulate) *out += v;
+        else *out = v;
+      }
     }
   }
 }
 
-template <int TT, int EPI>
+template <int TT, int LPR, int EPI>
 hipError_t launch_gemv_t(const DenseArgs& p, hipStream_t s) {
-  const int rows_per_wg = EPI == kEpiSwiglu ? 4 : kGemvRows;
-  const int grid = (p.N + rows_per_wg - 1) / rows_per_wg;
+  constexpr int RW = 256 / LPR;
+  const int grid = EPI == kEpiSwiglu ? (p.N + RW / 2 - 1) / (RW / 2) : (p.N + RW - 1) / RW;
   const int lds = TT * p.K * 2 > 256 ? TT * p.K * 2 : 256;
-  hipLaunchKernelGGL((dense_gemv_kernel<TT, EPI>), dim3(grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((dense_gemv_kernel<TT, LPR, EPI>), dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
+}
+
+template <int TT, int EPI>
+hipError_t gemv_lpr(const DenseArgs& p, hipStream_t s) {
+  // the fewest lanes per row that still give >= 256 workgroups and >= 2 pieces per lane
+  const int rows = EPI == kEpiSwiglu ? 2 * p.N : p.N, nk8 = p.K / 8;
+  if (rows / 8 >= 256 || nk8 < 128) return launch_gemv_t<TT, 32, EPI>(p, s);
+  if (rows / 4 >= 256 || nk8 < 256) return launch_gemv_t<TT, 64, EPI>(p, s);
+  return launch_gemv_t<TT, 128, EPI>(p, s);
 }
 
 template <int EPI>
 hipError_t gemv(const DenseArgs& p, hipStream_t s) {
-  switch (p.M) {
-    case 1: return launch_gemv_t<1, EPI>(p, s);
-    case 2: return launch_gemv_t<2, EPI>(p, s);
-    case 3: return launch_gemv_t<3, EPI>(p, s);
-    case 4: return launch_gemv_t<4, EPI>(p, s);
-    case 5: return launch_gemv_t<5, EPI>(p, s);
-    case 6: return launch_gemv_t<6, EPI>(p, s);
-    case 7: return launch_gemv_t<7, EPI>(p, s);
-    default: return launch_gemv_t<8, EPI>(p, s);
-  }
+  if (p.M <= 1) return gemv_lpr<1, EPI>(p, s);
+  if (p.M <= 2) return gemv_lpr<2, EPI>(p, s);
+  if (p.M <= 4) return gemv_lpr<4, EPI>(p, s);
+  return gemv_lpr<8, EPI>(p, s);
 }
+
+// Token rows the GEMV kernel for M rows is compiled for (LDS holds that many staged rows).
+inline int gemv_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 template <int EPI>
 hipError_t dense(const DenseArgs& p, hipStream_t s) {
-  if (p.M <= kGemvMaxRows && p.M * p.K * 2 <= kGemvMaxLds) return gemv<EPI>(p, s);
+  if (p.M <= kGemvMaxRows && gemv_rows(p.M) * p.K * 2 <= kGemvMaxLds) return gemv<EPI>(p, s);
   return gemm<EPI>(p, s);
 }
 

@@ -52,6 +52,7 @@ def gpu_router(x_np, wr_np):
 
 
 @pytest.mark.parametrize("T,H,E", [(1, 256, 64), (4, 3072, 512), (8, 256, 100), (9, 256, 100),
+                                   (6, 1024, 320), (2, 4096, 1024), (3, 2048, 2048),
                                    (16, 256, 64), (300, 512, 200), (700, 192, 384)])
 def test_router_logits(T, H, E):
     log(f"router T={T} H={H} E={E}")
@@ -90,6 +91,7 @@ def gpu_shared(x_np, sh, y0=None):
 
 
 @pytest.mark.parametrize("T,H,I", [(1, 256, 64), (4, 3072, 768), (8, 256, 128), (9, 256, 128),
+                                   (7, 512, 192), (2, 4096, 1024),
                                    (16, 256, 128), (300, 512, 192), (600, 192, 320)])
 def test_shared_expert(T, H, I):
     log(f"shared T={T} H={H} I={I}")
