@@ -43,7 +43,8 @@ class _Weights(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        src = os.path.join(_HERE, "oracle.c")
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(src) > os.path.getmtime(_LIB_PATH):
             build_library()
         L = ctypes.CDLL(_LIB_PATH)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
@@ -74,6 +75,10 @@ def lib():
         L.oracle_shared_expert.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
         L.oracle_rmsnorm.restype = None
         L.oracle_router_logits.restype = None
+        L.oracle_usage_update.argtypes = [vp, i32, i32, i32, vp]
+        L.oracle_usage_update.restype = None
+        L.oracle_usage_rank.argtypes = [vp, i32, vp]
+        L.oracle_usage_rank.restype = None
         L.oracle_shared_expert.restype = None
         _lib = L
     return _lib
@@ -236,3 +241,20 @@ def shared_expert(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray)
     out = np.empty((T, H), dtype=np.float64)
     lib().oracle_shared_expert(px, pg, pu, pd, T, H, Is, out.ctypes.data)
     return out
+
+
+def usage_update(ids: np.ndarray, E: int, usage: np.ndarray | None = None) -> np.ndarray:
+    """usage uint64 [E] += number of slots of ids (int32 [T][k]) routed to each expert."""
+    ii, pi = _c(ids, np.int32)
+    T, k = ii.shape
+    u = np.zeros(E, dtype=np.uint64) if usage is None else np.ascontiguousarray(usage, dtype=np.uint64).copy()
+    lib().oracle_usage_update(pi, T, k, E, u.ctypes.data)
+    return u
+
+
+def usage_rank(usage: np.ndarray) -> np.ndarray:
+    """Experts by usage, most used first, ties to the lower index (int32 [E])."""
+    u, pu = _c(usage, np.uint64)
+    order = np.empty(u.shape[0], dtype=np.int32)
+    lib().oracle_usage_rank(pu, u.shape[0], order.ctypes.data)
+    return order

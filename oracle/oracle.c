@@ -313,3 +313,36 @@ void oracle_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t*
   }
   free(a);
 }
+
+/*
+ * Expert usage statistics.  The pages' engine keeps a running distribution of how often each
+ * expert is used and treats the most-used ones as hot (video transcript on unbiasedbob.com, 7:47
+ * to 7:58; "Strata - the details", How it works / memory tiers).  This library's statistic is the
+ * plainest one: usage[e] += the number of (token, slot) pairs routed to expert e, accumulated
+ * over calls in 64-bit integers.
+ */
+void oracle_usage_update(const int32_t* ids, int32_t T, int32_t k, int32_t E, uint64_t* usage) {
+  for (int64_t s = 0; s < (int64_t)T * k; ++s) {
+    const int32_t e = ids[s];
+    if (e >= 0 && e < E) usage[e] += 1;
+  }
+}
+
+/*
+ * Hotness order: order[r] is the expert of rank r, experts sorted by usage, most used first,
+ * equal usage broken by the lower expert index.  Written as E rounds of picking the largest
+ * not-yet-picked count (selection), the definition read literally.
+ */
+void oracle_usage_rank(const uint64_t* usage, int32_t E, int32_t* order) {
+  char* taken = (char*)calloc((size_t)E, 1);
+  for (int32_t r = 0; r < E; ++r) {
+    int32_t best = -1;
+    for (int32_t e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || usage[e] > usage[best]) best = e;
+    }
+    order[r] = best;
+    taken[best] = 1;
+  }
+  free(taken);
+}

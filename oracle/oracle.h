@@ -50,6 +50,8 @@ void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int3
                           double* logits);
 void oracle_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                           const uint16_t* wd, int32_t T, int32_t H, int32_t Is, double* out);
+void oracle_usage_update(const int32_t* ids, int32_t T, int32_t k, int32_t E, uint64_t* usage);
+void oracle_usage_rank(const uint64_t* usage, int32_t E, int32_t* order);
 
 #ifdef __cplusplus
 }

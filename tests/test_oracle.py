@@ -437,6 +437,50 @@ def test_shared_expert_zero_and_scaling(oracle_lib):
                                rtol=1e-13, atol=1e-15)
 
 
+# ---------------------------------------------------------------------------------------------
+# Expert usage statistics and the hotness order
+
+
+def test_usage_counts_brute_force_and_accumulate(oracle_lib):
+    rng = np.random.default_rng(3)
+    E, k = 37, 5
+    u = None
+    total = np.zeros(E, dtype=np.int64)
+    for T in (1, 13, 64):
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        u = oracle.usage_update(ids, E, u)
+        total += np.bincount(ids.reshape(-1), minlength=E)
+        assert np.array_equal(u.astype(np.int64), total)
+    assert int(u.sum()) == (1 + 13 + 64) * k
+
+
+def test_usage_counts_from_routing(oracle_lib):
+    """Counts of a routed layer equal the permutation's per-expert counts and sum to T*k."""
+    shape = mi.TINY
+    ids, _ = oracle.route(mi.make_logits(shape), shape.k)
+    u = oracle.usage_update(ids, shape.E)
+    counts, *_ = oracle.permute(ids, shape.E)
+    assert np.array_equal(u.astype(np.int64), counts.astype(np.int64))
+    assert int(u.sum()) == shape.T * shape.k
+
+
+def test_usage_rank_hand_example_and_ties(oracle_lib):
+    assert oracle.usage_rank(np.array([3, 5, 5, 0, 3], dtype=np.uint64)).tolist() == [1, 2, 0, 4, 3]
+    assert oracle.usage_rank(np.zeros(6, dtype=np.uint64)).tolist() == list(range(6))
+    assert oracle.usage_rank(np.array([1 << 40, 1, (1 << 40) + 1], dtype=np.uint64)).tolist() == [2, 0, 1]
+
+
+def test_usage_rank_matches_library_sort(oracle_lib):
+    rng = np.random.default_rng(9)
+    for E in (1, 7, 512, 1024):
+        u = rng.integers(0, 6, size=E).astype(np.uint64)  # many ties
+        order = oracle.usage_rank(u)
+        ref = np.lexsort((np.arange(E), -u.astype(np.int64)))
+        assert np.array_equal(order, ref)
+        assert sorted(order.tolist()) == list(range(E))
+        assert np.all(np.diff(u[order].astype(np.int64)) <= 0)
+
+
 # Golden regression values (written by tests/golden/make_golden.py from the oracle only)
 
 
