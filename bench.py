@@ -11,7 +11,8 @@ logits): a layer's experts are re-read only after ~1.4 GB of other layers' traff
 Secondary (same JSON line, key "prefill"): one prefill chunk of one layer, T = 8192, same
 dimensions; a step is one whole-layer call.  Keys "block_decode" and "prefill.block": the dense
 layers on either side of the routed experts (router projection x W_r^T, shared SwiGLU expert),
-alone and as the whole block router -> routed layer -> + shared expert.
+alone and as the whole block router -> routed layer -> + shared expert.  Key "pruned": the same
+decode and prefill legs with 256 experts per layer (the pages' pruned coder variant).
 
 value = whole-job layer-tokens/s = T * steps / timed seconds, inputs resident in HBM.
 roofline: HBM-bound decode (touched experts' packed bytes per layer call / call duration, peak
@@ -97,14 +98,14 @@ def copy_calibration(mb, stream):
     log(f"copy calibration: 3 copies of {n} bytes")
 
 
-def bench_decode(args, stream):
+def bench_decode(args, stream, shape=None):
     import torch
 
     import bit_expert_ffn_fp32_amd as sm
     import moe_inputs as mi
     from gpu_helpers import Layer
 
-    s = mi.DECODE
+    s = mi.DECODE if shape is None else shape
     n_layers = args.decode_layers
     t0 = time.time()
     layers = []
@@ -443,6 +444,8 @@ def main():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-pruned", action="store_true",
+                   help="skip the 256-expert (pruned) variant")
     p.add_argument("--no-block", action="store_true",
                    help="skip the router projection / shared expert measurements")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -469,10 +472,33 @@ def main():
     layers = dec.pop("layers")
     blk = None if args.no_block else bench_block_decode(args, stream, layers)
     torch.cuda.empty_cache()
+    pruned = None
+    if not args.no_pruned:  # the pages' pruned coder variant: 256 experts per layer
+        for L in layers:
+            del L.w
+        torch.cuda.empty_cache()
+        pd = bench_decode(args, stream, mi.PRUNED_DECODE)
+        for L in pd.pop("layers"):
+            del L.w
+        torch.cuda.empty_cache()
+        pruned = {"decode": {k: pd[k] for k in ("ms_per_step", "value", "touched_experts_mean")},
+                  "decode_roofline": pd["roofline"]}
+        pruned["decode"]["unit"] = "layer-tokens/s"
+        pruned["decode_roofline"]["traffic"] = None
+        log(f"pruned decode (E=256): {pd['ms_per_step'] * 1e3:.2f} us/layer, "
+            f"{pd['roofline']['achieved']:.0f} GB/s")
+        if not args.no_prefill:
+            pp = bench_prefill(args, stream, "pruned_prefill")
+            pruned["prefill"] = {k: pp[k] for k in ("workload", "value", "unit", "ms_per_step",
+                                                    "layer_tflops", "roofline")}
+            log(f"pruned prefill (E=256): {pp['ms_per_step']:.3f} ms/layer, expert FFN "
+                f"{pp['roofline']['achieved']:.0f} TFLOP/s")
+            torch.cuda.empty_cache()
     pre = skw = None
     if not args.no_prefill:
         for L in layers:
-            del L.w
+            if hasattr(L, "w"):
+                del L.w
         torch.cuda.empty_cache()
         pre = bench_prefill(args, stream, "prefill")
         log(f"prefill: {pre['ms_per_step']:.3f} ms/layer, {pre['value']:.4g} tokens/s, layer "
@@ -533,6 +559,8 @@ def main():
     }
     if blk is not None:
         line["block_decode"] = blk
+    if pruned is not None:
+        line["pruned"] = pruned
     if pre is not None:
         line["prefill"] = pre
     if skw is not None:

@@ -24,6 +24,7 @@ CODE_BYTES = {Q2: 8, Q3: 12}
 EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "strata_moe_combine",
            "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
            "strata_moe_router_logits", "strata_moe_shared_expert",
+           "strata_moe_usage_update", "strata_moe_usage_rank",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
            "strata_moe_shared_workspace_bytes", "strata_status_string"]
 
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "strata_moe_pack_matrix": [i32, i32, i32, i32, vp, vp, vp, vp, vp],
             "strata_moe_router_logits": [vp, vp, i32, i32, i32, vp, vp],
             "strata_moe_shared_expert": [vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, sz, vp],
+            "strata_moe_usage_update": [vp, i32, i32, i32, vp, vp],
+            "strata_moe_usage_rank": [vp, i32, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -239,3 +242,17 @@ def strata_moe_shared_expert(x, w_gate, w_up, w_down, y, workspace, accumulate=F
         _p(x), _p(w_gate), _p(w_up), _p(w_down), T, H, I, _p(y), int(accumulate), _p(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream)))
+
+
+def strata_moe_usage_update(topk_ids, E, usage, stream=None) -> None:
+    """usage (int64 tensor [E], read as uint64) += per-expert slot counts of topk_ids [T][k]."""
+    T, k = topk_ids.shape
+    _check("strata_moe_usage_update", lib().strata_moe_usage_update(
+        _p(topk_ids), T, k, E, _p(usage), _stream(stream)))
+
+
+def strata_moe_usage_rank(usage, order, stream=None) -> None:
+    """order (int32 [E]) = experts by usage, most used first, ties to the lower index."""
+    E = usage.shape[0]
+    _check("strata_moe_usage_rank", lib().strata_moe_usage_rank(_p(usage), E, _p(order),
+                                                                _stream(stream)))

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstrata_moe.so")
-SOURCES = ["api.hip", "pack.hip", "route.hip", "permute.hip", "prefill.hip", "decode.hip", "dense.hip"]
+SOURCES = ["api.hip", "pack.hip", "route.hip", "permute.hip", "prefill.hip", "decode.hip", "dense.hip", "usage.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -361,6 +361,24 @@ strata_status strata_moe_shared_expert(const uint16_t* x, const uint16_t* w_gate
                                                static_cast<uint16_t*>(workspace), stream));
 }
 
+strata_status strata_moe_usage_update(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                                     uint64_t* usage, hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)T * k > INT32_MAX / 2) return STRATA_ERR_INVALID_ARGUMENT;
+  if (E > kMaxE) return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  if (!topk_ids || !usage || !aligned16(topk_ids) || !aligned16(usage)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_usage_update(topk_ids, (int64_t)T * k, E, usage, stream));
+}
+
+strata_status strata_moe_usage_rank(const uint64_t* usage, int32_t E, int32_t* order,
+                                   hipStream_t stream) {
+  if (E < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  if (E > kMaxE) return STRATA_ERR_UNSUPPORTED;
+  if (!usage || !order || !aligned16(usage) || !aligned16(order)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_usage_rank(usage, E, order, stream));
+}
+
 strata_status strata_moe_rmsnorm(const float* h, int32_t T, int32_t H, float eps, uint16_t* x,
                                  hipStream_t stream) {
   if (T < 0 || H < 1 || !(eps >= 0.0f)) return STRATA_ERR_INVALID_ARGUMENT;

@@ -64,6 +64,11 @@ hipError_t launch_shared_expert(const uint16_t* x, const uint16_t* wg, const uin
                                 const uint16_t* wd, int T, int H, int I, float* y, int accumulate,
                                 uint16_t* a, hipStream_t s);
 
+// Expert usage: usage[e] += slots of ids routed to e (E <= 1024); order = experts by usage, most
+// used first, ties to the lower index.
+hipError_t launch_usage_update(const int* ids, int64_t S, int E, uint64_t* usage, hipStream_t s);
+hipError_t launch_usage_rank(const uint64_t* usage, int E, int* order, hipStream_t s);
+
 // Decode path (T <= 8).
 hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T, int E, int k,
                          int H, int I, const void* gate_codes, const void* up_codes,

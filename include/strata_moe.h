@@ -262,6 +262,28 @@ strata_status strata_moe_shared_expert(const uint16_t* x, const uint16_t* w_gate
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
+/*
+ * Expert usage statistics.  The pages' engine keeps a running distribution of how often each
+ * expert is used and keeps the most-used experts nearest the compute (video transcript on
+ * unbiasedbob.com, 7:47 to 7:58; "Strata - the details", How it works / memory tiers).  This
+ * library's statistic: usage[e] += the number of (token, slot) pairs of topk_ids routed to e
+ * (ids outside [0, E) are ignored), in 64-bit integers, so it accumulates exactly over calls;
+ * the caller zeroes usage to start a new window.
+ *   topk_ids int32 [T][k] (read; e.g. the opt_topk_ids output of strata_moe_layer)
+ *   usage    uint64 [E] (read and written)
+ * Limits: E <= 1024 (STRATA_ERR_UNSUPPORTED otherwise).
+ */
+strata_status strata_moe_usage_update(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                                     uint64_t* usage, hipStream_t stream);
+
+/*
+ * Hotness order of the experts: order[r] = the expert of rank r by usage, most used first, equal
+ * usage broken by the lower expert index (a permutation of 0 .. E-1).
+ *   usage uint64 [E] (read), order int32 [E] (written).  E <= 1024.
+ */
+strata_status strata_moe_usage_rank(const uint64_t* usage, int32_t E, int32_t* order,
+                                   hipStream_t stream);
+
 /* Workspace sizes in bytes (host functions; 0 for invalid shapes). */
 size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k);
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);

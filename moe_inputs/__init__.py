@@ -185,7 +185,11 @@ PREFILL = Shape("prefill", T=8192, H=3072, E=512, k=10, I=768)
 SKEWED = Shape("skewed", T=2048, H=3072, E=512, k=10, I=768, fmt=Q3, zipf=True)
 STACK_PREFILL = replace(PREFILL, name="stack_prefill", layers=48)
 STACK_DECODE = replace(DECODE, name="stack_decode", layers=48)
-SHAPES = {s.name: s for s in (TINY, DECODE, PREFILL, SKEWED, STACK_PREFILL, STACK_DECODE)}
+# the pruned coder variant keeps 256 of a layer's 512 experts
+PRUNED_DECODE = replace(DECODE, name="pruned_decode", E=256)
+PRUNED_PREFILL = replace(PREFILL, name="pruned_prefill", E=256)
+SHAPES = {s.name: s for s in (TINY, DECODE, PREFILL, SKEWED, STACK_PREFILL, STACK_DECODE,
+                              PRUNED_DECODE, PRUNED_PREFILL)}
 
 
 def zipf_bias(seed: int, layer: int, E: int, s: float = 1.1, strength: float = 2.0) -> np.ndarray:

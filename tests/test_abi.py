@@ -133,6 +133,19 @@ def test_router_and_shared_validation(L):
     assert call(T=0, y=None, x=None) == OK
 
 
+def test_usage_validation(L):
+    assert L.strata_moe_usage_update(A, 4, 10, 0, A, None) == INVAL
+    assert L.strata_moe_usage_update(A, 4, 0, 512, A, None) == INVAL
+    assert L.strata_moe_usage_update(A, 4, 10, 2048, A, None) == UNSUP
+    assert L.strata_moe_usage_update(None, 4, 10, 512, A, None) == INVAL
+    assert L.strata_moe_usage_update(A, 4, 10, 512, MIS, None) == INVAL
+    assert L.strata_moe_usage_update(None, 0, 10, 512, None, None) == OK
+    assert L.strata_moe_usage_rank(A, 0, A, None) == INVAL
+    assert L.strata_moe_usage_rank(A, 1025, A, None) == UNSUP
+    assert L.strata_moe_usage_rank(None, 512, A, None) == INVAL
+    assert L.strata_moe_usage_rank(A, 512, MIS, None) == INVAL
+
+
 def test_workspace_sizes(L):
     assert L.strata_moe_workspace_bytes(-1, 512, 10, 3072, 768) == 0
     small = L.strata_moe_workspace_bytes(16, 64, 4, 256, 128)
