@@ -12,7 +12,8 @@ Secondary (same JSON line, key "prefill"): one prefill chunk of one layer, T = 8
 dimensions; a step is one whole-layer call.  Keys "block_decode" and "prefill.block": the dense
 layers on either side of the routed experts (router projection x W_r^T, shared SwiGLU expert),
 alone and as the whole block router -> routed layer -> + shared expert.  Key "pruned": the same
-decode and prefill legs with 256 experts per layer (the pages' pruned coder variant).
+decode and prefill legs with 256 experts per layer (the pages' pruned coder variant).  Key
+"sweep": the decode path at T = 1 .. 8 and the prefill path at T = 1 .. 256 (crossover).
 
 value = whole-job layer-tokens/s = T * steps / timed seconds, inputs resident in HBM.
 roofline: HBM-bound decode (touched experts' packed bytes per layer call / call duration, peak
@@ -296,6 +297,96 @@ def block_prefill(args, stream, L, ws, y):
     return out
 
 
+def bench_sweep(args, stream, layers):
+    """Decode / verify T-sweep and the decode-prefill crossover.  For T = 1 .. 8 (MTP verify is
+    T = 4, prompt-lookup verify up to T = 6) the layer runs on the decode path and, through the
+    staged entry points (route, permute, expert FFN, combine), on the prefill path; the prefill
+    path is also timed at T = 16 .. 256.  Each point is a graph replay of one call per resident
+    layer (16 layers cycled, each with its own experts, activations and logits)."""
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import to_dev, to_dev_bf16
+
+    s = mi.DECODE
+    n = len(layers)
+    t_dec = list(range(1, 9))
+    t_pre = t_dec + [16, 32, 64, 128, 256]
+    tmax = max(t_pre)
+    xs = [to_dev_bf16(mi.make_x(s, args.seed, l, tmax)) for l in range(n)]
+    lg_np = [mi.make_logits(s, args.seed, l, tmax) for l in range(n)]
+    lgs = [to_dev(a) for a in lg_np]
+    ws = sm.alloc_workspace(max(sm.workspace_bytes(T, s.E, s.k, s.H, s.I) for T in t_pre), "cuda")
+    y = torch.empty((tmax, s.H), dtype=torch.float32, device="cuda")
+    S = tmax * s.k
+    ids = torch.empty((tmax, s.k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((tmax, s.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(s.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(S, dtype=torch.int32, device="cuda")
+    sp = torch.empty(S, dtype=torch.int32, device="cuda")
+    out = torch.empty((S, s.H), dtype=torch.int16, device="cuda")
+
+    def decode_path(T):
+        def f(i, strm):
+            L = layers[i]
+            sm.strata_moe_layer(L.w, xs[i][:T], lgs[i][:T], s.k, y[:T], workspace=ws, stream=strm)
+        return f
+
+    def prefill_path(T):
+        def f(i, strm):
+            L = layers[i]
+            sm.strata_moe_route(lgs[i][:T], s.k, ids[:T], rw[:T], stream=strm)
+            sm.strata_moe_permute(ids[:T], s.E, counts, offsets, ss[:T * s.k], sp[:T * s.k], ws,
+                                  stream=strm)
+            sm.strata_moe_expert_ffn(L.w, xs[i][:T], s.k, offsets, ss[:T * s.k], out[:T * s.k], ws,
+                                     stream=strm)
+            sm.strata_moe_combine(out[:T * s.k], rw[:T], y[:T], stream=strm)
+        return f
+
+    def graph_us(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(n):
+                fn(i, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for i in range(n):
+                fn(i, cap)
+        g.replay()
+        reps = 4
+        return event_time_ms(lambda r: g.replay(), reps, stream) / (reps * n) * 1e3
+
+    def touched_bytes(T):
+        tot = 0
+        for a in lg_np:
+            top = np.argsort(-a[:T].astype(np.float64), axis=1, kind="stable")[:, :s.k]
+            tot += len(np.unique(top))
+        return tot / n * s.expert_bytes
+
+    dec, pre = [], []
+    for T in t_dec:
+        us = graph_us(decode_path(T))
+        b = touched_bytes(T)
+        dec.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6), "GBs": b / (us * 1e-6) / 1e9})
+    for T in t_pre:
+        us = graph_us(prefill_path(T))
+        pre.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6)})
+    faster = [p["T"] for p, d in zip(pre, dec) if p["us"] < d["us"]]
+    out_d = {"decode_path": dec, "prefill_path": pre,
+             "crossover_T": min(faster) if faster else None,
+             "note": "decode path used by strata_moe_layer for T <= 8"}
+    log("sweep: decode path " + ", ".join(f"T={d['T']} {d['us']:.1f}us" for d in dec))
+    log("sweep: prefill path " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in pre))
+    del xs, lgs, ws, out
+    return out_d
+
+
 def bench_prefill(args, stream, name):
     import torch
 
@@ -444,6 +535,8 @@ def main():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the decode T-sweep and the decode-prefill crossover")
     p.add_argument("--no-pruned", action="store_true",
                    help="skip the 256-expert (pruned) variant")
     p.add_argument("--no-block", action="store_true",
@@ -471,6 +564,8 @@ def main():
         f"{dec['roofline']['achieved']:.0f} GB/s ({dec['roofline']['frac'] * 100:.1f}% of HBM peak)")
     layers = dec.pop("layers")
     blk = None if args.no_block else bench_block_decode(args, stream, layers)
+    torch.cuda.empty_cache()
+    sweep = None if args.no_sweep else bench_sweep(args, stream, layers)
     torch.cuda.empty_cache()
     pruned = None
     if not args.no_pruned:  # the pages' pruned coder variant: 256 experts per layer
@@ -561,6 +656,8 @@ def main():
         line["block_decode"] = blk
     if pruned is not None:
         line["pruned"] = pruned
+    if sweep is not None:
+        line["sweep"] = sweep
     if pre is not None:
         line["prefill"] = pre
     if skw is not None:

@@ -43,9 +43,11 @@ def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False):
     return y, ids, rw, extra
 
 
-def test_decode_full_size():
-    log("decode full size: generating")
-    L = Layer(mi.DECODE)
+@pytest.mark.parametrize("T", [1, 4, 6, 8])
+def test_decode_full_size(T):
+    """T = 4: MTP verify (1 + 3 drafts); T = 6: prompt-lookup verify (1 + 5 drafts)."""
+    log(f"decode full size T={T}: generating")
+    L = Layer(mi.DECODE, T=T)
     y, ids, rw, _ = run_layer(L)
     y_ref, ids_ref, w_ref, _, _ = oracle.layer(L.w_np, L.x_np, L.l_np, 10, intermediates=True)
     assert np.array_equal(ids.cpu().numpy(), ids_ref)

@@ -212,7 +212,7 @@ def test_layer_against_oracle(s):
     np.testing.assert_allclose(ya, y0 + y, rtol=1e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 6, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decode_matches_prefill_path(T):
     s = shape("dp", T=T, H=512, E=32, k=4, I=256)
     L = Layer(s)
