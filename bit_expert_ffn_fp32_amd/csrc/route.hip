@@ -6,9 +6,12 @@
 // made on the logits themselves: k rounds of a wave-wide arg-max in which expert a beats b iff
 // l_a > l_b, or l_a == l_b and a < b.  The kept weights are exp(l_j - l_0) / sum_i exp(l_i - l_0).
 //
-// Lane l holds experts l, l + 64, l + 128, ... so every load of a token's row is coalesced.
+// Lane l holds experts l, l + 64, l + 128, ... so every load of a token's row is coalesced.  Each
+// lane sorts its own entries once (largest first); a round takes the wave-wide maximum of the
+// lanes' heads (DPP) and the winning lane pops its head, the selection the decode kernel runs too.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace strata {
 
@@ -16,43 +19,11 @@ template <int NPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int* __restrict__ ids,
                                                     float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float v[NPL];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
-    if (e >= E) taken |= 1u << i;
-  }
-  float my_v = 0.0f;
-  int my_i = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      const bool free_ = !((taken >> i) & 1u);
-      // within a lane e grows with i, so a strict '>' keeps the lower index on ties
-      if (free_ && (bi == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; bi = e; }
-    }
-    // lanes with nothing left must lose every comparison
-    if (bi == 0x7FFFFFFF) bv = -__builtin_inff();
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { my_v = bv; my_i = bi; }
-  }
-  const float top = __shfl(my_v, 0);
-  const float ex = lane < k ? expf(my_v - top) : 0.0f;
-  const float den = wave_sum(ex);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_i;
-    w[(size_t)t * k + lane] = ex / den;
-  }
+  TokenKeys<NPL> tk;
+  load_token_logits<NPL>(logits + (size_t)t * E, E, tk);
+  select_token_wave<NPL>(tk, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
