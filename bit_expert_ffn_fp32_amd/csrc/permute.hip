@@ -11,9 +11,9 @@
 //  2. scan:    one workgroup turns the histograms into counts, offsets (exclusive prefix sum)
 //              and each tile's starting position per expert; it also cuts every expert's segment
 //              into GEMM chunks of at most kChunkRows rows, balanced in 32-row fragments.
-//  3. scatter: each tile ranks its slots stably: in rounds of 256 slots, a slot's rank is the
+//  3. scatter: each tile ranks its slots stably in one round of 1024 threads: a slot's rank is the
 //              number of equal ids in earlier lanes of its wave (an LDS broadcast loop), plus the
-//              counts of earlier waves of the round, plus the tile's running count.
+//              counts of the earlier waves, plus the tile's starting position for its expert.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,43 +62,69 @@ __device__ int block_exclusive_scan(int v, int* lds16, int& total) {
   return wbase + inc - v;
 }
 
+// hist[t][e] summed over the tiles [t0, t1) of one expert, 16 loads in flight at a time.
+__device__ int tile_sum(const int* __restrict__ hist, int E, int e, int t0, int t1) {
+  int acc = 0, t = t0;
+  for (; t + 16 <= t1; t += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(t + u) * E + e];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += v[u];
+  }
+  for (; t < t1; ++t) acc += hist[(size_t)t * E + e];
+  return acc;
+}
+
+// P = 1024 / E' threads per expert (E' = E rounded up to a power of two): part q of expert e
+// handles tiles [q nt / P, (q+1) nt / P), so the loads of a long tile list are spread over P
+// threads.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
-    const int* __restrict__ hist, int ntiles, int E, int* __restrict__ tile_base,
+    const int* __restrict__ hist, int ntiles, int E, int P, int* __restrict__ tile_base,
     int* __restrict__ counts, int* __restrict__ offsets, Chunk* __restrict__ chunks,
     int* __restrict__ n_chunks) {
   __shared__ int lds16[16];
-  const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E) {
-    int t = 0;
-    for (; t + 8 <= ntiles; t += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(t + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) cnt += v[u];
+  __shared__ int psum[1024];  // [part][e]
+  const int Ep = 1024 / P;    // threads of one part (>= E)
+  const int q = threadIdx.x / Ep, e = threadIdx.x % Ep;
+  const bool mine = e < E;
+  const int t0 = (int)((int64_t)ntiles * q / P), t1 = (int)((int64_t)ntiles * (q + 1) / P);
+  const int part = mine ? tile_sum(hist, E, e, t0, t1) : 0;
+  psum[threadIdx.x] = part;
+  __syncthreads();
+  int cnt = 0, before = 0;  // the expert's count, and the parts before this one
+  if (mine) {
+    for (int r = 0; r < P; ++r) {
+      const int v = psum[r * Ep + e];
+      cnt += v;
+      before += r < q ? v : 0;
     }
-    for (; t < ntiles; ++t) cnt += hist[(size_t)t * E + e];
   }
   int total;
-  const int off = block_exclusive_scan(e < E ? cnt : 0, lds16, total);
-  if (e < E) {
-    counts[e] = cnt;
-    offsets[e] = off;
-    if (e == E - 1) offsets[E] = off + cnt;
-    int run = off;
-    int t = 0;
-    for (; t + 8 <= ntiles; t += 8) {
-      int v[8];
+  const int off = block_exclusive_scan(q == 0 && mine ? cnt : 0, lds16, total);
+  __shared__ int off_e[1024];
+  if (q == 0) off_e[e] = off;
+  __syncthreads();
+  if (mine) {
+    const int o = off_e[e];
+    if (q == 0) {
+      counts[e] = cnt;
+      offsets[e] = o;
+      if (e == E - 1) offsets[E] = o + cnt;
+    }
+    int run = o + before;
+    int t = t0;
+    for (; t + 16 <= t1; t += 16) {
+      int v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(t + u) * E + e];
+      for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(t + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         tile_base[(size_t)(t + u) * E + e] = run;
         run += v[u];
       }
     }
-    for (; t < ntiles; ++t) {
+    for (; t < t1; ++t) {
       tile_base[(size_t)t * E + e] = run;
       run += hist[(size_t)t * E + e];
     }
@@ -108,8 +134,8 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   const int nfrag = (cnt + 31) / 32;
   const int nch = (nfrag + (kChunkRows / 32) - 1) / (kChunkRows / 32);
   int ctotal;
-  const int cbase = block_exclusive_scan(e < E ? nch : 0, lds16, ctotal);
-  if (e < E && nch > 0) {
+  const int cbase = block_exclusive_scan(q == 0 && mine ? nch : 0, lds16, ctotal);
+  if (q == 0 && mine && nch > 0) {
     const int fb = nfrag / nch, extra = nfrag % nch;
     int row = off, frag_used = 0;
     for (int c = 0; c < nch; ++c) {
@@ -120,52 +146,47 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
       frag_used += nf;
     }
   }
-  if (e == 0) *n_chunks = ctotal;
+  if (threadIdx.x == 0) *n_chunks = ctotal;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
+// One workgroup of 1024 threads (16 waves) per tile of kPermTile = 1024 slots, in one round: a
+// slot's rank is the number of equal ids in earlier lanes of its wave (an LDS broadcast loop)
+// plus the counts of the earlier waves, plus the tile's starting position for its expert.
+constexpr int kScatterThreads = 1024;
+constexpr int kScatterWaves = kScatterThreads / 64;
+static_assert(kPermTile == kScatterThreads, "one slot per thread");
+
+__global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
     const int* __restrict__ ids, int S, int E, const int* __restrict__ tile_base,
     int* __restrict__ sorted_slot, int* __restrict__ slot_pos) {
   extern __shared__ int lds[];
-  int* cnt = lds;                 // [E] running position per expert
-  int* wc = lds + E;              // [4][E] per-wave counts of the current round
-  int* ids_l = lds + 5 * E;       // [256] ids of the current round
+  int* ids_l = lds;                                               // [1024]
+  uint8_t* wc = reinterpret_cast<uint8_t*>(lds + kScatterThreads);  // [16][E] per-wave counts (<= 64)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = tid; e < E; e += kPermThreads) {
-    cnt[e] = tile_base[(size_t)blockIdx.x * E + e];
-    wc[e] = wc[E + e] = wc[2 * E + e] = wc[3 * E + e] = 0;
+  for (int i = tid; i < kScatterWaves * E / 4; i += kScatterThreads) reinterpret_cast<int*>(wc)[i] = 0;
+  const int s = blockIdx.x * kPermTile + tid;
+  const int id0 = s < S ? ids[s] : -1;
+  const bool valid = (unsigned)id0 < (unsigned)E;  // out-of-range ids are skipped
+  const int id = valid ? id0 : -1;
+  const int base = valid ? tile_base[(size_t)blockIdx.x * E + id] : 0;
+  ids_l[tid] = id;
+  __syncthreads();
+  int rank = 0;
+  bool last = true;
+  const int* wids = ids_l + wv * 64;
+  for (int i = 0; i < 64; ++i) {
+    const int o = wids[i];
+    rank += (i < lane && o == id) ? 1 : 0;
+    last = last && !(i > lane && o == id);
   }
-  const int base = blockIdx.x * kPermTile;
-  for (int r = 0; r < kPermTile / kPermThreads; ++r) {
-    const int s = base + r * kPermThreads + tid;
-    const int id0 = s < S ? ids[s] : -1;
-    const bool valid = (unsigned)id0 < (unsigned)E;  // out-of-range ids are skipped
-    const int id = valid ? id0 : -1;
-    ids_l[tid] = id;
-    __syncthreads();
-    int rank = 0;
-    bool last = true;
-    const int* wids = ids_l + wv * 64;
-    for (int i = 0; i < 64; ++i) {
-      const int o = wids[i];
-      rank += (i < lane && o == id) ? 1 : 0;
-      last = last && !(i > lane && o == id);
-    }
-    if (valid && last) wc[wv * E + id] = rank + 1;
-    __syncthreads();
-    if (valid) {
-      int before = 0;
-      for (int w2 = 0; w2 < wv; ++w2) before += wc[w2 * E + id];
-      const int pos = cnt[id] + before + rank;
-      sorted_slot[pos] = s;
-      slot_pos[s] = pos;
-    }
-    __syncthreads();
-    if (valid && last) {
-      atomicAdd(&cnt[id], rank + 1);
-      wc[wv * E + id] = 0;
-    }
-    __syncthreads();
+  if (valid && last) wc[wv * E + id] = (uint8_t)(rank + 1);
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int w2 = 0; w2 < wv; ++w2) before += wc[w2 * E + id];
+    const int pos = base + before + rank;
+    sorted_slot[pos] = s;
+    slot_pos[s] = pos;
   }
 }
 
@@ -175,10 +196,13 @@ hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int*
   const int S = T * k;
   const int ntiles = (S + kPermTile - 1) / kPermTile;
   permute_count_kernel<<<ntiles, kPermThreads, E * sizeof(int), s>>>(ids, S, E, tile_hist);
-  permute_scan_kernel<<<1, 1024, 0, s>>>(tile_hist, ntiles, E, tile_base, counts, offsets, chunks,
-                                         n_chunks);
-  permute_scatter_kernel<<<ntiles, kPermThreads, (5 * E + kPermThreads) * sizeof(int), s>>>(
-      ids, S, E, tile_base, sorted_slot, slot_pos);
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;  // E <= 1024
+  permute_scan_kernel<<<1, 1024, 0, s>>>(tile_hist, ntiles, E, 1024 / Ep, tile_base, counts,
+                                         offsets, chunks, n_chunks);
+  const size_t scatter_lds = kScatterThreads * sizeof(int) + ((size_t)kScatterWaves * E + 3) / 4 * 4;
+  permute_scatter_kernel<<<ntiles, kScatterThreads, scatter_lds, s>>>(ids, S, E, tile_base,
+                                                                      sorted_slot, slot_pos);
   return hipGetLastError();
 }
 
