@@ -64,15 +64,14 @@ __device__ int block_exclusive_scan(int v, int* lds16, int& total) {
 
 // hist[t][e] summed over the tiles [t0, t1) of one expert, 16 loads in flight at a time.
 __device__ int tile_sum(const int* __restrict__ hist, int E, int e, int t0, int t1) {
-  int acc = 0, t = t0;
-  for (; t + 16 <= t1; t += 16) {
+  int acc = 0;
+  for (int t = t0; t < t1; t += 16) {
     int v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(t + u) * E + e];
+    for (int u = 0; u < 16; ++u) v[u] = t + u < t1 ? hist[(size_t)(t + u) * E + e] : 0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) acc += v[u];
   }
-  for (; t < t1; ++t) acc += hist[(size_t)t * E + e];
   return acc;
 }
 
@@ -113,20 +112,15 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
       if (e == E - 1) offsets[E] = o + cnt;
     }
     int run = o + before;
-    int t = t0;
-    for (; t + 16 <= t1; t += 16) {
+    for (int t = t0; t < t1; t += 16) {
       int v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(t + u) * E + e];
+      for (int u = 0; u < 16; ++u) v[u] = t + u < t1 ? hist[(size_t)(t + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        tile_base[(size_t)(t + u) * E + e] = run;
+        if (t + u < t1) tile_base[(size_t)(t + u) * E + e] = run;
         run += v[u];
       }
-    }
-    for (; t < t1; ++t) {
-      tile_base[(size_t)t * E + e] = run;
-      run += hist[(size_t)t * E + e];
     }
   }
   if (chunks == nullptr) return;
