@@ -153,3 +153,21 @@ def test_moe_block_router_layer_shared(T):
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     ref = ref_y + oracle.shared_expert(L.x_np, sh["gate"], sh["up"], sh["down"])
     assert rel_l2_rows(y.cpu().numpy(), ref).max() <= TOL_REL_L2
+
+
+def test_zero_tokens_and_accumulate_flag():
+    """T = 0 is a no-op for both entry points; accumulate = False overwrites whatever y held."""
+    s = shape(1, 256, I=128)
+    sh = mi.make_shared(s)
+    wr = mi.make_router(s)
+    x0 = torch.empty((0, 256), dtype=torch.int16, device=dev())
+    y0 = torch.empty((0, 256), dtype=torch.float32, device=dev())
+    lg0 = torch.empty((0, 64), dtype=torch.float32, device=dev())
+    ws = sm.alloc_workspace(0, dev())
+    sm.strata_moe_router_logits(x0, to_dev_bf16(wr), lg0)
+    sm.strata_moe_shared_expert(x0, to_dev_bf16(sh["gate"]), to_dev_bf16(sh["up"]),
+                                to_dev_bf16(sh["down"]), y0, ws)
+    x = mi.make_x(s, seed=3)
+    a = gpu_shared(x, sh)                                      # y preset to NaN, overwritten
+    b = gpu_shared(x, sh, np.zeros((1, 256), dtype=np.float32))  # accumulate onto zeros
+    assert np.array_equal(a, b)
