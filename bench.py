@@ -369,7 +369,10 @@ def bench_sweep(args, stream, layers):
             tot += len(np.unique(top))
         return tot / n * s.expert_bytes
 
-    dec, pre = [], []
+    dec, pre, lay = [], [], []
+    for T in (9, 12, 16, 24, 32, 48, 64):  # the one-call layer's own choice of path
+        us = graph_us(decode_path(T))
+        lay.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6)})
     for T in t_dec:
         us = graph_us(decode_path(T))
         b = touched_bytes(T)
@@ -378,11 +381,13 @@ def bench_sweep(args, stream, layers):
         us = graph_us(prefill_path(T))
         pre.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6)})
     faster = [p["T"] for p, d in zip(pre, dec) if p["us"] < d["us"]]
-    out_d = {"decode_path": dec, "prefill_path": pre,
+    out_d = {"decode_path": dec, "prefill_path": pre, "layer_call": lay,
              "crossover_T": min(faster) if faster else None,
-             "note": "decode path used by strata_moe_layer for T <= 8"}
+             "note": "strata_moe_layer runs the decode path for T <= 8, and on slices of at most "
+                     "8 tokens for T <= 48; layer_call times that choice"}
     log("sweep: decode path " + ", ".join(f"T={d['T']} {d['us']:.1f}us" for d in dec))
     log("sweep: prefill path " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in pre))
+    log("sweep: layer call " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in lay))
     del xs, lgs, ws, out
     return out_d
 

@@ -15,6 +15,10 @@ namespace {
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 constexpr int kMaxDecodeT = 8;
+// Up to this many tokens the one-call layer runs the decode path on slices of at most
+// kMaxDecodeT tokens: the tokens of a layer are independent, and streaming each touched expert
+// once per slice still beats the grouped GEMMs while experts see only a few rows each.
+constexpr int kSplitDecodeMaxT = 48;
 
 size_t round_up(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -157,7 +161,8 @@ size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k) {
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
   if (!shape_ok(T, E, k) || H < 1 || I < 1) return 0;
   const size_t pre = carve_prefill(nullptr, T, E, k, H, I).bytes;
-  const size_t dec = T <= kMaxDecodeT ? strata::decode_workspace_bytes(T, E, k, H, I) : 0;
+  const int32_t td = T < kMaxDecodeT ? T : kMaxDecodeT;
+  const size_t dec = T <= kSplitDecodeMaxT ? strata::decode_workspace_bytes(td, E, k, H, I) : 0;
   return pre > dec ? pre : dec;
 }
 
@@ -271,6 +276,33 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   if (T <= kMaxDecodeT && strata::decode_fits(T, w->num_experts, k, w->hidden, w->inter))
     return strata_moe_decode(w, x, logits, T, k, y, accumulate, opt_topk_ids, opt_topk_w, workspace,
                              workspace_bytes, stream);
+  if (T <= kSplitDecodeMaxT && !opt_counts && !opt_offsets && !opt_sorted_slot &&
+      strata::decode_fits(kMaxDecodeT, w->num_experts, k, w->hidden, w->inter)) {
+    const void* ptrs[4] = {x, logits, y, workspace};
+    for (const void* p : ptrs)
+      if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+    if ((opt_topk_ids && !aligned16(opt_topk_ids)) || (opt_topk_w && !aligned16(opt_topk_w)))
+      return STRATA_ERR_INVALID_ARGUMENT;
+    const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+    if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+    // Balanced slices of at most kMaxDecodeT tokens in token order on the same stream (the slices
+    // share the workspace one after the other).  The decode kernels read x with 16-byte loads
+    // (a slice starts at a multiple of H >= 256 values) and logits, ids and weights per element.
+    const int32_t n = (T + kMaxDecodeT - 1) / kMaxDecodeT;
+    int32_t t0 = 0;
+    hipError_t e = hipSuccess;
+    for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
+      const int32_t ts = T / n + (i < T % n ? 1 : 0);
+      e = strata::launch_decode(w->fmt, x + (size_t)t0 * H, logits + (size_t)t0 * E, ts, E, k, H, I,
+                                w->gate_codes, w->up_codes, w->down_codes, w->gate_scales,
+                                w->up_scales, w->down_scales, y + (size_t)t0 * H, accumulate,
+                                opt_topk_ids ? opt_topk_ids + (size_t)t0 * k : nullptr,
+                                opt_topk_w ? opt_topk_w + (size_t)t0 * k : nullptr, workspace,
+                                stream);
+      t0 += ts;
+    }
+    return from_hip(e);
+  }
   const void* ptrs[4] = {x, logits, y, workspace};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;

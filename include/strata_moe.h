@@ -196,7 +196,11 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
 
 /*
  * One-call layer: y (=, or += with accumulate) MoE(x).  T <= 8 runs strata_moe_decode's path
- * when the shape is within its limits; otherwise route -> permute -> expert_ffn -> combine.
+ * when the shape is within its limits.  9 <= T <= 48 with opt_counts, opt_offsets and
+ * opt_sorted_slot all NULL runs the same decode path on consecutive slices of at most 8 tokens
+ * (the layer's tokens are independent; with few rows per expert, streaming each touched expert
+ * once per slice is faster than the grouped GEMMs).  Otherwise route -> permute -> expert_ffn ->
+ * combine.
  * Each opt_* pointer may be NULL; when given it receives that intermediate (same layout as the
  * staged calls).  opt_counts, opt_offsets and opt_sorted_slot are only produced on the T > 8
  * path and must be NULL for T <= 8 (STRATA_ERR_INVALID_ARGUMENT otherwise).

@@ -24,7 +24,7 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False):
+def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False, perm=None):
     s, T = L.shape, L.T
     S = T * s.k
     x = L.x if x is None else x
@@ -33,7 +33,7 @@ def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False):
     ids = torch.empty((T, s.k), dtype=torch.int32, device=dev())
     rw = torch.empty((T, s.k), dtype=torch.float32, device=dev())
     extra = {}
-    if T > 8:
+    if (T > 8) if perm is None else perm:
         extra = dict(counts=torch.empty(s.E, dtype=torch.int32, device=dev()),
                      offsets=torch.empty(s.E + 1, dtype=torch.int32, device=dev()),
                      sorted_slot=torch.empty(S, dtype=torch.int32, device=dev()))
@@ -43,12 +43,13 @@ def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False):
     return y, ids, rw, extra
 
 
-@pytest.mark.parametrize("T", [1, 4, 6, 8])
+@pytest.mark.parametrize("T", [1, 4, 6, 8, 20])
 def test_decode_full_size(T):
-    """T = 4: MTP verify (1 + 3 drafts); T = 6: prompt-lookup verify (1 + 5 drafts)."""
+    """T = 4: MTP verify (1 + 3 drafts); T = 6: prompt-lookup verify (1 + 5 drafts); T = 20: the
+    decode path on slices of at most 8 tokens."""
     log(f"decode full size T={T}: generating")
     L = Layer(mi.DECODE, T=T)
-    y, ids, rw, _ = run_layer(L)
+    y, ids, rw, _ = run_layer(L, perm=False)
     y_ref, ids_ref, w_ref, _, _ = oracle.layer(L.w_np, L.x_np, L.l_np, 10, intermediates=True)
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     err = rel_l2_rows(y.cpu().numpy(), y_ref)

@@ -194,6 +194,8 @@ def gpu_layer(L: Layer, accumulate=False, y0=None, want_ids=False):
 
 
 @pytest.mark.parametrize("s", SMALL_SHAPES + [shape("t9", T=9), shape("t8", T=8), shape("t1", T=1),
+                                              shape("t17", T=17), shape("t48", T=48),
+                                              shape("t49", T=49), shape("t33_q3", T=33, fmt=3),
                                               shape("t5_q3", T=5, fmt=3), shape("t3_e1", T=3, E=1, k=1)],
                          ids=lambda s: s.name)
 def test_layer_against_oracle(s):
@@ -203,7 +205,8 @@ def test_layer_against_oracle(s):
     y, ids, rw = gpu_layer(L)
     assert np.array_equal(ids, ids_ref)
     err = rel_l2_rows(y, y_ref)
-    log(f"  y max rel-L2 {err.max():.3e} (T={s.T}, {'decode' if s.T <= 8 else 'prefill'} path)")
+    path = "decode" if s.T <= 8 else "decode slices" if s.T <= 48 else "prefill"
+    log(f"  y max rel-L2 {err.max():.3e} (T={s.T}, {path} path)")
     assert err.max() <= TOL_REL_L2
     y2, _, _ = gpu_layer(L)
     assert np.array_equal(y, y2), "second call differs"
