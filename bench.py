@@ -312,7 +312,7 @@ def bench_sweep(args, stream, layers):
     s = mi.DECODE
     n = len(layers)
     t_dec = list(range(1, 9))
-    t_pre = t_dec + [16, 32, 64, 128, 256]
+    t_pre = t_dec + [16, 32, 64, 128, 256, 512, 1024]
     tmax = max(t_pre)
     xs = [to_dev_bf16(mi.make_x(s, args.seed, l, tmax)) for l in range(n)]
     lg_np = [mi.make_logits(s, args.seed, l, tmax) for l in range(n)]
@@ -370,7 +370,7 @@ def bench_sweep(args, stream, layers):
         return tot / n * s.expert_bytes
 
     dec, pre, lay = [], [], []
-    for T in (9, 12, 16, 24, 32, 48, 64):  # the one-call layer's own choice of path
+    for T in (9, 12, 16, 24, 32, 48, 64):  # the layer call's own choice
         us = graph_us(decode_path(T))
         lay.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6)})
     for T in t_dec:
