@@ -618,17 +618,32 @@ def main():
     cpu = None
     if not args.no_cpu:
         s = mi.DECODE
+        model = "unknown"
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        affinity = os.sched_getaffinity(0)
+        core = min(affinity)
+        os.sched_setaffinity(0, {core})  # the single-threaded oracle on one pinned core
         t0 = time.time()
         n = 0
         cpu_time = 0.0
-        while n < len(layers) and (time.time() - t0) < args.cpu_seconds:
-            w_np = mi.make_weights(s, args.seed, n)
-            L = layers[n]
-            t1 = time.perf_counter()
-            oracle.layer(w_np, L.x_np, L.l_np, s.k)
-            cpu_time += time.perf_counter() - t1
-            n += 1
+        try:
+            while n < len(layers) and (time.time() - t0) < args.cpu_seconds:
+                w_np = mi.make_weights(s, args.seed, n)
+                L = layers[n]
+                t1 = time.perf_counter()
+                oracle.layer(w_np, L.x_np, L.l_np, s.k)
+                cpu_time += time.perf_counter() - t1
+                n += 1
+        finally:
+            os.sched_setaffinity(0, affinity)
         cpu = {"value": n * s.T / cpu_time, "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
+               "cpu": f"{model}; pinned to core {core} of {len(affinity)} available",
                "sample": f"{n} decode layers (T=4 each) of the benchmark's 16, full layer each, "
                          f"{cpu_time:.1f}s of single-threaded oracle time"}
         log(f"cpu oracle: {cpu['value']:.3g} layer-tokens/s over {n} layers ({cpu_time:.1f}s)")
