@@ -488,14 +488,11 @@ def bench_stack(args, stream):
     out = {"layers": n}
     for s, lg, tag in ((sd, lg_dec, "decode"), (sp, lg_pre, "prefill")):
         h = to_dev(mi.make_h0(s, args.seed))
-        x = torch.empty((s.T, s.H), dtype=torch.int16, device="cuda")
-        ws = sm.alloc_workspace(sm.workspace_bytes(s.T, s.E, s.k, s.H, s.I), "cuda")
+        ws = sm.alloc_workspace(sm.residual_workspace_bytes(s.T, s.E, s.k, s.H, s.I), "cuda")
 
         def step(strm):
             for l in range(n):
-                sm.strata_moe_rmsnorm(h, x, 1e-6, stream=strm)
-                sm.strata_moe_layer(weights[l], x, lg[l], s.k, h, accumulate=True, workspace=ws,
-                                    stream=strm)
+                sm.strata_moe_layer_residual(weights[l], h, lg[l], s.k, ws, eps=1e-6, stream=strm)
 
         step(stream)
         steps = args.stack_steps if tag == "decode" else max(1, args.stack_steps // 10)
@@ -521,7 +518,7 @@ def bench_stack(args, stream):
             out[tag] = {"T": s.T, "ms_per_step": ms, "stack_tokens_per_s": s.T / (ms * 1e-3),
                         "steps": steps, "achieved_TFLOPs": tf, "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
         log(f"stack {tag}: {ms:.3f} ms per {n}-layer step, {s.T / (ms * 1e-3):.4g} stack-tokens/s")
-        del h, x, ws
+        del h, ws
     return out
 
 

@@ -24,7 +24,8 @@ CODE_BYTES = {Q2: 8, Q3: 12}
 EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "strata_moe_combine",
            "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
            "strata_moe_router_logits", "strata_moe_shared_expert",
-           "strata_moe_usage_update", "strata_moe_usage_rank",
+           "strata_moe_usage_update", "strata_moe_usage_rank", "strata_moe_layer_residual",
+           "strata_moe_residual_workspace_bytes",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
            "strata_moe_shared_workspace_bytes", "strata_status_string"]
 
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "strata_moe_shared_expert": [vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, sz, vp],
             "strata_moe_usage_update": [vp, i32, i32, i32, vp, vp],
             "strata_moe_usage_rank": [vp, i32, vp, vp],
+            "strata_moe_layer_residual": [W, vp, vp, i32, i32, ctypes.c_float, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.strata_moe_permute_workspace_bytes.restype = sz
         L.strata_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.strata_moe_workspace_bytes.restype = sz
+        L.strata_moe_residual_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.strata_moe_residual_workspace_bytes.restype = sz
         L.strata_moe_shared_workspace_bytes.argtypes = [i32, i32]
         L.strata_moe_shared_workspace_bytes.restype = sz
         L.strata_status_string.argtypes = [ctypes.c_int]
@@ -154,6 +158,10 @@ def permute_workspace_bytes(T: int, E: int, k: int) -> int:
 
 def workspace_bytes(T: int, E: int, k: int, H: int, I: int) -> int:
     return lib().strata_moe_workspace_bytes(T, E, k, H, I)
+
+
+def residual_workspace_bytes(T: int, E: int, k: int, H: int, I: int) -> int:
+    return lib().strata_moe_residual_workspace_bytes(T, E, k, H, I)
 
 
 def shared_workspace_bytes(T: int, I: int) -> int:
@@ -256,3 +264,12 @@ def strata_moe_usage_rank(usage, order, stream=None) -> None:
     E = usage.shape[0]
     _check("strata_moe_usage_rank", lib().strata_moe_usage_rank(_p(usage), E, _p(order),
                                                                 _stream(stream)))
+
+
+def strata_moe_layer_residual(w: Weights, h, logits, k, workspace, eps=1e-6, stream=None) -> None:
+    """h (fp32 [T][H]) <- h + MoE(RMSNorm(h))."""
+    cw = w.c_struct()
+    _check("strata_moe_layer_residual", lib().strata_moe_layer_residual(
+        ctypes.byref(cw), _p(h), _p(logits), h.shape[0], k, eps, _p(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))

@@ -256,7 +256,8 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x, 
     return STRATA_ERR_INVALID_ARGUMENT;
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
   if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(strata::launch_decode(w->fmt, x, logits, T, E, k, H, I, w->gate_codes, w->up_codes,
+  return from_hip(strata::launch_decode(w->fmt, x, nullptr, 0.0f, logits, T, E, k, H, I,
+                                        w->gate_codes, w->up_codes,
                                         w->down_codes, w->gate_scales, w->up_scales, w->down_scales,
                                         y, accumulate, opt_topk_ids, opt_topk_w, workspace, stream));
 }
@@ -293,7 +294,8 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
     hipError_t e = hipSuccess;
     for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
       const int32_t ts = T / n + (i < T % n ? 1 : 0);
-      e = strata::launch_decode(w->fmt, x + (size_t)t0 * H, logits + (size_t)t0 * E, ts, E, k, H, I,
+      e = strata::launch_decode(w->fmt, x + (size_t)t0 * H, nullptr, 0.0f, logits + (size_t)t0 * E, ts,
+                                E, k, H, I,
                                 w->gate_codes, w->up_codes, w->down_codes, w->gate_scales,
                                 w->up_scales, w->down_scales, y + (size_t)t0 * H, accumulate,
                                 opt_topk_ids ? opt_topk_ids + (size_t)t0 * k : nullptr,
@@ -333,6 +335,40 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
                                 w->down_codes, w->down_scales, E, H, I, p.expert_out, stream);
   if (e == hipSuccess) e = strata::launch_combine(p.expert_out, rw, T, k, H, y, accumulate, stream);
   return from_hip(e);
+}
+
+size_t strata_moe_residual_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+  const size_t layer = strata_moe_workspace_bytes(T, E, k, H, I);
+  if (layer == 0) return 0;
+  return round_up(layer) + round_up((size_t)T * H * 2);
+}
+
+strata_status strata_moe_layer_residual(const strata_moe_weights* w, float* h, const float* logits,
+                                        int32_t T, int32_t k, float eps, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  st = check_route_shape(T, w->num_experts, k);
+  if (st != STRATA_OK) return st;
+  if (!(eps >= 0.0f)) return STRATA_ERR_INVALID_ARGUMENT;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[3] = {h, logits, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (workspace_bytes < strata_moe_residual_workspace_bytes(T, E, k, H, I))
+    return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  if (T <= kMaxDecodeT && strata::decode_fits(T, E, k, H, I))  // RMSNorm inside the first kernel
+    return from_hip(strata::launch_decode(w->fmt, nullptr, h, eps, logits, T, E, k, H, I,
+                                          w->gate_codes, w->up_codes, w->down_codes,
+                                          w->gate_scales, w->up_scales, w->down_scales, h, 1,
+                                          nullptr, nullptr, workspace, stream));
+  const size_t layer = round_up(strata_moe_workspace_bytes(T, E, k, H, I));
+  uint16_t* x = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + layer);
+  hipError_t e = strata::launch_rmsnorm(h, T, H, eps, x, stream);
+  if (e != hipSuccess) return STRATA_ERR_HIP;
+  return strata_moe_layer(w, x, logits, T, k, h, 1, nullptr, nullptr, nullptr, nullptr, nullptr,
+                          workspace, layer, stream);
 }
 
 strata_status strata_moe_pack_matrix(int32_t fmt, int32_t n_mat, int32_t rows, int32_t K,

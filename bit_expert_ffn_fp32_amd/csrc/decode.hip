@@ -325,16 +325,30 @@ STRATA_DEVICE void item_range(int n_items, int& begin, int& end) {
 
 // ---------------------------------------------------------------------------------------------
 // K1: route + gate/up GEMV + SiLU*mul.  Items (distinct expert d, block of 16 rows of I).
+//
+// RES (layer stacks): the input is the residual stream h (fp32) and x = bf16(h / rms(h)) is formed
+// here.  While the routing waves route, every other thread loads its blocks of h (at most two:
+// T * H / 32 <= 1024 blocks over >= 512 threads), keeps them in registers and leaves each block's
+// sum of squares in LDS.  After the routing barrier a thread sums its token's block sums (in block
+// order, four interleaved partial sums), scales and stages its blocks, and one more barrier
+// publishes x.
 
-template <int FMT, int MC>
+// fp32 pair -> two bf16 (round to nearest even) in one word, low half first.
+STRATA_DEVICE uint32_t bf16_pair(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+template <int FMT, int MC, bool RES>
 __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ logits, int T, int E, int k, int H,
+    const uint16_t* __restrict__ x, const float* __restrict__ h_res, float eps,
+    const float* __restrict__ logits, int T, int E, int k, int H,
     int I, const uint8_t* __restrict__ gate_codes, const uint8_t* __restrict__ up_codes,
     const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales,
     uint16_t* __restrict__ a16 /* [S][I] bf16 */, int* __restrict__ ids_ws,
     float* __restrict__ w_ws, GlobalTable* __restrict__ gt) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ RouteTable rt;
+  __shared__ __align__(16) float part[RES ? kDecMaxT * 128 : 4];  // block sums of squares of h
   const int tid = threadIdx.x, S = T * k;
   const int nb = H / 32, nblk = T * nb, nchunk = H / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
@@ -343,8 +357,32 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   table_clear<kUpThreads>(rt, S, E, scratch);  // visible after the barrier below
   // waves 0 .. T-1 route one token each while the other waves stage x
   const int nr = T * 64;
+  f32x4_t hv[RES ? 2 : 1][8];  // RES: this thread's blocks of h (blocks tid - nr + j (1024 - nr))
   if (tid < nr) {
     route_token(logits, tid >> 6, E, k, rt.ids, rt.w);
+  } else if constexpr (RES) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int b = tid - nr + j * (kUpThreads - nr);
+      if (b < nblk) {
+        const int t = b / nb, blk = b - t * nb;
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(h_res + (size_t)t * H + blk * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[j][i] = src[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int b = tid - nr + j * (kUpThreads - nr);
+      if (b < nblk) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ss = __builtin_fmaf(hv[j][i][q], hv[j][i][q], ss);
+        part[b] = ss;
+      }
+    }
   } else {
     for (int b = tid - nr; b < nblk; b += kUpThreads - nr) {
       u32x4_t v[4];
@@ -399,10 +437,41 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
       }
     }
   };
+  // RES: stage x = bf16(h / rms) from registers while the first weights load; where the held
+  // blocks and one item's weight registers do not fit together (Q3 with >= 3 chunks per lane, Q2
+  // with 4) the blocks are staged before the first loads instead.
+  constexpr bool kStageEarly = FMT == 3 ? MC >= 3 : MC >= 4;
+  auto stage_res = [&]() {
+    if (tid >= nr) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int b = tid - nr + j * (kUpThreads - nr);
+        if (b < nblk) {
+          const int t = b / nb, blk = b - t * nb;
+          const f32x4_t* pt = reinterpret_cast<const f32x4_t*>(part + t * nb);
+          f32x4_t acc = pt[0];
+          for (int q = 1; q < nb / 4; ++q) acc += pt[q];
+          const float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+          const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+          u32x4_t v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4_t p = hv[j][2 * i], q = hv[j][2 * i + 1];
+            v[i] = u32x4_t{bf16_pair(p[0] * inv, p[1] * inv), bf16_pair(p[2] * inv, p[3] * inv),
+                           bf16_pair(q[0] * inv, q[1] * inv), bf16_pair(q[2] * inv, q[3] * inv)};
+          }
+          stage_block<FMT>(v, pairs + t * rs, cs + t * nb, blk);
+        }
+      }
+    }
+    __syncthreads();
+  };
+  if constexpr (RES && kStageEarly) stage_res();
   // (no barrier after the first weight loads: they are accepted only as fast as data returns, so
   // a barrier would hold every wave until the whole first batch had been issued)
   it += grp;
   if (it < end) load_item(it, gu[0]);
+  if constexpr (RES && !kStageEarly) stage_res();
   if constexpr (kTwo) {
     if (it + kGroups < end) load_item(it + kGroups, gu[kTwo ? 1 : 0]);
     for (; it < end; it += 2 * kGroups) {
@@ -571,15 +640,18 @@ static void allow_lds(K kernel) {
 
 template <int F>
 static void allow_all_decode_lds() {
-  allow_lds(decode_up_kernel<F, 1>); allow_lds(decode_up_kernel<F, 2>);
-  allow_lds(decode_up_kernel<F, 3>); allow_lds(decode_up_kernel<F, 4>);
+  allow_lds(decode_up_kernel<F, 1, false>); allow_lds(decode_up_kernel<F, 2, false>);
+  allow_lds(decode_up_kernel<F, 3, false>); allow_lds(decode_up_kernel<F, 4, false>);
+  allow_lds(decode_up_kernel<F, 1, true>); allow_lds(decode_up_kernel<F, 2, true>);
+  allow_lds(decode_up_kernel<F, 3, true>); allow_lds(decode_up_kernel<F, 4, true>);
   allow_lds(decode_down_kernel<F, 1, 4>); allow_lds(decode_down_kernel<F, 2, 4>);
   allow_lds(decode_down_kernel<F, 3, 4>); allow_lds(decode_down_kernel<F, 4, 4>);
   allow_lds(decode_down_kernel<F, 2, 16>); allow_lds(decode_down_kernel<F, 3, 16>);
   allow_lds(decode_down_kernel<F, 4, 16>);
 }
 
-hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T, int E, int k,
+hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float eps,
+                         const float* logits, int T, int E, int k,
                          int H, int I, const void* gate_codes, const void* up_codes,
                          const void* down_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, const uint16_t* down_scales, float* y,
@@ -606,8 +678,14 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T,
   const int lpu = nch_dn <= 16 ? 4 : 16;                 // lanes per down row
   const int mc_dn = (nch_dn + lpu - 1) / lpu;            // 1..4
 #define STRATA_UP(F, M)                                                                          \
-  decode_up_kernel<F, M><<<kGrid, kUpThreads, lds_up, s>>>(x, logits, T, E, k, H, I, gc, uc,   \
-                                                              gate_scales, up_scales, a16, ids, w, gt)
+  do {                                                                                           \
+    if (h_res)                                                                                   \
+      decode_up_kernel<F, M, true><<<kGrid, kUpThreads, lds_up, s>>>(                            \
+          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a16, ids, w, gt); \
+    else                                                                                         \
+      decode_up_kernel<F, M, false><<<kGrid, kUpThreads, lds_up, s>>>(                           \
+          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a16, ids, w, gt); \
+  } while (0)
 #define STRATA_DN(F, M, L)                                                                       \
   decode_down_kernel<F, M, L><<<kGrid, kDnThreads, lds_dn, s>>>(a16, gt, w, T, E, k, H, I, dc,  \
                                                                    down_scales, y, accumulate)

@@ -69,8 +69,10 @@ hipError_t launch_shared_expert(const uint16_t* x, const uint16_t* wg, const uin
 hipError_t launch_usage_update(const int* ids, int64_t S, int E, uint64_t* usage, hipStream_t s);
 hipError_t launch_usage_rank(const uint64_t* usage, int E, int* order, hipStream_t s);
 
-// Decode path (T <= 8).
-hipError_t launch_decode(int fmt, const uint16_t* x, const float* logits, int T, int E, int k,
+// Decode path (T <= 8).  With h_res != NULL the input is the residual stream h (fp32 [T][H]) and
+// x = bf16(h / sqrt(mean(h^2) + eps)) is formed in the first kernel (x is then unused).
+hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float eps,
+                         const float* logits, int T, int E, int k,
                          int H, int I, const void* gate_codes, const void* up_codes,
                          const void* down_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, const uint16_t* down_scales, float* y,

@@ -212,6 +212,21 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * One layer of a stack with a residual stream: h <- h + MoE(RMSNorm(h)), with
+ * RMSNorm(h)[t] = bf16_RNE(h[t] / sqrt(mean_i h[t][i]^2 + eps)) (unit gain, as strata_moe_rmsnorm).
+ * The pages' model runs 48 such MoE layers ("Strata vs Llama.cpp vs vLLM", transcript at 08:23);
+ * the pre-norm residual form is this library's definition.  For T <= 8 (decode limits as
+ * strata_moe_decode) the normalisation is formed inside the decode path's first kernel (no separate
+ * launch); otherwise strata_moe_rmsnorm into the workspace, then strata_moe_layer accumulating into h.
+ *   h      fp32 [T][H] (read and written)
+ *   logits fp32 [T][E] (read)
+ * Workspace: at least strata_moe_residual_workspace_bytes(T, E, k, H, I).  eps >= 0.
+ */
+strata_status strata_moe_layer_residual(const strata_moe_weights* w, float* h, const float* logits,
+                                        int32_t T, int32_t k, float eps, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Weight repack, row-major -> tiled (see the layouts above), for n_mat matrices of rows x K
  * stored back to back (e.g. all E gate matrices: n_mat = E, rows = I, K = H).  A one-time
  * load step; the compute entry points read only the tiled layout.
@@ -292,6 +307,7 @@ strata_status strata_moe_usage_rank(const uint64_t* usage, int32_t E, int32_t* o
 size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k);
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
 size_t strata_moe_shared_workspace_bytes(int32_t T, int32_t I);
+size_t strata_moe_residual_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
 
 /* Static string for a status code (host function; never NULL). */
 const char* strata_status_string(strata_status status);

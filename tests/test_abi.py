@@ -90,6 +90,22 @@ def test_weights_validation(L):
                                    None) == WS
 
 
+def test_layer_residual_validation(L):
+    ws = L.strata_moe_residual_workspace_bytes(4, 512, 10, 3072, 768)
+    assert ws >= L.strata_moe_workspace_bytes(4, 512, 10, 3072, 768) + 4 * 3072 * 2
+    assert L.strata_moe_residual_workspace_bytes(-1, 512, 10, 3072, 768) == 0
+    call = lambda w, h=A, T=4, k=10, eps=1e-6, wsb=ws: L.strata_moe_layer_residual(
+        ctypes.byref(w), h, A, T, k, ctypes.c_float(eps), A, wsb, None)
+    assert call(weights(), wsb=ws - 1) == WS
+    assert call(weights(), eps=-1.0) == INVAL
+    assert call(weights(), eps=float("nan")) == INVAL
+    assert call(weights(), h=MIS) == INVAL
+    assert call(weights(), h=None) == INVAL
+    assert call(weights(E=8), k=9) == INVAL
+    assert call(weights(fmt=4)) == INVAL
+    assert call(weights(), T=0, h=None) == OK       # T = 0: no-op
+
+
 def test_combine_and_rmsnorm_validation(L):
     assert L.strata_moe_combine(A, A, 4, 10, 3072, None, 0, None) == INVAL
     assert L.strata_moe_combine(A, A, 4, 10, 3071, A, 0, None) == UNSUP

@@ -238,6 +238,44 @@ def test_zero_tokens_is_noop():
 
 
 # ---------------------------------------------------------------------------------------------
+# Residual layer of a stack: h <- h + MoE(RMSNorm(h))
+
+
+@pytest.mark.parametrize("s", [shape("r1", T=1), shape("r4", T=4, H=512, E=32, k=4, I=256),
+                               shape("r8_q3", T=8, fmt=3), shape("r3_e1", T=3, E=1, k=1),
+                               shape("r9", T=9), shape("r40", T=40, fmt=3), shape("r70", T=70)],
+                         ids=lambda s: s.name)
+def test_layer_residual_against_oracle(s):
+    log(f"layer residual {s}")
+    L = Layer(s)
+    rng = np.random.default_rng(s.T + 31)
+    h_np = (rng.standard_normal((s.T, s.H)) * 2.5).astype(np.float32)
+    h = to_dev(h_np)
+    ws = sm.alloc_workspace(sm.residual_workspace_bytes(s.T, s.E, s.k, s.H, s.I), dev())
+    sm.strata_moe_layer_residual(L.w, h, L.logits, s.k, ws, eps=1e-6)
+    torch.cuda.synchronize()
+    got = h.cpu().numpy().astype(np.float64) - h_np.astype(np.float64)
+    x_ref = oracle.rmsnorm(h_np, 1e-6)
+    y_ref = oracle.layer(L.w_np, x_ref, L.l_np, s.k)
+    err = rel_l2_rows(got, y_ref)
+    path = "fused decode" if s.T <= 8 else "rmsnorm + layer"
+    log(f"  max rel-L2 {err.max():.3e} ({path})")
+    assert err.max() <= TOL_REL_L2
+    # the same step with the normalisation as its own call, then the layer accumulating into h
+    h2 = to_dev(h_np)
+    x = torch.empty((s.T, s.H), dtype=torch.int16, device=dev())
+    sm.strata_moe_rmsnorm(h2, x, 1e-6)
+    sm.strata_moe_layer(L.w, x, L.logits, s.k, h2, accumulate=True, workspace=L.workspace())
+    torch.cuda.synchronize()
+    got2 = h2.cpu().numpy().astype(np.float64) - h_np.astype(np.float64)
+    assert rel_l2_rows(got, got2).max() <= TOL_REL_L2
+    h3 = to_dev(h_np)
+    sm.strata_moe_layer_residual(L.w, h3, L.logits, s.k, ws, eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h3), "second call differs"
+
+
+# ---------------------------------------------------------------------------------------------
 # RMSNorm
 
 
