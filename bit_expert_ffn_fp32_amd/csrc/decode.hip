@@ -42,24 +42,26 @@ constexpr int kDecMaxT = 8;
 constexpr int kDecMaxS = 128;      // T * k <= 8 * 16
 constexpr int kDecMaxR = 16;       // rows of H per K2 workgroup (H <= 4096)
 constexpr int kUpRows = 16;        // rows of I per K1 item (4 per wave, 16 lanes per row)
+constexpr int kDnPieces = 9;       // K2: 16-byte pieces of staged a per thread (<= 144 KB of LDS)
 
 
 // Routes token t (this wave) into LDS.
 template <int NPL>
 STRATA_DEVICE void route_token_npl(const float* __restrict__ logits, int t, int E, int k,
-                                   int* ids_s, float* w_s) {
+                                   int* ids_s, float* w_s, uint64_t* sel) {
   TokenKeys<NPL> tk;
   load_token_logits<NPL>(logits + (size_t)t * E, E, tk);
-  select_token_wave<NPL>(tk, E, k, ids_s + t * k, w_s + t * k);
+  select_token_wave<NPL>(tk, E, k, ids_s + t * k, w_s + t * k, sel);
 }
 
+// sel: this wave's 80 uint64 of selection LDS.
 STRATA_DEVICE void route_token(const float* __restrict__ logits, int t, int E, int k, int* ids_s,
-                               float* w_s) {
-  if (E <= 64) route_token_npl<1>(logits, t, E, k, ids_s, w_s);
-  else if (E <= 128) route_token_npl<2>(logits, t, E, k, ids_s, w_s);
-  else if (E <= 256) route_token_npl<4>(logits, t, E, k, ids_s, w_s);
-  else if (E <= 512) route_token_npl<8>(logits, t, E, k, ids_s, w_s);
-  else route_token_npl<16>(logits, t, E, k, ids_s, w_s);
+                               float* w_s, uint64_t* sel) {
+  if (E <= 64) route_token_npl<1>(logits, t, E, k, ids_s, w_s, sel);
+  else if (E <= 128) route_token_npl<2>(logits, t, E, k, ids_s, w_s, sel);
+  else if (E <= 256) route_token_npl<4>(logits, t, E, k, ids_s, w_s, sel);
+  else if (E <= 512) route_token_npl<8>(logits, t, E, k, ids_s, w_s, sel);
+  else route_token_npl<16>(logits, t, E, k, ids_s, w_s, sel);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -344,11 +346,12 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
     const float* __restrict__ logits, int T, int E, int k, int H,
     int I, const uint8_t* __restrict__ gate_codes, const uint8_t* __restrict__ up_codes,
     const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales,
-    uint16_t* __restrict__ a16 /* [S][I] bf16 */, int* __restrict__ ids_ws,
+    uint32_t* __restrict__ a_st /* [S][I/2] staged a, unpadded */, int* __restrict__ ids_ws,
     float* __restrict__ w_ws, GlobalTable* __restrict__ gt) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ RouteTable rt;
   __shared__ __align__(16) float part[RES ? kDecMaxT * 128 : 4];  // block sums of squares of h
+  __shared__ __align__(16) uint64_t sel[kDecMaxT][80];  // the routing waves' selection LDS
   const int tid = threadIdx.x, S = T * k;
   const int nb = H / 32, nblk = T * nb, nchunk = H / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   const int nr = T * 64;
   f32x4_t hv[RES ? 2 : 1][8];  // RES: this thread's blocks of h (blocks tid - nr + j (1024 - nr))
   if (tid < nr) {
-    route_token(logits, tid >> 6, E, k, rt.ids, rt.w);
+    route_token(logits, tid >> 6, E, k, rt.ids, rt.w, sel[tid >> 6]);
   } else if constexpr (RES) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -423,17 +426,25 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
     load_row_chunks<FMT, MC>(rr[1], tiled_row_codes<FMT>(up_codes, row, nchunk),
                              tiled_row_scales(up_scales, row, nchunk), nchunk, c, 16);
   };
+  // a = SiLU(g) u, rounded to bf16, goes out already in K2's staged layout without the chunk
+  // padding: row n = 16 q + rsub is value rsub of word q & 3 of chunk q >> 2, i.e. half rsub >> 3
+  // of pair m = rsub & 7, multiplied by that pair's power of two (exact).
+  const int m_a = rsub & 7;
+  const float sc_a = FMT == 2 ? (m_a % 3 == 0 ? 64.0f : m_a % 3 == 1 ? 16.0f : 4.0f) : 2.0f;
   auto compute_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
-    const int d = item / blocks, n = (item % blocks) * kUpRows + rsub;
+    const int d = item / blocks, q = item % blocks;
     const int Tp = rt.dtp[d];
     for (int tt = 0; tt < Tp; ++tt) {
       const int t = rt.dtok[d][tt];
       float acc[2];
       row_dots<FMT, MC, 2>(rr, nchunk, c, 16, pairs + t * rs, cs + t * nb, acc);
       const float gs = sum16(acc[0]), us = sum16(acc[1]);
+      const int slot = rt.dslot[d][tt];
+      const float a = gs / (1.0f + expf(-gs)) * us;
+      const float xa = __uint_as_float((uint32_t)f32_to_bf16(a) << 16);
       if (c == 0) {
-        const float a = gs / (1.0f + expf(-gs)) * us;
-        a16[(size_t)rt.dslot[d][tt] * I + n] = f32_to_bf16(a);
+        uint32_t* word = a_st + (size_t)slot * (I / 2) + 32 * (q >> 2) + 8 * (q & 3) + m_a;
+        reinterpret_cast<uint16_t*>(word)[rsub >> 3] = (uint16_t)(__float_as_uint(xa * sc_a) >> 16);
       }
     }
   };
@@ -495,7 +506,8 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
 
 template <int FMT, int MC, int LPU>
 __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
-    const uint16_t* __restrict__ a16, const GlobalTable* __restrict__ gt, const float* __restrict__ w_ws,
+    const uint32_t* __restrict__ a_st, const GlobalTable* __restrict__ gt,
+    const float* __restrict__ w_ws,
     int T, int E, int k, int H, int I, const uint8_t* __restrict__ down_codes,
     const uint16_t* __restrict__ down_scales, float* __restrict__ y, int accumulate) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -506,22 +518,21 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
   const int nb = I / 32, nchunk = I / 64, rs = kChunkDwords * nchunk;
   uint32_t* pairs = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)S * rs * 4);
-  // Waves 0-7 stage every slot's intermediate a while waves 8-15 fetch the routing table, then
-  // start their weight loads at once; an LDS counter (not a barrier, which would hold everyone
+  // Every thread loads its 16-byte pieces of the slots' staged a (K1 wrote it in the layout
+  // below, without the chunk padding), while waves 8-15 also fetch the routing table.  After the
+  // barrier each wave writes its pieces to LDS and the block constants C = sum coef x (a block is
+  // four consecutive pieces, so four consecutive lanes: a quad sum), counts itself in an LDS
+  // counter and starts its weight loads; the counter (not a barrier, which would hold everyone
   // behind the throttled weight loads) tells the waves when the staged a is complete.
   constexpr int kStage = 512;
   __shared__ int staged_waves;
-  const int nsb = S * nb;
-  u32x4_t av[4][4];
-  if (tid < kStage) {
+  const int ppr = I / 8, ncp = S * ppr;  // pieces per row; pieces
+  const u32x4_t* src_st = reinterpret_cast<const u32x4_t*>(a_st);
+  u32x4_t cv[kDnPieces];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = min(tid + kStage * i, nsb - 1);
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) av[i][v] = src[v];
-    }
-  } else {
+  for (int i = 0; i < kDnPieces; ++i)
+    if (tid + kDnThreads * i < ncp) cv[i] = src_st[tid + kDnThreads * i];
+  if (tid >= kStage) {
     const int q = tid - kStage;
     if (q == 0) { rt.nd = gt->nd; staged_waves = 0; }
     if (q < S) {
@@ -551,25 +562,41 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
     load_row_chunks<FMT, MC>(rr[1], tiled_row_codes<FMT>(down_codes, base + r1, nchunk),
                              tiled_row_scales(down_scales, base + r1, nchunk), nchunk, j, LPU);
   };
-  if (tid < kStage) {
+  {
+    // piece q: row q / ppr, chunk (q % ppr) / 8, dwords 4 (q % 8) .. + 3 of the chunk, pairs
+    // m = 4 (q % 2) .. + 3 of its word; the stored values are x * s(m), so coef(m) x is
+    // (coef(m) / s(m)) times them, exactly
+    const int m0 = 4 * (tid & 1);
+    float f[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = tid + kStage * i;
-      if (b < nsb) stage_block<FMT>(av[i], pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + e;
+      f[e] = FMT == 2 ? (m % 3 == 0 ? 2.0f + 1.5f / 64.0f : m % 3 == 1 ? 2.0f + 1.5f / 16.0f
+                                                                     : 2.0f + 1.5f / 4.0f)
+                      : 11.5f / 2.0f;
     }
-    for (int b = tid + 4 * kStage; b < nsb; b += kStage) {
-      u32x4_t v[4];
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a16 + (size_t)(b / nb) * I + (b % nb) * 32);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = src[i];
-      stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+    for (int i = 0; i < kDnPieces; ++i) {
+      const int q = tid + kDnThreads * i;
+      if (q - (q & 3) < ncp) {  // the whole quad is in range or out (ncp is a multiple of 4)
+        const int row = q / ppr, pr = q - row * ppr;
+        *reinterpret_cast<u32x4_t*>(pairs + row * rs + kChunkDwords * (pr >> 3) + 4 * (pr & 7)) = cv[i];
+        float c = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c = __builtin_fmaf(f[e], __uint_as_float(cv[i][e] << 16), c);
+          c = __builtin_fmaf(f[e], __uint_as_float(cv[i][e] & 0xFFFF0000u), c);
+        }
+        c = sum4(c);
+        if ((q & 3) == 0) cs[q >> 2] = c;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if ((tid & 63) == 0) atomicAdd(&staged_waves, 1);
   }
   if (g < U) load_unit(g, wr[0]);
   if (g + kGroups < U) load_unit(g + kGroups, wr[1]);
-  while (__hip_atomic_load(&staged_waves, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kStage / 64)
+  while (__hip_atomic_load(&staged_waves, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kDnThreads / 64)
     __builtin_amdgcn_s_sleep(1);
   auto compute_unit = [&](int u, RowChunks<FMT, MC> (&rr)[2]) {
     const int d = u / RH;
@@ -621,10 +648,14 @@ constexpr size_t kDecLdsLimit = 160 * 1024 - 16 * 1024;  // dynamic LDS beside t
 bool decode_fits(int T, int E, int k, int H, int I) {
   if (T < 1 || T > kDecMaxT || T * k > kDecMaxS || E > 1024) return false;
   if (H % 256 || H > 4096 || I % 128 || I > 4096) return false;
-  return up_lds_bytes(T, E, H) <= kDecLdsLimit && dn_lds_bytes(T, E, k, I) <= kDecLdsLimit;
+  // (K2 holds every slot's staged a in registers on its way to LDS: <= kDnPieces pieces a thread)
+  const size_t pieces = (size_t)T * k * I / 8;
+  return up_lds_bytes(T, E, H) <= kDecLdsLimit && dn_lds_bytes(T, E, k, I) <= kDecLdsLimit &&
+         pieces <= (size_t)kDnPieces * kDnThreads;
 }
 
-// Workspace: ids [S] int32 | w [S] fp32 | routing table | a [S][I] bf16
+// Workspace: ids [S] int32 | w [S] fp32 | routing table | staged a [S][I/2] (K2's LDS layout
+// without the chunk padding)
 size_t decode_workspace_bytes(int T, int E, int k, int H, int I) {
   (void)E; (void)H;
   const size_t S = (size_t)T * k;
@@ -668,7 +699,7 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float e
   p += up(S * 4);
   GlobalTable* gt = reinterpret_cast<GlobalTable*>(p);
   p += up(sizeof(GlobalTable));
-  uint16_t* a16 = reinterpret_cast<uint16_t*>(p);
+  uint32_t* a_st = reinterpret_cast<uint32_t*>(p);
   const uint8_t* gc = static_cast<const uint8_t*>(gate_codes);
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
@@ -681,14 +712,14 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float e
   do {                                                                                           \
     if (h_res)                                                                                   \
       decode_up_kernel<F, M, true><<<kGrid, kUpThreads, lds_up, s>>>(                            \
-          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a16, ids, w, gt); \
+          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a_st, ids, w, gt); \
     else                                                                                         \
       decode_up_kernel<F, M, false><<<kGrid, kUpThreads, lds_up, s>>>(                           \
-          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a16, ids, w, gt); \
+          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a_st, ids, w, gt); \
   } while (0)
 #define STRATA_DN(F, M, L)                                                                       \
-  decode_down_kernel<F, M, L><<<kGrid, kDnThreads, lds_dn, s>>>(a16, gt, w, T, E, k, H, I, dc,  \
-                                                                   down_scales, y, accumulate)
+  decode_down_kernel<F, M, L><<<kGrid, kDnThreads, lds_dn, s>>>(a_st, gt, w, T, E, k, H, I, \
+                                                                   dc, down_scales, y, accumulate)
 #define STRATA_DEC(F)                                                                            \
   switch (mc_up) { case 1: STRATA_UP(F, 1); break; case 2: STRATA_UP(F, 2); break;              \
                    case 3: STRATA_UP(F, 3); break; default: STRATA_UP(F, 4); break; }           \

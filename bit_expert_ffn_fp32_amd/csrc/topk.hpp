@@ -102,13 +102,102 @@ STRATA_DEVICE void sort_lane_desc(uint64_t (&c)[NPL]) {
           }
 }
 
-// Top-k of one token by one wave: k rounds of "largest remaining logit, equal logits to the lower
-// expert index"; weights = softmax over the k kept logits (the router kernel's rule).  Each lane
-// sorts its own entries once; a round takes the maximum of the lanes' heads and the winning lane
-// pops its head.
+// Orders this wave's LDS accesses across its lanes.  The LDS executes one wave's instructions in
+// issue order, so keeping the compiler from moving accesses across this point suffices (wavefront
+// scope: no wait is emitted).
+STRATA_DEVICE void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Top-k selection over the wave's per-lane sorted entries (composite keys, all distinct among real
+// entries, 0 = empty).  On lane j < k it leaves the j-th largest key's logit key and expert.
+//
+// Threshold and rank: the k-th largest of the 64 lane heads, tau, is at most the k-th largest
+// entry overall (k heads are >= tau), so the top k are among the entries >= tau: usually k to
+// k + 5 of them, at most k * NPL.  They are gathered in LDS and each one's rank among them is
+// counted; ranks 0..k-1 are the selection.  Returns false (LDS untouched beyond this wave's 80
+// entries, c unchanged) when more than 64 entries pass, left to select_rounds.  Real heads number
+// min(E, 64) >= k and are distinct, so exactly one lane's head has k - 1 heads above it.
+template <int NPL>
+STRATA_DEVICE bool select_threshold(const uint64_t (&c)[NPL], int k, uint64_t* lds,
+                                    uint32_t& my_key, int& my_i) {
+  typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const uint64_t h = c[0];
+  lds[lane] = h;
+  wave_lds_sync();
+  int above = 0;
+#pragma unroll 8
+  for (int j = 0; j < 64; j += 2) {
+    const u64x2_t p = *reinterpret_cast<const u64x2_t*>(lds + j);
+    above += (p[0] > h) + (p[1] > h);
+  }
+  const int tl = __ffsll((unsigned long long)__ballot(above == k - 1)) - 1;
+  const uint64_t tau = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(h >> 32), tl) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)h, tl);
+  wave_lds_sync();
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {  // lanes are sorted: entry i passes only where entry i - 1 did
+    const bool in = c[i] >= tau;
+    const uint64_t b = __ballot(in);
+    if (b == 0) break;
+    const int cnt = __popcll(b);
+    if (n + cnt > 64) return false;
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+    if (in) lds[n + below] = c[i];
+    n += cnt;
+  }
+  wave_lds_sync();
+  const uint64_t mine = lds[lane < n ? lane : 0];
+  int r = 0;
+  for (int j = 0; j < n; ++j) r += lds[j] > mine;
+  wave_lds_sync();
+  if (lane < n && r < k) lds[64 + r] = mine;
+  wave_lds_sync();
+  const uint64_t sel = lds[64 + (lane < k ? lane : 0)];
+  my_key = lane < k ? (uint32_t)(sel >> 32) : 0u;
+  my_i = lane < k ? (int)~(uint32_t)sel : 0;
+  return true;
+}
+
+// The same selection by k rounds of a wave-wide arg-max over the lanes' heads, the winning lane
+// popping its head (c is consumed).
+template <int NPL>
+STRATA_DEVICE void select_rounds(uint64_t (&c)[NPL], int k, uint32_t& my_key, int& my_i) {
+  const int lane = threadIdx.x & 63;
+  my_key = 0;
+  my_i = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t hk = (uint32_t)(c[0] >> 32);
+    const uint32_t m = wave_max_u32(hk);
+    const bool cand = hk == m;
+    const uint64_t ball = __ballot(cand);
+    int win;
+    if (__popcll(ball) == 1) {  // the usual case: one lane holds the maximum
+      const int wl = __ffsll((unsigned long long)ball) - 1;
+      win = (int)~(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c[0], wl);
+    } else {                    // equal logits in several lanes: lowest expert index
+      win = (int)~wave_max_u32(cand ? (uint32_t)c[0] : 0u);
+    }
+    if (lane == j) { my_key = m; my_i = win; }
+    const bool pop = lane == (win & 63);
+#pragma unroll
+    for (int i = 0; i + 1 < NPL; ++i) c[i] = pop ? c[i + 1] : c[i];
+    c[NPL - 1] = pop ? 0ull : c[NPL - 1];
+  }
+}
+
+// Top-k of one token by one wave: the k largest logits, equal logits to the lower expert index;
+// weights = softmax over the k kept logits (the router kernel's rule).  Each lane sorts its own
+// entries once, then select_threshold (select_rounds where it declines).  lds: 80 uint64 of LDS
+// (16-byte aligned) used by this wave alone.
 template <int NPL>
 STRATA_DEVICE void select_token_wave(TokenKeys<NPL>& tk, int E, int k, int* ids_out,
-                                     float* w_out) {
+                                     float* w_out, uint64_t* lds) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -116,26 +205,9 @@ STRATA_DEVICE void select_token_wave(TokenKeys<NPL>& tk, int E, int k, int* ids_
     tk.c[i] = e < E ? ((uint64_t)route_key(tk.v[i]) << 32) | (uint32_t)~e : 0ull;
   }
   sort_lane_desc<NPL>(tk.c);
-  uint32_t my_key = 0;
-  int my_i = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t hk = (uint32_t)(tk.c[0] >> 32);
-    const uint32_t m = wave_max_u32(hk);
-    const bool cand = hk == m;
-    const uint64_t ball = __ballot(cand);
-    int win;
-    if (__popcll(ball) == 1) {  // the usual case: one lane holds the maximum
-      const int wl = __ffsll((unsigned long long)ball) - 1;
-      win = (int)~(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)tk.c[0], wl);
-    } else {                    // equal logits in several lanes: lowest expert index
-      win = (int)~wave_max_u32(cand ? (uint32_t)tk.c[0] : 0u);
-    }
-    if (lane == j) { my_key = m; my_i = win; }
-    const bool pop = lane == (win & 63);
-#pragma unroll
-    for (int i = 0; i + 1 < NPL; ++i) tk.c[i] = pop ? tk.c[i + 1] : tk.c[i];
-    tk.c[NPL - 1] = pop ? 0ull : tk.c[NPL - 1];
-  }
+  uint32_t my_key;
+  int my_i;
+  if (!select_threshold<NPL>(tk.c, k, lds, my_key, my_i)) select_rounds<NPL>(tk.c, k, my_key, my_i);
   const float top = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
   const float ex = lane < k ? expf(key_value(my_key) - top) : 0.0f;
   const float den = wave_sum(ex);

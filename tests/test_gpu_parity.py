@@ -40,7 +40,8 @@ def gpu_route(logits_np, k):
 @pytest.mark.parametrize("T,E,k,kind", [
     (16, 64, 4, "normal"), (4, 512, 10, "normal"), (8192, 512, 10, "normal"),
     (2048, 512, 10, "zipf"), (333, 1024, 16, "normal"), (50, 5, 5, "normal"), (7, 1, 1, "normal"),
-    (257, 512, 10, "ties"), (64, 64, 8, "ties2"), (31, 200, 3, "signed_zero")])
+    (257, 512, 10, "ties"), (64, 64, 8, "ties2"), (31, 200, 3, "signed_zero"),
+    (9, 1024, 16, "crowded"), (12, 512, 10, "crowded")])
 def test_route_bit_exact(T, E, k, kind):
     log(f"route T={T} E={E} k={k} {kind}")
     rng = np.random.default_rng(T * 7 + E)
@@ -53,6 +54,14 @@ def test_route_bit_exact(T, E, k, kind):
     elif kind == "ties2":
         logits = np.zeros((T, E), dtype=np.float32)
         logits[::2, 5:] = 1.0
+    elif kind == "crowded":
+        # lanes 0..k-2 of the selecting wave (experts e with e % 64 < k - 1) hold only large
+        # logits and lane k-1 one: more than 64 entries reach the k-th largest lane head, the case
+        # the selection hands to its round-by-round arg-max
+        logits = mi.normal_f32(0, 950 + E, T * E).reshape(T, E)
+        lane = np.arange(E) % 64
+        logits[:, lane < k - 1] += 100.0
+        logits[:, k - 1] += 50.0
     else:
         logits = np.where(rng.random((T, E)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
         logits[:, 17] = -1.0
@@ -213,6 +222,24 @@ def test_layer_against_oracle(s):
     y0 = np.random.default_rng(1).standard_normal((s.T, s.H)).astype(np.float32)
     ya, _, _ = gpu_layer(L, accumulate=True, y0=y0)
     np.testing.assert_allclose(ya, y0 + y, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_decode_crowded_routing(T):
+    """Routing inside the decode kernel where more than 64 entries reach the k-th largest lane
+    head (its round-by-round arg-max) for some tokens, and the threshold path for the others."""
+    s = shape("crowd", T=T, E=512, k=10)
+    L = Layer(s)
+    l = L.l_np.copy()
+    lane = np.arange(s.E) % 64
+    l[::2, lane < s.k - 1] += 100.0
+    l[::2, s.k - 1] += 50.0
+    L.l_np, L.logits = l, to_dev(l)
+    y_ref, ids_ref, w_ref, _, _ = oracle.layer(L.w_np, L.x_np, l, s.k, intermediates=True)
+    y, ids, rw = gpu_layer(L)
+    assert np.array_equal(ids, ids_ref)
+    np.testing.assert_allclose(rw, w_ref, rtol=1e-6, atol=0)
+    assert rel_l2_rows(y, y_ref).max() <= TOL_REL_L2
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
