@@ -217,6 +217,12 @@ def bench_block_decode(args, stream, layers):
         sm.strata_moe_layer(layers[i].w, layers[i].x, logits, s.k, y, workspace=ws, stream=strm)
         shared(i, strm)
 
+    bws = sm.alloc_workspace(sm.block_workspace_bytes(s.T, s.E, s.k, s.H, s.I, s.I), "cuda")
+
+    def block_fused(i, strm):  # one call: three launches
+        sm.strata_moe_block(layers[i].w, layers[i].x, s.k, wr[i], *sh[i], logits, y,
+                            workspace=bws, stream=strm)
+
     def graph_ms(fn):
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -235,6 +241,7 @@ def bench_block_decode(args, stream, layers):
         return event_time_ms(lambda r: g.replay(), reps, stream) / (reps * n)
 
     ms_r, ms_s, ms_b = graph_ms(router), graph_ms(shared), graph_ms(block)
+    ms_f = graph_ms(block_fused)
     r_bytes = s.E * s.H * 2 + s.T * s.H * 2
     s_bytes = 3 * s.H * s.I * 2
     out = {
@@ -242,11 +249,12 @@ def bench_block_decode(args, stream, layers):
         "router_us": ms_r * 1e3, "router_GBs": r_bytes / (ms_r * 1e-3) / 1e9,
         "shared_us": ms_s * 1e3, "shared_GBs": s_bytes / (ms_s * 1e-3) / 1e9,
         "block_us": ms_b * 1e3, "block_tokens_per_s": s.T / (ms_b * 1e-3),
+        "block_one_call_us": ms_f * 1e3, "block_one_call_tokens_per_s": s.T / (ms_f * 1e-3),
         "unit_of_work": "router: E*H*2 + T*H*2 bytes; shared: 3*H*I*2 bytes of bf16 weights",
     }
     log(f"block decode: router {out['router_us']:.2f} us ({out['router_GBs']:.0f} GB/s), shared "
         f"{out['shared_us']:.2f} us ({out['shared_GBs']:.0f} GB/s), router+layer+shared "
-        f"{out['block_us']:.2f} us")
+        f"{out['block_us']:.2f} us, one call (strata_moe_block) {out['block_one_call_us']:.2f} us")
     return out
 
 

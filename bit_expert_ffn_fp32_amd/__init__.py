@@ -25,7 +25,7 @@ EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "s
            "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
            "strata_moe_router_logits", "strata_moe_shared_expert",
            "strata_moe_usage_update", "strata_moe_usage_rank", "strata_moe_layer_residual",
-           "strata_moe_residual_workspace_bytes",
+           "strata_moe_residual_workspace_bytes", "strata_moe_block", "strata_moe_block_workspace_bytes",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
            "strata_moe_shared_workspace_bytes", "strata_status_string"]
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "strata_moe_usage_update": [vp, i32, i32, i32, vp, vp],
             "strata_moe_usage_rank": [vp, i32, vp, vp],
             "strata_moe_layer_residual": [W, vp, vp, i32, i32, ctypes.c_float, vp, sz, vp],
+            "strata_moe_block": [W, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.strata_moe_permute_workspace_bytes.restype = sz
         L.strata_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.strata_moe_workspace_bytes.restype = sz
+        L.strata_moe_block_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.strata_moe_block_workspace_bytes.restype = sz
         L.strata_moe_residual_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.strata_moe_residual_workspace_bytes.restype = sz
         L.strata_moe_shared_workspace_bytes.argtypes = [i32, i32]
@@ -158,6 +161,10 @@ def permute_workspace_bytes(T: int, E: int, k: int) -> int:
 
 def workspace_bytes(T: int, E: int, k: int, H: int, I: int) -> int:
     return lib().strata_moe_workspace_bytes(T, E, k, H, I)
+
+
+def block_workspace_bytes(T: int, E: int, k: int, H: int, I: int, Is: int) -> int:
+    return lib().strata_moe_block_workspace_bytes(T, E, k, H, I, Is)
 
 
 def residual_workspace_bytes(T: int, E: int, k: int, H: int, I: int) -> int:
@@ -271,5 +278,16 @@ def strata_moe_layer_residual(w: Weights, h, logits, k, workspace, eps=1e-6, str
     cw = w.c_struct()
     _check("strata_moe_layer_residual", lib().strata_moe_layer_residual(
         ctypes.byref(cw), _p(h), _p(logits), h.shape[0], k, eps, _p(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def strata_moe_block(w: Weights, x, k, w_router, w_sgate, w_sup, w_sdown, logits, y,
+                     accumulate=False, workspace=None, stream=None) -> None:
+    """logits = x W_r^T; y (+)= routed layer(x, logits) + shared expert(x)."""
+    cw = w.c_struct()
+    _check("strata_moe_block", lib().strata_moe_block(
+        ctypes.byref(cw), _p(x), x.shape[0], k, _p(w_router), _p(w_sgate), _p(w_sup), _p(w_sdown),
+        w_sgate.shape[0], _p(logits), _p(y), int(bool(accumulate)), _p(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream)))

@@ -429,6 +429,56 @@ strata_status strata_moe_shared_expert(const uint16_t* x, const uint16_t* w_gate
                                                static_cast<uint16_t*>(workspace), stream));
 }
 
+size_t strata_moe_block_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
+                                        int32_t Is) {
+  const size_t layer = strata_moe_workspace_bytes(T, E, k, H, I);
+  if (layer == 0 || Is < 1) return 0;
+  return round_up((size_t)T * Is * 2) + round_up(layer);
+}
+
+strata_status strata_moe_block(const strata_moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
+                               const uint16_t* w_router, const uint16_t* w_sgate,
+                               const uint16_t* w_sup, const uint16_t* w_sdown, int32_t Is,
+                               float* logits, float* y, int32_t accumulate, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  st = check_route_shape(T, w->num_experts, k);
+  if (st != STRATA_OK) return st;
+  if (Is < 1) return STRATA_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (Is % 64) return STRATA_ERR_UNSUPPORTED;
+  if ((int64_t)T * Is > INT32_MAX || (int64_t)H * Is > INT32_MAX || (int64_t)T * H > INT32_MAX ||
+      (int64_t)T * E > INT32_MAX)
+    return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  const void* ptrs[8] = {x, w_router, w_sgate, w_sup, w_sdown, logits, y, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < strata_moe_block_workspace_bytes(T, E, k, H, I, Is))
+    return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  uint16_t* a = static_cast<uint16_t*>(workspace);
+  const size_t a_bytes = round_up((size_t)T * Is * 2);
+  void* lws = static_cast<uint8_t*>(workspace) + a_bytes;
+  const size_t lwb = workspace_bytes - a_bytes;
+  if (T <= kMaxDecodeT && strata::decode_fits(T, E, k, H, I) && strata::router_shared_up_fits(T, H)) {
+    hipError_t e = strata::launch_router_shared_up(x, w_router, E, w_sgate, w_sup, Is, T, H, logits,
+                                                   a, stream);
+    if (e != hipSuccess) return STRATA_ERR_HIP;
+    return from_hip(strata::launch_decode(w->fmt, x, nullptr, 0.0f, logits, T, E, k, H, I,
+                                          w->gate_codes, w->up_codes, w->down_codes,
+                                          w->gate_scales, w->up_scales, w->down_scales, y,
+                                          accumulate, nullptr, nullptr, lws, stream, a, w_sdown, Is));
+  }
+  st = strata_moe_router_logits(x, w_router, T, H, E, logits, stream);
+  if (st != STRATA_OK) return st;
+  st = strata_moe_shared_expert(x, w_sgate, w_sup, w_sdown, T, H, Is, y, accumulate, a, a_bytes,
+                                stream);
+  if (st != STRATA_OK) return st;
+  return strata_moe_layer(w, x, logits, T, k, y, 1, nullptr, nullptr, nullptr, nullptr, nullptr,
+                          lws, lwb, stream);
+}
+
 strata_status strata_moe_usage_update(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                      uint64_t* usage, hipStream_t stream) {
   if (T < 0 || k < 1 || E < 1) return STRATA_ERR_INVALID_ARGUMENT;

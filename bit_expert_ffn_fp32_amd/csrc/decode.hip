@@ -335,6 +335,20 @@ STRATA_DEVICE void item_range(int n_items, int& begin, int& end) {
 // order, four interleaved partial sums), scales and stages its blocks, and one more barrier
 // publishes x.
 
+// Dot product of 8 bf16 values of weights and activations (natural order), fp32 accumulation.
+// (Named components: a subscripted vector element bit-cast inside an unrolled loop has compiled to
+// element 0 every time.)
+STRATA_DEVICE float bf16_dot2(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
+STRATA_DEVICE float bf16_dot8(const u32x4_t& w, const u32x4_t& x, float acc) {
+  acc = bf16_dot2(w.x, x.x, acc);
+  acc = bf16_dot2(w.y, x.y, acc);
+  acc = bf16_dot2(w.z, x.z, acc);
+  return bf16_dot2(w.w, x.w, acc);
+}
+
 // fp32 pair -> two bf16 (round to nearest even) in one word, low half first.
 STRATA_DEVICE uint32_t bf16_pair(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
@@ -347,7 +361,8 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
     int I, const uint8_t* __restrict__ gate_codes, const uint8_t* __restrict__ up_codes,
     const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales,
     uint32_t* __restrict__ a_st /* [S][I/2] staged a, unpadded */, int* __restrict__ ids_ws,
-    float* __restrict__ w_ws, GlobalTable* __restrict__ gt) {
+    float* __restrict__ w_ws, GlobalTable* __restrict__ gt, const uint16_t* __restrict__ a_sh,
+    const uint16_t* __restrict__ w_sd, int Is, float* __restrict__ y_sh, int sh_acc) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ RouteTable rt;
   __shared__ __align__(16) float part[RES ? kDecMaxT * 128 : 4];  // block sums of squares of h
@@ -393,6 +408,48 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = src[i];
       stage_block<FMT>(v, pairs + (b / nb) * rs, cs + (b / nb) * nb, b % nb);
+    }
+  }
+  // Block calls: the shared expert's down projection for rows [b R, (b + 1) R) of H (R = H / 256),
+  // y[t][row] (=|+=) sum_n W_sd[row][n] a_sh[t][n], by the waves that staged x, while the routing
+  // waves are still routing (they would otherwise wait at the barrier).  K2 then accumulates.
+  if constexpr (!RES) {
+    if (a_sh != nullptr && tid >= nr) {
+      const int nsw = (kUpThreads - nr) >> 6, sw = (tid - nr) >> 6, sl = tid & 63;
+      const int R = H / kGrid, h0 = blockIdx.x * R, np = Is >> 3;  // 16-byte pieces per row
+      const u32x4_t* av = reinterpret_cast<const u32x4_t*>(a_sh);
+      for (int r = sw; r < R; r += nsw) {
+        const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(w_sd + (size_t)(h0 + r) * Is);
+        float acc[kDecMaxT];
+#pragma unroll
+        for (int t = 0; t < kDecMaxT; ++t) acc[t] = 0.0f;
+        for (int q0 = sl; q0 < np; q0 += 128) {
+          const int q1 = q0 + 64;
+          const u32x4_t z = {0u, 0u, 0u, 0u};
+          const u32x4_t w0 = wrow[q0], w1 = q1 < np ? wrow[q1] : z;
+          u32x4_t x0[kDecMaxT], x1[kDecMaxT];
+#pragma unroll
+          for (int t = 0; t < kDecMaxT; ++t) {
+            x0[t] = t < T ? av[(size_t)t * np + q0] : z;
+            x1[t] = t < T && q1 < np ? av[(size_t)t * np + q1] : z;
+          }
+#pragma unroll
+          for (int t = 0; t < kDecMaxT; ++t) {
+            acc[t] = bf16_dot8(w0, x0[t], acc[t]);
+            acc[t] = bf16_dot8(w1, x1[t], acc[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < kDecMaxT; ++t) {
+          if (t < T) {
+            const float v = wave_sum(acc[t]);
+            if (sl == 0) {
+              float* dst = y_sh + (size_t)t * H + h0 + r;
+              *dst = sh_acc ? *dst + v : v;
+            }
+          }
+        }
+      }
     }
   }
   __syncthreads();
@@ -686,8 +743,11 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float e
                          int H, int I, const void* gate_codes, const void* up_codes,
                          const void* down_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, const uint16_t* down_scales, float* y,
-                         int accumulate, int* ids_out, float* w_out, void* ws, hipStream_t s) {
+                         int accumulate, int* ids_out, float* w_out, void* ws, hipStream_t s,
+                         const uint16_t* a_sh, const uint16_t* w_sd, int Is) {
   if (!decode_fits(T, E, k, H, I)) return hipErrorInvalidValue;
+  if (a_sh && (h_res || Is < 8 || Is % 8)) return hipErrorInvalidValue;
+  const int sh_acc = accumulate, acc_dn = a_sh ? 1 : accumulate;
   static std::once_flag once;
   std::call_once(once, [] { allow_all_decode_lds<2>(); allow_all_decode_lds<3>(); });
   const size_t S = (size_t)T * k;
@@ -712,14 +772,14 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float e
   do {                                                                                           \
     if (h_res)                                                                                   \
       decode_up_kernel<F, M, true><<<kGrid, kUpThreads, lds_up, s>>>(                            \
-          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a_st, ids, w, gt); \
+          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a_st, ids, w, gt, a_sh, w_sd, Is, y, sh_acc); \
     else                                                                                         \
       decode_up_kernel<F, M, false><<<kGrid, kUpThreads, lds_up, s>>>(                           \
-          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a_st, ids, w, gt); \
+          x, h_res, eps, logits, T, E, k, H, I, gc, uc, gate_scales, up_scales, a_st, ids, w, gt, a_sh, w_sd, Is, y, sh_acc); \
   } while (0)
 #define STRATA_DN(F, M, L)                                                                       \
   decode_down_kernel<F, M, L><<<kGrid, kDnThreads, lds_dn, s>>>(a_st, gt, w, T, E, k, H, I, \
-                                                                   dc, down_scales, y, accumulate)
+                                                                   dc, down_scales, y, acc_dn)
 #define STRATA_DEC(F)                                                                            \
   switch (mc_up) { case 1: STRATA_UP(F, 1); break; case 2: STRATA_UP(F, 2); break;              \
                    case 3: STRATA_UP(F, 3); break; default: STRATA_UP(F, 4); break; }           \

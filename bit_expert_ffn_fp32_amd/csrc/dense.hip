@@ -303,9 +303,9 @@ STRATA_DEVICE float dot8_bf16(const u32x4_t& w, const u32x4_t& x, float acc) {
 }
 
 // TT >= M token rows; LDS holds TT staged rows (rows M .. TT - 1 are unset, their sums are never
-// stored).
+// stored).  bid: this workgroup's index within the GEMV's grid.
 template <int TT, int LPR, int EPI>
-__global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
+STRATA_DEVICE void gemv_body(const DenseArgs& p, int bid) {
   constexpr int RW = 256 / LPR;                  // weight rows per workgroup
   constexpr int WL = LPR < 64 ? LPR : 64;        // lanes of a row within one wave
   constexpr int WPR = LPR / WL;                  // waves per row
@@ -314,10 +314,10 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
   const int nk8 = p.K >> 3;  // 16-byte pieces per row
   const uint16_t* row;
   if constexpr (EPI == kEpiSwiglu) {  // rows 0 .. RW/2-1: gate, RW/2 .. RW-1: up, same outputs
-    const int o = blockIdx.x * (RW / 2) + r % (RW / 2);
+    const int o = bid * (RW / 2) + r % (RW / 2);
     row = (r >= RW / 2 ? p.b1 : p.b0) + (size_t)min(o, p.N - 1) * p.K;
   } else {
-    row = p.b0 + (size_t)min(blockIdx.x * RW + r, p.N - 1) * p.K;
+    row = p.b0 + (size_t)min(bid * RW + r, p.N - 1) * p.K;
   }
   const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(row);
   u32x4_t w[kGemvBatch];
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
   if constexpr (EPI == kEpiSwiglu) {
     if (tid < (RW / 2) * TT) {
       const int o = tid / TT, t = tid % TT;
-      const int n = blockIdx.x * (RW / 2) + o;
+      const int n = bid * (RW / 2) + o;
       if (n < p.N && t < p.M)
         static_cast<uint16_t*>(p.out)[(size_t)t * p.N + n] =
             f32_to_bf16(silu_mul_f(total(o, t), total(o + RW / 2, t)));
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
   } else {
     if (tid < RW * TT) {
       const int rr = tid / TT, t = tid % TT;
-      const int n = blockIdx.x * RW + rr;
+      const int n = bid * RW + rr;
       if (n < p.N && t < p.M) {
         float* out = static_cast<float*>(p.out) + (size_t)t * p.N + n;
         const float v = total(rr, t);
@@ -390,6 +390,19 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
       }
     }
   }
+}
+
+template <int TT, int LPR, int EPI>
+__global__ __launch_bounds__(256) void dense_gemv_kernel(DenseArgs p) {
+  gemv_body<TT, LPR, EPI>(p, blockIdx.x);
+}
+
+// The router projection and the shared expert's gate/up projection in one launch (both read the
+// same token rows): workgroups [0, g0) take the router rows, the rest the gate/up rows.
+template <int TT, int LPR>
+__global__ __launch_bounds__(256) void router_shared_up_kernel(DenseArgs router, DenseArgs up, int g0) {
+  if ((int)blockIdx.x < g0) gemv_body<TT, LPR, kEpiStore>(router, blockIdx.x);
+  else gemv_body<TT, LPR, kEpiSwiglu>(up, blockIdx.x - g0);
 }
 
 template <int TT, int LPR, int EPI>
@@ -427,12 +440,46 @@ hipError_t dense(const DenseArgs& p, hipStream_t s) {
   return gemm<EPI>(p, s);
 }
 
+template <int TT, int LPR>
+hipError_t launch_router_shared_up_t(const DenseArgs& r, const DenseArgs& u, hipStream_t s) {
+  constexpr int RW = 256 / LPR;
+  const int g0 = (r.N + RW - 1) / RW, g1 = (u.N + RW / 2 - 1) / (RW / 2);
+  const int lds = TT * r.K * 2 > 256 ? TT * r.K * 2 : 256;
+  hipLaunchKernelGGL((router_shared_up_kernel<TT, LPR>), dim3(g0 + g1), dim3(256), lds, s, r, u, g0);
+  return hipGetLastError();
+}
+
+template <int TT>
+hipError_t router_shared_up_lpr(const DenseArgs& r, const DenseArgs& u, hipStream_t s) {
+  // as gemv_lpr, over the router's rows and the gate/up rows together
+  const int rows = r.N + 2 * u.N, nk8 = r.K / 8;
+  if (rows / 8 >= 256 || nk8 < 128) return launch_router_shared_up_t<TT, 32>(r, u, s);
+  if (rows / 4 >= 256 || nk8 < 256) return launch_router_shared_up_t<TT, 64>(r, u, s);
+  return launch_router_shared_up_t<TT, 128>(r, u, s);
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
                                 float* logits, hipStream_t s) {
   DenseArgs p{x, wr, nullptr, logits, T, E, H, 0};
   return dense<kEpiStore>(p, s);
+}
+
+bool router_shared_up_fits(int T, int H) {
+  return T >= 1 && T <= kGemvMaxRows && gemv_rows(T) * H * 2 <= kGemvMaxLds;
+}
+
+hipError_t launch_router_shared_up(const uint16_t* x, const uint16_t* wr, int E, const uint16_t* wg,
+                                   const uint16_t* wu, int Is, int T, int H, float* logits,
+                                   uint16_t* a, hipStream_t s) {
+  if (!router_shared_up_fits(T, H)) return hipErrorInvalidValue;
+  DenseArgs r{x, wr, nullptr, logits, T, E, H, 0};
+  DenseArgs u{x, wg, wu, a, T, Is, H, 0};
+  if (T <= 1) return router_shared_up_lpr<1>(r, u, s);
+  if (T <= 2) return router_shared_up_lpr<2>(r, u, s);
+  if (T <= 4) return router_shared_up_lpr<4>(r, u, s);
+  return router_shared_up_lpr<8>(r, u, s);
 }
 
 hipError_t launch_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,

@@ -58,6 +58,12 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, 
 
 // Dense bf16 layers.  Router: logits fp32 [T][E] = x W_r^T.  Shared expert: a = bf16(SiLU(x W_sg^T)
 // * (x W_su^T)) into a [T][I], then y (+)= a W_sd^T.  H and I multiples of 64.
+// Router projection and shared-expert gate/up GEMV in one launch (T <= 8 token rows; see
+// router_shared_up_fits): logits fp32 [T][E] = x W_r^T, a bf16 [T][Is] = SiLU(x W_sg^T) * (x W_su^T).
+bool router_shared_up_fits(int T, int H);
+hipError_t launch_router_shared_up(const uint16_t* x, const uint16_t* wr, int E, const uint16_t* wg,
+                                   const uint16_t* wu, int Is, int T, int H, float* logits,
+                                   uint16_t* a, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
                                 float* logits, hipStream_t s);
 hipError_t launch_shared_expert(const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
@@ -70,13 +76,18 @@ hipError_t launch_usage_update(const int* ids, int64_t S, int E, uint64_t* usage
 hipError_t launch_usage_rank(const uint64_t* usage, int E, int* order, hipStream_t s);
 
 // Decode path (T <= 8).  With h_res != NULL the input is the residual stream h (fp32 [T][H]) and
-// x = bf16(h / sqrt(mean(h^2) + eps)) is formed in the first kernel (x is then unused).
+// x = bf16(h / sqrt(mean(h^2) + eps)) is formed in the first kernel (x is then unused).  With
+// a_sh != NULL (and h_res == NULL) the first kernel also applies a shared expert's down projection,
+// y (=|+= by accumulate) a_sh W_sd^T (a_sh bf16 [T][Is], W_sd bf16 [H][Is], Is % 8 == 0), and the
+// routed output is then added to y.
 hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float eps,
                          const float* logits, int T, int E, int k,
                          int H, int I, const void* gate_codes, const void* up_codes,
                          const void* down_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, const uint16_t* down_scales, float* y,
-                         int accumulate, int* ids, float* w, void* ws, hipStream_t s);
+                         int accumulate, int* ids, float* w, void* ws, hipStream_t s,
+                         const uint16_t* a_sh = nullptr, const uint16_t* w_sd = nullptr,
+                         int Is = 0);
 size_t decode_workspace_bytes(int T, int E, int k, int H, int I);
 // Whether the decode kernels take this shape (T <= 8, T*k <= 128, H <= 4096, I <= 4096 and the
 // staged activations fit in LDS).

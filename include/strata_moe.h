@@ -282,6 +282,31 @@ strata_status strata_moe_shared_expert(const uint16_t* x, const uint16_t* w_gate
                                        hipStream_t stream);
 
 /*
+ * One whole MoE block step: logits = x W_r^T (written, as strata_moe_router_logits), the routed
+ * layer on those logits (as strata_moe_layer) and the shared expert (as strata_moe_shared_expert),
+ * y = routed + shared (y += both with accumulate != 0).  The pages keep the routers and the shared
+ * experts on the GPU beside the routed experts ("Strata vs Llama.cpp vs vLLM", transcript at 09:28;
+ * "Strata - the details", How it works / memory tiers); the block's composition is this library's
+ * definition.  For T <= 8 within the decode limits (strata_moe_decode) it is three launches: the
+ * router and the shared gate/up projection in one GEMV, then the decode kernels, the first of
+ * which also applies the shared down projection while its routing waves route; otherwise the
+ * three entry points above in turn.
+ *   x        bf16 [T][H] (read)
+ *   w_router bf16 [E][H]; w_sgate, w_sup bf16 [Is][H]; w_sdown bf16 [H][Is] (read), row-major
+ *   logits   fp32 [T][E] (written)
+ *   y        fp32 [T][H] (written or accumulated)
+ * Workspace: at least strata_moe_block_workspace_bytes(T, E, k, H, I, Is).
+ * Limits: those of strata_moe_layer and strata_moe_shared_expert (Is a multiple of 64).
+ */
+strata_status strata_moe_block(const strata_moe_weights* w, const uint16_t* x, int32_t T, int32_t k,
+                               const uint16_t* w_router, const uint16_t* w_sgate,
+                               const uint16_t* w_sup, const uint16_t* w_sdown, int32_t Is,
+                               float* logits, float* y, int32_t accumulate, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t strata_moe_block_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
+                                        int32_t Is);
+
+/*
  * Expert usage statistics.  The pages' engine keeps a running distribution of how often each
  * expert is used and keeps the most-used experts nearest the compute (video transcript on
  * unbiasedbob.com, 7:47 to 7:58; "Strata - the details", How it works / memory tiers).  This

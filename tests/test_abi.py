@@ -106,6 +106,22 @@ def test_layer_residual_validation(L):
     assert call(weights(), T=0, h=None) == OK       # T = 0: no-op
 
 
+def test_block_validation(L):
+    ws = L.strata_moe_block_workspace_bytes(4, 512, 10, 3072, 768, 768)
+    assert ws >= L.strata_moe_workspace_bytes(4, 512, 10, 3072, 768) + 4 * 768 * 2
+    assert L.strata_moe_block_workspace_bytes(4, 512, 10, 3072, 768, 0) == 0
+    call = lambda w, x=A, T=4, k=10, Is=768, lg=A, wsb=ws: L.strata_moe_block(
+        ctypes.byref(w), x, T, k, A, A, A, A, Is, lg, A, 0, A, wsb, None)
+    assert call(weights(), wsb=ws - 1) == WS
+    assert call(weights(), Is=0) == INVAL
+    assert call(weights(), Is=96) == UNSUP          # not a multiple of 64
+    assert call(weights(), x=MIS) == INVAL
+    assert call(weights(), lg=None) == INVAL
+    assert call(weights(fmt=4)) == INVAL
+    assert call(weights(E=8), k=9) == INVAL
+    assert call(weights(), T=0, x=None, lg=None) == OK   # T = 0: no-op
+
+
 def test_combine_and_rmsnorm_validation(L):
     assert L.strata_moe_combine(A, A, 4, 10, 3072, None, 0, None) == INVAL
     assert L.strata_moe_combine(A, A, 4, 10, 3071, A, 0, None) == UNSUP

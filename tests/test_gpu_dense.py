@@ -155,6 +155,47 @@ def test_moe_block_router_layer_shared(T):
     assert rel_l2_rows(y.cpu().numpy(), ref).max() <= TOL_REL_L2
 
 
+def gpu_block(L, s, wr, sh, y0=None):
+    T = L.T
+    logits = torch.full((T, s.E), float("nan"), dtype=torch.float32, device=dev())
+    y = torch.full((T, s.H), float("nan"), dtype=torch.float32, device=dev()) if y0 is None \
+        else to_dev(y0.astype(np.float32))
+    ws = sm.alloc_workspace(sm.block_workspace_bytes(T, s.E, s.k, s.H, s.I, sh["I"]), dev())
+    sm.strata_moe_block(L.w, L.x, s.k, to_dev_bf16(wr), to_dev_bf16(sh["gate"]),
+                        to_dev_bf16(sh["up"]), to_dev_bf16(sh["down"]), logits, y,
+                        accumulate=y0 is not None, workspace=ws)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), y.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,E,I,k,Is", [(1, 256, 64, 128, 4, 128), (4, 256, 64, 128, 4, 192),
+                                          (8, 512, 100, 256, 6, 128), (3, 256, 64, 128, 4, 64),
+                                          (9, 256, 64, 128, 4, 128), (33, 256, 64, 128, 4, 128),
+                                          (4, 3072, 512, 768, 10, 768)])
+def test_moe_block_one_call(T, H, E, I, k, Is):
+    """strata_moe_block (for T <= 8: router + shared gate/up in one GEMV, the shared down
+    projection inside the first decode kernel) against the oracle fed the GPU's logits; the
+    logits themselves within the router bound; accumulate adds onto y."""
+    log(f"block one call T={T} H={H} E={E} I={I} k={k} Is={Is}")
+    s = mi.Shape("b", T=T, H=H, E=E, k=k, I=I)
+    L = Layer(s, seed=13, T=T)
+    wr = mi.make_router(s, seed=13)
+    sh = mi.make_shared(mi.Shape("bs", T=T, H=H, E=E, k=k, I=Is), seed=13)
+    lg, y = gpu_block(L, s, wr, sh)
+    assert np.all(np.abs(lg - oracle.router_logits(L.x_np, wr)) <= router_bound(L.x_np, wr, H))
+    ref = oracle.layer(L.w_np, L.x_np, lg, k) + oracle.shared_expert(L.x_np, sh["gate"], sh["up"],
+                                                                      sh["down"])
+    err = rel_l2_rows(y, ref)
+    log(f"  max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL_REL_L2
+    y0 = mi.normal_f32(13, 998, T * H).reshape(T, H)
+    lg2, ya = gpu_block(L, s, wr, sh, y0)
+    assert np.array_equal(lg, lg2)
+    np.testing.assert_allclose(ya, y0.astype(np.float64) + y, rtol=1e-5, atol=1e-5)
+    _, y2 = gpu_block(L, s, wr, sh)
+    assert np.array_equal(y, y2), "second call differs"
+
+
 def test_zero_tokens_and_accumulate_flag():
     """T = 0 is a no-op for both entry points; accumulate = False overwrites whatever y held."""
     s = shape(1, 256, I=128)
