@@ -605,7 +605,11 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
   // units (distinct expert d, row pair r < RH): rows r and r + RH (the second repeats r when it
   // falls outside the R rows), so that each activation read from LDS serves two rows
   const int RH = (R + 1) / 2, U = rt.nd * RH, g = tid / LPU, j = tid % LPU;
-  RowChunks<FMT, MC> wr[2][2];
+  // Two units' weights in flight per lane group, except where two do not fit in the registers
+  // beside everything else (3-bit with >= 3 chunks per lane, 2-bit with 4): one unit at a time
+  // there (with 256 lane groups and 6 units per distinct expert a group rarely has a second).
+  constexpr bool kTwoUnits = FMT == 3 ? MC < 3 : MC < 4;
+  RowChunks<FMT, MC> wr[kTwoUnits ? 2 : 1][2];
   auto unit_rows = [&](int u, int& r0, int& r1) {
     r0 = u % RH;
     r1 = r0 + RH < R ? r0 + RH : r0;
@@ -652,7 +656,8 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
     if ((tid & 63) == 0) atomicAdd(&staged_waves, 1);
   }
   if (g < U) load_unit(g, wr[0]);
-  if (g + kGroups < U) load_unit(g + kGroups, wr[1]);
+  if constexpr (kTwoUnits)
+    if (g + kGroups < U) load_unit(g + kGroups, wr[kTwoUnits ? 1 : 0]);
   while (__hip_atomic_load(&staged_waves, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kDnThreads / 64)
     __builtin_amdgcn_s_sleep(1);
   auto compute_unit = [&](int u, RowChunks<FMT, MC> (&rr)[2]) {
@@ -672,12 +677,19 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
       }
     }
   };
-  for (int u = g; u < U; u += 2 * kGroups) {
-    compute_unit(u, wr[0]);
-    if (u + 2 * kGroups < U) load_unit(u + 2 * kGroups, wr[0]);
-    if (u + kGroups < U) {
-      compute_unit(u + kGroups, wr[1]);
-      if (u + 3 * kGroups < U) load_unit(u + 3 * kGroups, wr[1]);
+  if constexpr (kTwoUnits) {
+    for (int u = g; u < U; u += 2 * kGroups) {
+      compute_unit(u, wr[0]);
+      if (u + 2 * kGroups < U) load_unit(u + 2 * kGroups, wr[0]);
+      if (u + kGroups < U) {
+        compute_unit(u + kGroups, wr[kTwoUnits ? 1 : 0]);
+        if (u + 3 * kGroups < U) load_unit(u + 3 * kGroups, wr[kTwoUnits ? 1 : 0]);
+      }
+    }
+  } else {
+    for (int u = g; u < U; u += kGroups) {
+      compute_unit(u, wr[0]);
+      if (u + kGroups < U) load_unit(u + kGroups, wr[0]);
     }
   }
   __syncthreads();

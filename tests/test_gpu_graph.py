@@ -40,10 +40,11 @@ def test_graph_replay_matches_eager(T):
         del scratch
 
 
-@pytest.mark.parametrize("T", [4, 40])
-def test_graph_replay_of_the_block_matches_eager(T):
-    """Router projection -> routed layer -> + shared expert captured in one graph: every replay
-    equals the eager result (the benchmark replays such graphs)."""
+@pytest.mark.parametrize("T,one_call", [(4, False), (40, False), (4, True), (40, True)])
+def test_graph_replay_of_the_block_matches_eager(T, one_call):
+    """Router projection -> routed layer -> + shared expert captured in one graph, as three entry
+    points or as strata_moe_block: every replay equals the eager result (the benchmark replays
+    such graphs)."""
     import moe_inputs as mi
     from gpu_helpers import to_dev_bf16
 
@@ -56,7 +57,13 @@ def test_graph_replay_of_the_block_matches_eager(T):
     sws = sm.alloc_workspace(sm.shared_workspace_bytes(T, s.I), dev())
     logits = torch.empty((T, s.E), dtype=torch.float32, device=dev())
 
+    bws = sm.alloc_workspace(sm.block_workspace_bytes(T, s.E, s.k, s.H, s.I, s.I), dev())
+
     def block(y, strm):
+        if one_call:
+            sm.strata_moe_block(L.w, L.x, s.k, wr, g_, u_, d_, logits, y, workspace=bws,
+                                stream=strm)
+            return
         sm.strata_moe_router_logits(L.x, wr, logits, stream=strm)
         sm.strata_moe_layer(L.w, L.x, logits, s.k, y, workspace=ws, stream=strm)
         sm.strata_moe_shared_expert(L.x, g_, u_, d_, y, sws, accumulate=True, stream=strm)

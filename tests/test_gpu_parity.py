@@ -205,7 +205,10 @@ def gpu_layer(L: Layer, accumulate=False, y0=None, want_ids=False):
 @pytest.mark.parametrize("s", SMALL_SHAPES + [shape("t9", T=9), shape("t8", T=8), shape("t1", T=1),
                                               shape("t17", T=17), shape("t48", T=48),
                                               shape("t49", T=49), shape("t33_q3", T=33, fmt=3),
-                                              shape("t5_q3", T=5, fmt=3), shape("t3_e1", T=3, E=1, k=1)],
+                                              shape("t5_q3", T=5, fmt=3), shape("t3_e1", T=3, E=1, k=1),
+                                              shape("t4_q3_i768", T=4, H=512, I=768, fmt=3),
+                                              shape("t3_i1024", T=3, I=1024),
+                                              shape("t6_q3_i1024", T=6, I=1024, fmt=3)],
                          ids=lambda s: s.name)
 def test_layer_against_oracle(s):
     log(f"layer {s}")
