@@ -682,6 +682,8 @@ __global__ void x_to_f16_kernel(const uint16_t* __restrict__ x, size_t n8, uint1
 // ---------------------------------------------------------------------------------------------
 // Combine: y[t][h] (+)= sum_j w[t][j] * out[t*k + j][h], j ascending (one thread per 8 h).
 
+constexpr int kCombineMaxK = 16;  // rows requested together (the largest k the router takes)
+
 __global__ void combine_kernel(const uint16_t* __restrict__ out, const float* __restrict__ w, int T,
                                int k, int H, float* __restrict__ y, int accumulate) {
   const int h8 = H / 8;
@@ -696,13 +698,35 @@ __global__ void combine_kernel(const uint16_t* __restrict__ out, const float* __
     for (int m = 0; m < 4; ++m) { acc[m] = a[m]; acc[m + 4] = b[m]; }
   }
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(out + ((size_t)t * k + j) * H + c * 8);
+  // all k rows requested before the first is used (k <= 16)
+  u32x4_t v[kCombineMaxK];
+  float wj[kCombineMaxK];
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; ++j) {
+    if (j < k) {
+      wj[j] = w[(size_t)t * k + j];
+      v[j] = *reinterpret_cast<const u32x4_t*>(out + ((size_t)t * k + j) * H + c * 8);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; ++j) {
+    if (j < k) {
+      const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        s[2 * m] = __builtin_fmaf(wj[j], __uint_as_float(q[m] << 16), s[2 * m]);
+        s[2 * m + 1] = __builtin_fmaf(wj[j], __uint_as_float(q[m] & 0xFFFF0000u), s[2 * m + 1]);
+      }
+    }
+  }
+  for (int j = kCombineMaxK; j < k; ++j) {  // k > 16: only through strata_moe_combine
+    const float wr = w[(size_t)t * k + j];
+    const u32x4_t vr = *reinterpret_cast<const u32x4_t*>(out + ((size_t)t * k + j) * H + c * 8);
+    const uint32_t q[4] = {vr.x, vr.y, vr.z, vr.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      s[2 * m] = __builtin_fmaf(wj, __uint_as_float(v[m] << 16), s[2 * m]);
-      s[2 * m + 1] = __builtin_fmaf(wj, __uint_as_float(v[m] & 0xFFFF0000u), s[2 * m + 1]);
+      s[2 * m] = __builtin_fmaf(wr, __uint_as_float(q[m] << 16), s[2 * m]);
+      s[2 * m + 1] = __builtin_fmaf(wr, __uint_as_float(q[m] & 0xFFFF0000u), s[2 * m + 1]);
     }
   }
   f32x4_t o0, o1;

@@ -169,9 +169,9 @@ def test_staged_prefill_path(s):
     assert e_y.max() <= TOL_REL_L2
 
 
-def test_combine_against_oracle():
-    rng = np.random.default_rng(3)
-    T, k, H = 37, 5, 512
+@pytest.mark.parametrize("T,k,H", [(37, 5, 512), (9, 1, 256), (5, 16, 64), (6, 20, 128)])
+def test_combine_against_oracle(T, k, H):
+    rng = np.random.default_rng(3 + k)
     out_bits = mi.f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
     w = rng.random((T, k)).astype(np.float32)
     y0 = rng.standard_normal((T, H)).astype(np.float32)
