@@ -168,16 +168,17 @@ def gpu_block(L, s, wr, sh, y0=None):
     return logits.cpu().numpy(), y.cpu().numpy()
 
 
-@pytest.mark.parametrize("T,H,E,I,k,Is", [(1, 256, 64, 128, 4, 128), (4, 256, 64, 128, 4, 192),
-                                          (8, 512, 100, 256, 6, 128), (3, 256, 64, 128, 4, 64),
-                                          (9, 256, 64, 128, 4, 128), (33, 256, 64, 128, 4, 128),
-                                          (4, 3072, 512, 768, 10, 768)])
-def test_moe_block_one_call(T, H, E, I, k, Is):
+@pytest.mark.parametrize("T,H,E,I,k,Is,fmt", [(1, 256, 64, 128, 4, 128, 2), (4, 256, 64, 128, 4, 192, 2),
+                                              (8, 512, 100, 256, 6, 128, 2), (3, 256, 64, 128, 4, 64, 2),
+                                              (5, 512, 64, 768, 4, 256, 3), (20, 256, 64, 128, 4, 128, 3),
+                                              (9, 256, 64, 128, 4, 128, 2), (33, 256, 64, 128, 4, 128, 2),
+                                              (4, 3072, 512, 768, 10, 768, 2)])
+def test_moe_block_one_call(T, H, E, I, k, Is, fmt):
     """strata_moe_block (for T <= 8: router + shared gate/up in one GEMV, the shared down
     projection inside the first decode kernel) against the oracle fed the GPU's logits; the
     logits themselves within the router bound; accumulate adds onto y."""
-    log(f"block one call T={T} H={H} E={E} I={I} k={k} Is={Is}")
-    s = mi.Shape("b", T=T, H=H, E=E, k=k, I=I)
+    log(f"block one call T={T} H={H} E={E} I={I} k={k} Is={Is} Q{fmt}")
+    s = mi.Shape("b", T=T, H=H, E=E, k=k, I=I, fmt=fmt)
     L = Layer(s, seed=13, T=T)
     wr = mi.make_router(s, seed=13)
     sh = mi.make_shared(mi.Shape("bs", T=T, H=H, E=E, k=k, I=Is), seed=13)
