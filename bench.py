@@ -556,7 +556,7 @@ def main():
     args = p.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every layer's "
-              "experts fit in one MI355X's HBM and this build has no multi-GPU path.", file=sys.stderr)
+              "experts fit in one MI355X's HBM and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
