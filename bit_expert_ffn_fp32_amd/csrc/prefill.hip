@@ -144,22 +144,26 @@ STRATA_DEVICE half8_t q2_decode(uint32_t w0, uint32_t w1, int s, const Q2Tab& ta
   return __builtin_bit_cast(half8_t, r);
 }
 
-// 3-bit: the block's 12 code bytes as 3 words; step s covers bits 24s .. 24s+23.
-STRATA_DEVICE half8_t q3_decode(uint32_t w0, uint32_t w1, uint32_t w2, int s, float d) {
+// 3-bit: the block's 12 code bytes as 3 words; step s covers bits 24s .. 24s+23.  A code q is
+// placed in the mantissa of an fp16 2.0, giving 2 + q/4; minus 2.875 that is (q - 3.5)/4 exactly,
+// and times 4d (exact: a power-of-two multiple of the scale) it is d (q - 3.5) with one rounding,
+// so each pair costs a few bit operations and two packed fp16 operations.  d4: 4d in both halves.
+STRATA_DEVICE half8_t q3_decode(uint32_t w0, uint32_t w1, uint32_t w2, int s, half2_t d4) {
   uint32_t v;
   if (s == 0) v = w0;
   else if (s == 1) v = __builtin_amdgcn_alignbit(w1, w0, 24);
   else if (s == 2) v = __builtin_amdgcn_alignbit(w2, w1, 16);
   else v = w2 >> 8;
-  const float off = -3.5f * d;  // exact: 13 significant bits
-  half8_t r;
+  const half2_t off = {(_Float16)-2.875f, (_Float16)-2.875f};
+  u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t qa = (v >> (3 * i)) & 7u, qb = (v >> (3 * i + 12)) & 7u;
-    r[2 * i] = (_Float16)__builtin_fmaf((float)qa, d, off);  // exact in fp32, one rounding
-    r[2 * i + 1] = (_Float16)__builtin_fmaf((float)qb, d, off);
+    const uint32_t t = v >> (3 * i);  // code a at bits 0..2, code b at bits 12..14
+    const uint32_t h = ((t & 7u) << 7) | ((t & 0x7000u) << 11) | 0x40004000u;  // 2 + q/4 each
+    const half2_t w = (__builtin_bit_cast(half2_t, h) + off) * d4;
+    r[i] = __builtin_bit_cast(uint32_t, w);
   }
-  return r;
+  return __builtin_bit_cast(half8_t, r);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -263,7 +267,7 @@ template <int FMT>
 struct StageWeights {
   uint32_t cw0[3], cw1[3];
   Q2Tab t0, t1;
-  float f0, f1;
+  half2_t d40, d41;  // 3-bit: 4 d of each stream's block, in both halves
 };
 
 template <int FMT, int NF>
@@ -288,8 +292,10 @@ STRATA_DEVICE void load_stage_weights(StageWeights<FMT>& sw, const uint8_t* stag
     sw.t0 = q2_table(d0);
     sw.t1 = q2_table(d1);
   } else {
-    sw.f0 = f16_to_f32(d0);
-    sw.f1 = f16_to_f32(d1);
+    const _Float16 e0 = __builtin_bit_cast(_Float16, d0) * (_Float16)4.0f;  // exact
+    const _Float16 e1 = __builtin_bit_cast(_Float16, d1) * (_Float16)4.0f;
+    sw.d40 = half2_t{e0, e0};
+    sw.d41 = half2_t{e1, e1};
   }
 }
 
@@ -300,8 +306,8 @@ STRATA_DEVICE void decode_step(const StageWeights<FMT>& sw, int s, half8_t (&b)[
     b[0] = q2_decode(sw.cw0[0], sw.cw0[1], s, sw.t0, k);
     b[1] = q2_decode(sw.cw1[0], sw.cw1[1], s, sw.t1, k);
   } else {
-    b[0] = q3_decode(sw.cw0[0], sw.cw0[1], sw.cw0[2], s, sw.f0);
-    b[1] = q3_decode(sw.cw1[0], sw.cw1[1], sw.cw1[2], s, sw.f1);
+    b[0] = q3_decode(sw.cw0[0], sw.cw0[1], sw.cw0[2], s, sw.d40);
+    b[1] = q3_decode(sw.cw1[0], sw.cw1[1], sw.cw1[2], s, sw.d41);
   }
 }
 
