@@ -172,6 +172,7 @@ def gpu_block(L, s, wr, sh, y0=None):
                                               (8, 512, 100, 256, 6, 128, 2), (3, 256, 64, 128, 4, 64, 2),
                                               (5, 512, 64, 768, 4, 256, 3), (20, 256, 64, 128, 4, 128, 3),
                                               (9, 256, 64, 128, 4, 128, 2), (33, 256, 64, 128, 4, 128, 2),
+                                              (2, 256, 1, 128, 1, 64, 2), (8, 256, 512, 128, 16, 128, 2),
                                               (4, 3072, 512, 768, 10, 768, 2)])
 def test_moe_block_one_call(T, H, E, I, k, Is, fmt):
     """strata_moe_block (for T <= 8: router + shared gate/up in one GEMV, the shared down
