@@ -186,7 +186,7 @@ strata_status strata_moe_combine(const uint16_t* expert_out, const float* topk_w
  *   opt_topk_ids int32 [T][k], opt_topk_w fp32 [T][k]: written when not NULL.
  * Workspace: at least strata_moe_workspace_bytes(T, E, k, H, I).
  * Limits: 1 <= T <= 8, T*k <= 128, hidden and inter at most 4096, and the activations staged
- * in LDS must fit: 19/8 * T * hidden <= 147456 and 19/8 * T * k * inter <= 147456 (bytes);
+ * in LDS must fit: 19/8 * T * hidden + 4 * E <= 147456 and 19/8 * T * k * inter <= 147456 (bytes);
  * STRATA_ERR_UNSUPPORTED otherwise.  Others as strata_moe_expert_ffn.
  */
 strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
