@@ -249,23 +249,36 @@ int32_t oracle_layer_rows(const oracle_weights* w, const uint16_t* x, const floa
 }
 
 /*
- * RMSNorm with unit gain for the layer stack: x = bf16(h / sqrt(mean(h^2) + eps)).  The
- * normalised value is formed in fp64, rounded to fp32 and then to bf16 (both round to nearest
- * even), the precision in which the GPU takes the same rounding decision.
+ * Round an fp64 value to bf16, nearest with ties to even, in one step: bf16 keeps 8 significant
+ * bits (exponent range as binary32).  v = m * 2^e with m in [0.5, 1); the kept value is
+ * rint(m * 2^8) * 2^(e - 8) (rint rounds half to even in the default rounding mode).  Values
+ * below the smallest normal binary32 keep fewer bits, as the format's subnormals do.
+ */
+static uint16_t bf16_from_f64(double v) {
+  int e;
+  double m = frexp(v, &e);
+  int keep = 8;
+  if (e - 1 < -126) keep = 8 - (-126 - (e - 1)); /* subnormal range of the format */
+  double r = keep >= 0 ? ldexp(rint(ldexp(m, keep)), e - keep) : 0.0;
+  float f = (float)r; /* exact: r has at most 8 significant bits and is in binary32 range */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if (r == 0.0 && signbit(v)) u = 0x80000000u;
+  return (uint16_t)(u >> 16);
+}
+
+/*
+ * RMSNorm with unit gain for the layer stack: x = bf16(h / sqrt(mean(h^2) + eps)), eps inside
+ * the square root.  The mean of squares and the quotient are formed in fp64 and each quotient is
+ * rounded once, straight to bf16 (nearest, ties to even).
  */
 void oracle_rmsnorm(const float* h, int32_t T, int32_t H, double eps, uint16_t* x) {
   for (int32_t t = 0; t < T; ++t) {
     const float* r = h + (int64_t)t * H;
     double ss = 0.0;
     for (int32_t i = 0; i < H; ++i) ss += (double)r[i] * (double)r[i];
-    double inv = 1.0 / sqrt(ss / (double)H + eps);
-    for (int32_t i = 0; i < H; ++i) {
-      float v = (float)((double)r[i] * inv);
-      uint32_t u;
-      memcpy(&u, &v, 4);
-      uint32_t lsb = (u >> 16) & 1u;
-      x[(int64_t)t * H + i] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
-    }
+    double den = sqrt(ss / (double)H + eps);
+    for (int32_t i = 0; i < H; ++i) x[(int64_t)t * H + i] = bf16_from_f64((double)r[i] / den);
   }
 }
 

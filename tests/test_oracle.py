@@ -351,6 +351,79 @@ def test_rmsnorm_unit_rms_and_scale_invariance(oracle_lib):
     assert np.mean(x2 == oracle.rmsnorm(h, 1e-6)) > 0.999
 
 
+def bf16_nearest_by_search(v: float) -> float:
+    """bf16 value nearest to the fp64 value v, ties to the even bit pattern, found by comparing
+    v with the candidate bit patterns around its binary32 rounding (exact fp64 distances; a
+    different route from the oracle's frexp/rint)."""
+    f = np.float32(v)
+    c = int(f.view(np.uint32)) >> 16
+    best, best_d = None, None
+    for b in (c - 1, c, c + 1, c + 2):
+        val = float(np.uint32((b & 0xFFFF) << 16).view(np.float32))
+        d = abs(val - v)
+        if best is None or d < best_d or (d == best_d and (b & 1) == 0):
+            best, best_d = b & 0xFFFF, d
+    return float(np.uint32(best << 16).view(np.float32))
+
+
+def test_rmsnorm_eps_inside_the_square_root(oracle_lib):
+    """mean(h^2) = 1e-8 is far below eps = 1e-6: x = h / sqrt(mean + eps) = 0.0995 differs from
+    h / (sqrt(mean) + eps) = 0.990, from h / sqrt((sum + eps) / H) = 0.848 and from h / sqrt(mean)
+    = 1, so a misplaced eps fails."""
+    H, eps = 256, 1e-6
+    h = np.full((2, H), 1e-4, dtype=np.float32)
+    h[1, ::2] = -1e-4
+    x = mi.bf16_bits_to_f32(oracle.rmsnorm(h, eps)).astype(np.float64)
+    hv = float(np.float32(1e-4))
+    want = bf16_nearest_by_search(hv / np.sqrt(hv * hv + eps))
+    assert abs(want - 0.0995) < 1e-3
+    assert np.all(x[0] == want)
+    assert np.array_equal(x[1], np.where(np.arange(H) % 2 == 0, -want, want))
+    for wrong in (hv / (hv + eps), hv / np.sqrt((H * hv * hv + eps) / H), 1.0):
+        assert bf16_nearest_by_search(wrong) != want
+
+
+def test_rmsnorm_ties_round_to_even(oracle_lib):
+    """Rows whose mean square is exactly 256^2 (eps = 0), so each quotient is exact: 257/256 and
+    259/256 lie half-way between neighbouring bf16 values and go to the even one (1 and 260/256),
+    which truncation, half-up or half-down rounding each get wrong in one of the two rows."""
+    rows = np.array([[257, 676, 35, 6, 1, 1, 0, 0], [259, 676, 15, 2, 1, 1, 0, 0]], dtype=np.float32)
+    assert np.all((rows.astype(np.float64) ** 2).sum(axis=1) == 8 * 256.0 ** 2)
+    x = mi.bf16_bits_to_f32(oracle.rmsnorm(rows, 0.0)).astype(np.float64)
+    assert x[0, 0] == 1.0 and x[1, 0] == 260 / 256
+    assert np.array_equal(x[0, 1:], rows[0, 1:] / 256.0)  # exactly representable
+    assert np.array_equal(x[1, 1:], rows[1, 1:] / 256.0)
+
+
+def test_rmsnorm_rounds_once(oracle_lib):
+    """h[5] = 1 - 2^-9 makes the mean square 2^-30 below 256^2, so 257 / rms lies 2^-28 (relative)
+    above the tie 257/256: rounded once it goes up to 258/256; rounded to binary32 first it
+    would land on the tie and then go down to 1."""
+    row = np.array([[257, 676, 35, 6, 1, 1 - 2.0 ** -9, 0, 0]], dtype=np.float32)
+    q = 257.0 / np.sqrt((row.astype(np.float64) ** 2).sum() / 8)
+    assert q > 257 / 256 and float(np.float32(q)) == 257 / 256
+    x = mi.bf16_bits_to_f32(oracle.rmsnorm(row, 0.0)).astype(np.float64)
+    assert x[0, 0] == 258 / 256
+
+
+def test_rmsnorm_matches_numpy_fp64(oracle_lib):
+    """Random rows over a wide range of scales against numpy in fp64 (exact sum of squares by
+    math.fsum) rounded by the candidate search above."""
+    import math
+
+    rng = np.random.default_rng(12)
+    H = 512
+    scales = [1e-30, 1e-6, 3e-3, 1.0, 7.0, 4e5, 1e30]
+    h = np.concatenate([(rng.standard_normal((2, H)) * s).astype(np.float32) for s in scales])
+    eps = 1e-6
+    x = mi.bf16_bits_to_f32(oracle.rmsnorm(h, eps)).astype(np.float64)
+    for t in range(h.shape[0]):
+        r = h[t].astype(np.float64)
+        den = math.sqrt(math.fsum(r * r) / H + eps)
+        want = np.array([bf16_nearest_by_search(v / den) for v in r])
+        assert np.array_equal(x[t], want), t
+
+
 # ---------------------------------------------------------------------------------------------
 # ---------------------------------------------------------------------------------------------
 # Router projection and shared expert (dense bf16 layers on either side of the routed experts)
