@@ -25,6 +25,7 @@ EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "s
            "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
            "strata_moe_router_logits", "strata_moe_shared_expert",
            "strata_moe_usage_update", "strata_moe_usage_rank", "strata_moe_layer_residual",
+           "strata_moe_weight_stats",
            "strata_moe_residual_workspace_bytes", "strata_moe_block", "strata_moe_block_workspace_bytes",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
            "strata_moe_shared_workspace_bytes", "strata_status_string"]
@@ -37,11 +38,19 @@ class StrataError(RuntimeError):
 
 
 class CWeights(ctypes.Structure):
+    """strata_moe_weights, field for field (include/strata_moe.h)."""
     _fields_ = [("fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("gate_codes", ctypes.c_void_p), ("up_codes", ctypes.c_void_p),
-                ("down_codes", ctypes.c_void_p), ("gate_scales", ctypes.c_void_p),
-                ("up_scales", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
+                ("gate_scales", ctypes.c_void_p), ("up_scales", ctypes.c_void_p),
+                ("down_codes", ctypes.c_void_p), ("down_scales", ctypes.c_void_p),
+                ("stats", ctypes.c_void_p)]
+
+
+class CExpertStats(ctypes.Structure):
+    """strata_moe_expert_stats (16 bytes per expert)."""
+    _fields_ = [("shift_gate", ctypes.c_int32), ("shift_up", ctypes.c_int32),
+                ("shift_down", ctypes.c_int32), ("norm_gate_up", ctypes.c_float)]
 
 
 _lib = None
@@ -71,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "strata_moe_usage_rank": [vp, i32, vp, vp],
             "strata_moe_layer_residual": [W, vp, vp, i32, i32, ctypes.c_float, vp, sz, vp],
             "strata_moe_block": [W, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
+            "strata_moe_weight_stats": [W, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -124,11 +134,19 @@ class Weights:
     gate_scales: torch.Tensor
     up_scales: torch.Tensor
     down_scales: torch.Tensor
+    stats: torch.Tensor | None = None  # int32 [E][4] holding strata_moe_expert_stats
 
     def c_struct(self) -> CWeights:
         return CWeights(self.fmt, self.E, self.H, self.I, _p(self.gate_codes), _p(self.up_codes),
-                        _p(self.down_codes), _p(self.gate_scales), _p(self.up_scales),
-                        _p(self.down_scales))
+                        _p(self.gate_scales), _p(self.up_scales), _p(self.down_codes),
+                        _p(self.down_scales), _p(self.stats))
+
+    def compute_stats(self, stream=None) -> "Weights":
+        """Fills self.stats with the range statistics of the tiled weights (strata_moe_weight_stats;
+        the prefill path needs them)."""
+        self.stats = torch.zeros((self.E, 4), dtype=torch.int32, device=self.gate_codes.device)
+        strata_moe_weight_stats(self, self.stats, stream)
+        return self
 
     @property
     def nbytes(self) -> int:
@@ -152,7 +170,7 @@ class Weights:
         gc, gs = packed(w["gate_codes"], w["gate_scales"], I, H)
         uc, us = packed(w["up_codes"], w["up_scales"], I, H)
         dc, ds = packed(w["down_codes"], w["down_scales"], H, I)
-        return Weights(fmt, E, H, I, gc, uc, dc, gs, us, ds)
+        return Weights(fmt, E, H, I, gc, uc, dc, gs, us, ds).compute_stats()
 
 
 def permute_workspace_bytes(T: int, E: int, k: int) -> int:
@@ -231,6 +249,13 @@ def strata_moe_pack_matrix(fmt, n_mat, rows, K, codes, scales, tiled_codes, tile
     _check("strata_moe_pack_matrix", lib().strata_moe_pack_matrix(
         fmt, n_mat, rows, K, _p(codes), _p(scales), _p(tiled_codes), _p(tiled_scales),
         _stream(stream)))
+
+
+def strata_moe_weight_stats(w: Weights, stats, stream=None) -> None:
+    """stats (int32 [E][4] viewed as strata_moe_expert_stats) = range statistics of w."""
+    cw = w.c_struct()
+    _check("strata_moe_weight_stats", lib().strata_moe_weight_stats(ctypes.byref(cw), _p(stats),
+                                                                    _stream(stream)))
 
 
 def strata_moe_rmsnorm(h, x, eps=1e-6, stream=None) -> None:

@@ -10,6 +10,16 @@
 
 using strata::Chunk;
 
+// The weights struct's layout is part of the ABI (field order as documented in the header).
+static_assert(offsetof(strata_moe_weights, fmt) == 0 && offsetof(strata_moe_weights, num_experts) == 4 &&
+              offsetof(strata_moe_weights, hidden) == 8 && offsetof(strata_moe_weights, inter) == 12 &&
+              offsetof(strata_moe_weights, gate_codes) == 16 && offsetof(strata_moe_weights, up_codes) == 24 &&
+              offsetof(strata_moe_weights, gate_scales) == 32 && offsetof(strata_moe_weights, up_scales) == 40 &&
+              offsetof(strata_moe_weights, down_codes) == 48 && offsetof(strata_moe_weights, down_scales) == 56 &&
+              offsetof(strata_moe_weights, stats) == 64 && sizeof(strata_moe_weights) == 72,
+              "strata_moe_weights layout");
+static_assert(sizeof(strata_moe_expert_stats) == 16, "strata_moe_expert_stats layout");
+
 namespace {
 
 constexpr int kMaxE = 1024;
@@ -50,6 +60,11 @@ strata_status check_weights(const strata_moe_weights* w) {
   return STRATA_OK;
 }
 
+// The prefill path also needs the weights' range statistics.
+strata_status check_stats(const strata_moe_weights* w) {
+  return w->stats && aligned16(w->stats) ? STRATA_OK : STRATA_ERR_INVALID_ARGUMENT;
+}
+
 strata_status from_hip(hipError_t e) { return e == hipSuccess ? STRATA_OK : STRATA_ERR_HIP; }
 
 // Workspace of the prefill path, carved in this order (each piece 256-byte aligned).
@@ -64,6 +79,7 @@ struct PrefillWs {
   int* tile_base;
   Chunk* chunks;
   int* n_chunks;
+  strata::XInfo* xinfo;
   uint16_t* x16;
   uint16_t* a16;
   uint16_t* expert_out;
@@ -93,6 +109,7 @@ PrefillWs carve_prefill(void* base, int32_t T, int32_t E, int32_t k, int32_t H, 
   p.tile_base = static_cast<int*>(take(ntiles * E * 4));
   p.chunks = static_cast<Chunk*>(take((size_t)p.max_chunks * sizeof(Chunk)));
   p.n_chunks = static_cast<int*>(take(16));
+  p.xinfo = static_cast<strata::XInfo*>(take((size_t)T * sizeof(strata::XInfo)));
   p.x16 = static_cast<uint16_t*>(take((size_t)T * H * 2));
   p.a16 = static_cast<uint16_t*>(take(S * I * 2));
   p.expert_out = static_cast<uint16_t*>(take(S * H * 2));
@@ -136,6 +153,43 @@ __global__ void chunks_from_offsets_kernel(const int* offsets, int E, Chunk* chu
   if (e == 0) *n_chunks = tot;
 }
 
+// Decode paths (T <= kSplitDecodeMaxT): the decode kernels' workspace for slices of at most
+// kMaxDecodeT tokens, then, for a caller that asks strata_moe_layer for the permutation, the
+// routing result of all T tokens and one counting sort's outputs and scratch.
+struct DecodePermWs {
+  int* ids;
+  int* counts;
+  int* offsets;
+  int* sorted_slot;
+  int* slot_pos;
+  int* tile_hist;
+  int* tile_base;
+  size_t bytes;
+};
+
+DecodePermWs carve_decode_perm(void* base, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+  DecodePermWs q{};
+  const size_t S = (size_t)T * k;
+  const size_t ntiles = (S + strata::kPermTile - 1) / strata::kPermTile;
+  const int32_t td = T < kMaxDecodeT ? T : kMaxDecodeT;
+  uint8_t* c = static_cast<uint8_t*>(base);
+  size_t off = round_up(strata::decode_workspace_bytes(td, E, k, H, I));
+  auto take = [&](size_t bytes) {
+    void* r = c ? c + off : nullptr;
+    off += round_up(bytes);
+    return r;
+  };
+  q.ids = static_cast<int*>(take(S * 4));
+  q.counts = static_cast<int*>(take((size_t)E * 4));
+  q.offsets = static_cast<int*>(take((size_t)(E + 1) * 4));
+  q.sorted_slot = static_cast<int*>(take(S * 4));
+  q.slot_pos = static_cast<int*>(take(S * 4));
+  q.tile_hist = static_cast<int*>(take(ntiles * E * 4));
+  q.tile_base = static_cast<int*>(take(ntiles * E * 4));
+  q.bytes = off;
+  return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,8 +215,7 @@ size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k) {
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
   if (!shape_ok(T, E, k) || H < 1 || I < 1) return 0;
   const size_t pre = carve_prefill(nullptr, T, E, k, H, I).bytes;
-  const int32_t td = T < kMaxDecodeT ? T : kMaxDecodeT;
-  const size_t dec = T <= kSplitDecodeMaxT ? strata::decode_workspace_bytes(td, E, k, H, I) : 0;
+  const size_t dec = T <= kSplitDecodeMaxT ? carve_decode_perm(nullptr, T, E, k, H, I).bytes : 0;
   return pre > dec ? pre : dec;
 }
 
@@ -208,21 +261,22 @@ strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t*
   const void* ptrs[5] = {x, offsets, sorted_slot, expert_out, workspace};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  st = check_stats(w);
+  if (st != STRATA_OK) return st;
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
   if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
   PrefillWs p = carve_prefill(workspace, T, E, k, H, I);
   chunks_from_offsets_kernel<<<1, 1024, 0, stream>>>(offsets, E, p.chunks, p.n_chunks);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, stream);
+  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, p.xinfo, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_up(w->fmt, p.x16, sorted_slot, k, (int64_t)T * k, p.chunks, p.n_chunks,
-                              p.max_chunks,
-                              w->gate_codes, w->up_codes, w->gate_scales, w->up_scales, E, H, I,
-                              p.a16, stream);
+    e = strata::launch_ffn_up(w->fmt, p.x16, p.xinfo, sorted_slot, k, (int64_t)T * k, p.chunks,
+                              p.n_chunks, p.max_chunks, w->gate_codes, w->up_codes,
+                              w->gate_scales, w->up_scales, w->stats, E, H, I, p.a16, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_down(w->fmt, p.a16, sorted_slot, (int64_t)T * k, p.chunks, p.n_chunks,
-                                p.max_chunks,
-                                w->down_codes, w->down_scales, E, H, I, expert_out, stream);
+    e = strata::launch_ffn_down(w->fmt, p.a16, p.xinfo, sorted_slot, k, (int64_t)T * k, p.chunks,
+                                p.n_chunks, p.max_chunks, w->down_codes, w->down_scales, w->stats,
+                                E, H, I, expert_out, stream);
   return from_hip(e);
 }
 
@@ -271,40 +325,7 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   if (st != STRATA_OK) return st;
   st = check_route_shape(T, w->num_experts, k);
   if (st != STRATA_OK) return st;
-  if (T <= kMaxDecodeT && (opt_counts || opt_offsets || opt_sorted_slot))
-    return STRATA_ERR_INVALID_ARGUMENT;
   if (T == 0) return STRATA_OK;
-  if (T <= kMaxDecodeT && strata::decode_fits(T, w->num_experts, k, w->hidden, w->inter))
-    return strata_moe_decode(w, x, logits, T, k, y, accumulate, opt_topk_ids, opt_topk_w, workspace,
-                             workspace_bytes, stream);
-  if (T <= kSplitDecodeMaxT && !opt_counts && !opt_offsets && !opt_sorted_slot &&
-      strata::decode_fits(kMaxDecodeT, w->num_experts, k, w->hidden, w->inter)) {
-    const void* ptrs[4] = {x, logits, y, workspace};
-    for (const void* p : ptrs)
-      if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
-    if ((opt_topk_ids && !aligned16(opt_topk_ids)) || (opt_topk_w && !aligned16(opt_topk_w)))
-      return STRATA_ERR_INVALID_ARGUMENT;
-    const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
-    if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
-    // Balanced slices of at most kMaxDecodeT tokens in token order on the same stream (the slices
-    // share the workspace one after the other).  The decode kernels read x with 16-byte loads
-    // (a slice starts at a multiple of H >= 256 values) and logits, ids and weights per element.
-    const int32_t n = (T + kMaxDecodeT - 1) / kMaxDecodeT;
-    int32_t t0 = 0;
-    hipError_t e = hipSuccess;
-    for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
-      const int32_t ts = T / n + (i < T % n ? 1 : 0);
-      e = strata::launch_decode(w->fmt, x + (size_t)t0 * H, nullptr, 0.0f, logits + (size_t)t0 * E, ts,
-                                E, k, H, I,
-                                w->gate_codes, w->up_codes, w->down_codes, w->gate_scales,
-                                w->up_scales, w->down_scales, y + (size_t)t0 * H, accumulate,
-                                opt_topk_ids ? opt_topk_ids + (size_t)t0 * k : nullptr,
-                                opt_topk_w ? opt_topk_w + (size_t)t0 * k : nullptr, workspace,
-                                stream);
-      t0 += ts;
-    }
-    return from_hip(e);
-  }
   const void* ptrs[4] = {x, logits, y, workspace};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
@@ -313,6 +334,39 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
     if (p && !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
   if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  const bool want_perm = opt_counts || opt_offsets || opt_sorted_slot;
+  const bool decode_path =
+      (T <= kMaxDecodeT && strata::decode_fits(T, E, k, H, I)) ||
+      (T <= kSplitDecodeMaxT && strata::decode_fits(kMaxDecodeT, E, k, H, I));
+  if (decode_path) {
+    // Balanced slices of at most kMaxDecodeT tokens in token order on the same stream (the
+    // slices share the workspace one after the other).  The decode kernels read x with 16-byte
+    // loads (a slice starts at a multiple of H >= 256 values) and logits, ids and weights per
+    // element.
+    const DecodePermWs q = carve_decode_perm(workspace, T, E, k, H, I);
+    int* ids = opt_topk_ids ? opt_topk_ids : (want_perm ? q.ids : nullptr);
+    const int32_t n = (T + kMaxDecodeT - 1) / kMaxDecodeT;
+    int32_t t0 = 0;
+    hipError_t e = hipSuccess;
+    for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
+      const int32_t ts = T / n + (i < T % n ? 1 : 0);
+      e = strata::launch_decode(w->fmt, x + (size_t)t0 * H, nullptr, 0.0f, logits + (size_t)t0 * E, ts,
+                                E, k, H, I, w->gate_codes, w->up_codes, w->down_codes,
+                                w->gate_scales, w->up_scales, w->down_scales, y + (size_t)t0 * H,
+                                accumulate, ids ? ids + (size_t)t0 * k : nullptr,
+                                opt_topk_w ? opt_topk_w + (size_t)t0 * k : nullptr, workspace,
+                                stream);
+      t0 += ts;
+    }
+    if (e == hipSuccess && want_perm)
+      e = strata::launch_permute(ids, T, E, k, opt_counts ? opt_counts : q.counts,
+                                 opt_offsets ? opt_offsets : q.offsets,
+                                 opt_sorted_slot ? opt_sorted_slot : q.sorted_slot, q.slot_pos,
+                                 q.tile_hist, q.tile_base, nullptr, nullptr, stream);
+    return from_hip(e);
+  }
+  st = check_stats(w);
+  if (st != STRATA_OK) return st;
   PrefillWs p = carve_prefill(workspace, T, E, k, H, I);
   int* ids = opt_topk_ids ? opt_topk_ids : p.ids;
   float* rw = opt_topk_w ? opt_topk_w : p.w;
@@ -323,16 +377,15 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   if (e == hipSuccess)
     e = strata::launch_permute(ids, T, E, k, counts, offsets, sorted, p.slot_pos, p.tile_hist,
                                p.tile_base, p.chunks, p.n_chunks, stream);
-  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, stream);
+  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, p.xinfo, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_up(w->fmt, p.x16, sorted, k, (int64_t)T * k, p.chunks, p.n_chunks,
-                              p.max_chunks,
-                              w->gate_codes, w->up_codes, w->gate_scales, w->up_scales, E, H, I,
-                              p.a16, stream);
+    e = strata::launch_ffn_up(w->fmt, p.x16, p.xinfo, sorted, k, (int64_t)T * k, p.chunks,
+                              p.n_chunks, p.max_chunks, w->gate_codes, w->up_codes,
+                              w->gate_scales, w->up_scales, w->stats, E, H, I, p.a16, stream);
   if (e == hipSuccess)
-    e = strata::launch_ffn_down(w->fmt, p.a16, sorted, (int64_t)T * k, p.chunks, p.n_chunks,
-                                p.max_chunks,
-                                w->down_codes, w->down_scales, E, H, I, p.expert_out, stream);
+    e = strata::launch_ffn_down(w->fmt, p.a16, p.xinfo, sorted, k, (int64_t)T * k, p.chunks,
+                                p.n_chunks, p.max_chunks, w->down_codes, w->down_scales, w->stats,
+                                E, H, I, p.expert_out, stream);
   if (e == hipSuccess) e = strata::launch_combine(p.expert_out, rw, T, k, H, y, accumulate, stream);
   return from_hip(e);
 }
@@ -369,6 +422,17 @@ strata_status strata_moe_layer_residual(const strata_moe_weights* w, float* h, c
   if (e != hipSuccess) return STRATA_ERR_HIP;
   return strata_moe_layer(w, x, logits, T, k, h, 1, nullptr, nullptr, nullptr, nullptr, nullptr,
                           workspace, layer, stream);
+}
+
+strata_status strata_moe_weight_stats(const strata_moe_weights* w, strata_moe_expert_stats* stats,
+                                      hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  if (!stats || !aligned16(stats)) return STRATA_ERR_INVALID_ARGUMENT;
+  return from_hip(strata::launch_weight_stats(w->fmt, w->num_experts, w->hidden, w->inter,
+                                              w->gate_codes, w->up_codes, w->down_codes,
+                                              w->gate_scales, w->up_scales, w->down_scales, stats,
+                                              stream));
 }
 
 strata_status strata_moe_pack_matrix(int32_t fmt, int32_t n_mat, int32_t rows, int32_t K,

@@ -29,12 +29,6 @@ STRATA_DEVICE uint16_t f32_to_bf16(float f) {
 // fp16 bit pattern -> fp32 (exact; the hardware conversion handles subnormals).
 STRATA_DEVICE float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// fp32 -> fp16 with round to nearest even, saturating to the largest finite fp16.
-STRATA_DEVICE _Float16 f32_to_f16_sat(float f) {
-  f = __builtin_fminf(__builtin_fmaxf(f, -65504.0f), 65504.0f);
-  return (_Float16)f;
-}
-
 // (value, index) arg-max with ties to the lower index, across the 64 lanes of a wave.
 STRATA_DEVICE void wave_argmax(float& v, int& i) {
 #pragma unroll

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct strata_moe_expert_stats;
+
 namespace strata {
 
 // Chunk of one expert's segment of the sorted slot order, processed by one GEMM work unit.
@@ -36,20 +38,37 @@ hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int*
                           int* sorted_slot, int* slot_pos, int* tile_hist, int* tile_base,
                           Chunk* chunks, int* n_chunks, hipStream_t s);
 
-// x bf16 [T][H] -> fp16 in the fragment order of the grouped GEMM (see prefill.hip).
-hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, hipStream_t s);
+// Per-token range of the fp16 activations of the grouped GEMM: x16 = x * 2^sx with the row's
+// largest |x| in [2^14, 2^15) (sx = 0 for an all-zero row), n2 = sum of x16^2 in fp32.
+struct XInfo {
+  int32_t sx;
+  float n2;
+};
+
+// x bf16 [T][H] -> fp16 (scaled per token) in the fragment order of the grouped GEMM (see
+// prefill.hip), and each token's XInfo.
+hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo* xinfo,
+                           hipStream_t s);
 
 // S: the number of slots (sizes the work units; the chunk list itself is read on the device).
-hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k, int64_t S,
-                         const Chunk* chunks, const int* n_chunks, int max_chunks,
+hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const int* sorted_slot,
+                         int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_chunks,
                          const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
-                         const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
-                         hipStream_t s);
+                         const uint16_t* up_scales, const strata_moe_expert_stats* stats, int E,
+                         int H, int I, uint16_t* a16, hipStream_t s);
 
-hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot, int64_t S,
-                           const Chunk* chunks, const int* n_chunks, int max_chunks,
-                           const void* down_codes, const uint16_t* down_scales, int E, int H,
-                           int I, uint16_t* expert_out, hipStream_t s);
+hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
+                           const int* sorted_slot, int k, int64_t S, const Chunk* chunks,
+                           const int* n_chunks, int max_chunks, const void* down_codes,
+                           const uint16_t* down_scales, const strata_moe_expert_stats* stats,
+                           int E, int H, int I, uint16_t* expert_out, hipStream_t s);
+
+// Range statistics of a layer's tiled weights, one strata_moe_expert_stats per expert.
+hipError_t launch_weight_stats(int fmt, int E, int H, int I, const void* gate_codes,
+                               const void* up_codes, const void* down_codes,
+                               const uint16_t* gate_scales, const uint16_t* up_scales,
+                               const uint16_t* down_scales, strata_moe_expert_stats* stats,
+                               hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* expert_out, const float* w, int T, int k, int H,
                           float* y, int accumulate, hipStream_t s);

@@ -9,10 +9,15 @@
 // accumulation.
 //
 // Numerics.  A weight is d * (q - c0) with an fp16 scale d.  The decoder forms the fp16 product
-// fp16(d * (q - c0)) with one round-to-nearest-even (exact whenever q - c0 = +-0.5; otherwise the
-// product needs 12-13 significant bits and is rounded to fp16's 11).  Activations enter the
-// matrix cores as fp16 (bf16 inputs convert exactly within fp16's normal range); the SiLU*mul
-// intermediate is stored as fp16 and expert outputs as bf16.
+// fp16(d * 2^s * (q - c0)) with one round-to-nearest-even (exact whenever q - c0 = +-0.5;
+// otherwise the product needs 12-13 significant bits and is rounded to fp16's 11), where the
+// matrix's shift s (from the per-expert range statistics) puts its largest product in
+// [2^14, 2^15): no scale overflows fp16 and blocks within 2^28 of the largest stay normal.
+// Activations enter the matrix cores as fp16 scaled per token by 2^sx (the row's largest |x| in
+// [2^14, 2^15), so the bf16 values convert exactly).  The SiLU*mul intermediate is stored as fp16
+// scaled per row by the power of two that puts its Cauchy-Schwarz bound (|x| times the largest
+// gate-row and up-row norms) just below 2^15, and the expert outputs as bf16.  Every power of two
+// is taken back out exactly (ldexp) in the fp32 epilogues.
 //
 // Operand order.  Within every group of 8 consecutive reduction indices the GEMM feeds the
 // matrix cores the order P8 = {0,4,1,5,2,6,3,7}: the decoder then produces each fp16 pair from one
@@ -27,6 +32,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "strata_moe.h"
 
 namespace strata {
 
@@ -110,8 +116,9 @@ struct Q2Tab {
   uint32_t lo, hi;  // byte q of lo/hi = low/high byte of fp16(d * (q - 1.5))
 };
 
-STRATA_DEVICE Q2Tab q2_table(uint16_t dbits) {
-  const _Float16 d = __builtin_bit_cast(_Float16, dbits);
+// sh: the matrix's range shift (d * 2^sh is exact unless it falls below fp16's normal range).
+STRATA_DEVICE Q2Tab q2_table(uint16_t dbits, int sh) {
+  const _Float16 d = __builtin_ldexpf16(__builtin_bit_cast(_Float16, dbits), sh);
   const half2_t dd = {d, d};
   const half2_t p01 = dd * half2_t{(_Float16)-1.5f, (_Float16)-0.5f};  // one rounding each
   const half2_t p23 = dd * half2_t{(_Float16)0.5f, (_Float16)1.5f};
@@ -272,7 +279,7 @@ struct StageWeights {
 
 template <int FMT, int NF>
 STRATA_DEVICE void load_stage_weights(StageWeights<FMT>& sw, const uint8_t* stage, int ti0, int ti1,
-                                      int ri0, int ri1, int hh) {
+                                      int ri0, int ri1, int hh, int sh0, int sh1) {
   using GM = Geom<FMT, NF>;
   constexpr int CB = GM::kCB;
   const uint8_t* carea = stage + GM::kXBytes;
@@ -289,11 +296,11 @@ STRATA_DEVICE void load_stage_weights(StageWeights<FMT>& sw, const uint8_t* stag
   }
   const uint16_t d0 = sarea[ti0 * 128 + ri0 * 2 + hh], d1 = sarea[ti1 * 128 + ri1 * 2 + hh];
   if constexpr (FMT == 2) {
-    sw.t0 = q2_table(d0);
-    sw.t1 = q2_table(d1);
+    sw.t0 = q2_table(d0, sh0);
+    sw.t1 = q2_table(d1, sh1);
   } else {
-    const _Float16 e0 = __builtin_bit_cast(_Float16, d0) * (_Float16)4.0f;  // exact
-    const _Float16 e1 = __builtin_bit_cast(_Float16, d1) * (_Float16)4.0f;
+    const _Float16 e0 = __builtin_ldexpf16(__builtin_bit_cast(_Float16, d0), sh0 + 2);  // 4 d 2^s
+    const _Float16 e1 = __builtin_ldexpf16(__builtin_bit_cast(_Float16, d1), sh1 + 2);
     sw.d40 = half2_t{e0, e0};
     sw.d41 = half2_t{e1, e1};
   }
@@ -334,8 +341,30 @@ STRATA_DEVICE void mfma_step(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], const h
 // Row of a 32x32 accumulator tile held in register r of this lane.
 STRATA_DEVICE int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-STRATA_DEVICE float silu_mul(float g, float u) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+// The stored intermediate fp16(2^es * SiLU(g) * u) from the fp32 sums acc_g = 2^-ecg g and
+// acc_u of the scaled operands: SiLU(g) u 2^es = acc_g acc_u sigmoid(g) 2^es' with the row's
+// shifts folded into es by the caller; below 2^15 by construction (clamped to fp16's range
+// regardless).
+STRATA_DEVICE _Float16 silu_mul_scaled(float acc_g, float acc_u, int ecg, int es) {
+  const float g = __builtin_ldexpf(acc_g, ecg);
+  const float v = acc_g * acc_u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+  return (_Float16)__builtin_amdgcn_fmed3f(__builtin_ldexpf(v, es), -65504.0f, 65504.0f);
+}
+
+// Per-row exponents of a unit (one int per unit row, in LDS):
+//  up:   ecg (low 16 bits, signed) = -(sx + shift_gate), taking the gate sum back to g;
+//        es (high 16 bits, signed) = 15 - E with the row's bound n2 * norm_gate_up < 2^E;
+//  down: -(es + 2 sx + shift_gate + shift_up + shift_down), taking the down sum back to out.
+STRATA_DEVICE int a_exponent(const XInfo& xi, const strata_moe_expert_stats& st) {
+  const float b = xi.n2 * st.norm_gate_up;
+  return b > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(b) : 15;
+}
+
+template <bool UP>
+STRATA_DEVICE int row_exponent(const XInfo& xi, const strata_moe_expert_stats& st) {
+  const int es = a_exponent(xi, st);
+  if constexpr (UP) return (int)((uint32_t)(-(xi.sx + st.shift_gate)) & 0xFFFFu) | (es << 16);
+  else return -(es + 2 * xi.sx + st.shift_gate + st.shift_up + st.shift_down);
 }
 
 // Writes one slice's outputs, fragment by fragment, through two LDS staging buffers, with 16-byte
@@ -343,7 +372,8 @@ STRATA_DEVICE float silu_mul(float g, float u) {
 // slice, lane c < 16 of a tile holding the gate and lane c + 16 the up value of output 16 w + c ...
 // (acc0 = gate, acc1 = up columns); down: out = expert outputs (bf16, [slots][H]), 256 per slice.
 // dst_lds[r]: the destination row of unit row r (rows past the chunk repeat row 0, whose values
-// they equal, so every lane stores).  Each wave issues kStores stores per fragment.
+// they equal, so every lane stores); exps[r]: its exponents (row_exponent).  Each wave issues
+// kStores stores per fragment.
 template <int NF, bool UP>
 struct Epilogue {
   static constexpr int kRow = UP ? kUpOutRow : kDownOutRow;        // halfs per staged row
@@ -354,7 +384,8 @@ struct Epilogue {
 
 template <int NF, bool UP>
 STRATA_DEVICE void write_slice(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], uint16_t* epi,
-                               const int* dst_lds, uint16_t* __restrict__ out, int out_ld, int col0) {
+                               const int* dst_lds, const int* exps, uint16_t* __restrict__ out,
+                               int out_ld, int col0) {
   using EP = Epilogue<NF, UP>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 31, hh = lane >> 5;
@@ -372,17 +403,26 @@ STRATA_DEVICE void write_slice(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], uint1
     // copies at once would need 32 NF VGPRs).
     asm volatile("" : "+a"(acc0[f]), "+a"(acc1[f]));
     uint16_t* eb = e0 + (f & 1) * EP::kBuf;
+    // exponents of this lane's rows f*32 + 8 q + 4 hh + (0..3), q = r >> 2
+    int ex[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 v = *reinterpret_cast<const int4*>(exps + f * 32 + 8 * q + 4 * hh);
+      ex[4 * q] = v.x; ex[4 * q + 1] = v.y; ex[4 * q + 2] = v.z; ex[4 * q + 3] = v.w;
+    }
     if constexpr (UP) {
       // acc0 columns: gate of outputs w*32 + n; acc1: up of the same outputs
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) {
+        const int ecg = (int)(int16_t)(ex[r] & 0xFFFF), es = ex[r] >> 16;
         eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] =
-            __builtin_bit_cast(uint16_t, f32_to_f16_sat(silu_mul(acc0[f][r], acc1[f][r])));
+            __builtin_bit_cast(uint16_t, silu_mul_scaled(acc0[f][r], acc1[f][r], ecg, es));
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] = f32_to_bf16(acc0[f][r]);
-        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow + 32] = f32_to_bf16(acc1[f][r]);
+        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] = f32_to_bf16(__builtin_ldexpf(acc0[f][r], ex[r]));
+        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow + 32] = f32_to_bf16(__builtin_ldexpf(acc1[f][r], ex[r]));
       }
     }
     // the buffer is complete for every wave; (the other buffer's previous reads finished before
@@ -412,9 +452,9 @@ struct StageState {
 // Stage set-up: weight words and tables, step-0 fragments and weights of the stage in buffer st.
 template <int FMT, int NF>
 STRATA_DEVICE void stage_setup(StageState<FMT, NF>& ss, const uint8_t* st, int ti0, int ti1, int ri0,
-                               int ri1, const Q2Sel& ksel) {
+                               int ri1, int sh0, int sh1, const Q2Sel& ksel) {
   const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
-  load_stage_weights<FMT, NF>(ss.sw, st, ti0, ti1, ri0, ri1, hh);
+  load_stage_weights<FMT, NF>(ss.sw, st, ti0, ti1, ri0, ri1, hh, sh0, sh1);
   read_frags<NF>(st, m, hh, 0, ss.a[0]);
   decode_step<FMT>(ss.sw, 0, ss.b[0], ksel);
 }
@@ -507,12 +547,16 @@ STRATA_DEVICE void stage_barrier(int n) {
 //
 // src/ld: the activation rows (rows_lds[r]: row of unit row r); wt: this lane's weight pieces of
 // slice 0, stage 0; wslice / sslice: byte / fp16 distance between slices in the tiled weights;
-// (ti, ri): this lane's B rows in the LDS weight tiles; out/out_ld/ocols: destination and the
-// columns per slice.
+// (ti, ri): this lane's B rows in the LDS weight tiles; sh0 / sh1: the range shifts of the two
+// weight streams; out/out_ld/ocols: destination and the columns per slice.  xi: the token range
+// of unit row threadIdx.x (if it has one), st: the expert's range statistics; once every wave
+// has taken its activation offsets from rows_lds, the rows' exponents (row_exponent) replace them
+// there for the epilogues.
 template <int FMT, int NF, bool UP>
 STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src, int ld, int K,
-                            const int* rows_lds, const int* dst_lds, const WeightTile& wt,
+                            int* rows_lds, const int* dst_lds, const WeightTile& wt,
                             size_t wslice, size_t sslice, int ti0, int ti1, int ri0, int ri1,
+                            int sh0, int sh1, const XInfo& xi, const strata_moe_expert_stats& st,
                             uint16_t* __restrict__ out, int out_ld, int ocols, uint8_t* lds) {
   constexpr int kEpi = UP ? kUpEpiBytes : kDownEpiBytes;
   using P = Pipe<FMT, NF, kGemmLds - kRowsBytes - kEpi>;
@@ -537,9 +581,12 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
       cursor_advance<FMT>(cc);
     }
   stage_barrier<P::kPer * (P::kPD - 1)>(ops_after<P::kPer, P::kPD>(0, -1, NT, NKs, kSt));
+  // (every wave has read rows_lds; the stage barriers of the first slice order these writes
+  // before the epilogue's reads)
+  if ((int)threadIdx.x < NF * 32) rows_lds[threadIdx.x] = row_exponent<UP>(xi, st);
   const Q2Sel ksel = q2_sel();
   StageState<FMT, NF> ss;
-  stage_setup<FMT, NF>(ss, lds, ti0, ti1, ri0, ri1, ksel);
+  stage_setup<FMT, NF>(ss, lds, ti0, ti1, ri0, ri1, sh0, sh1, ksel);
   int j = 0, rb = 0;  // stage and its ring buffer
   int last_end = -1;  // iteration of the latest slice end
   for (int sl = 0; sl < u.nsl; ++sl) {
@@ -558,13 +605,13 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
       cursor_advance<FMT>(cc);
       stage_barrier<P::kPer * (P::kPD - 1)>(ops_after<P::kPer, P::kPD>(j + 1, last_end, NT, NKs, kSt));
       // (the set-up writes the even operands; step 3 uses the odd ones)
-      stage_setup<FMT, NF>(ss, lds + nb * P::kStage, ti0, ti1, ri0, ri1, ksel);
+      stage_setup<FMT, NF>(ss, lds + nb * P::kStage, ti0, ti1, ri0, ri1, sh0, sh1, ksel);
       mfma_step<NF>(acc0, acc1, ss.a[1], ss.b[1], kPre, NF);
       __builtin_amdgcn_sched_barrier(0);
       rb = nb;
     }
     // (the staging area is separate from the stage ring, which the next slice's copies fill)
-    write_slice<NF, UP>(acc0, acc1, epi, dst_lds, out, out_ld, (u.slice0 + sl) * ocols);
+    write_slice<NF, UP>(acc0, acc1, epi, dst_lds, rows_lds, out, out_ld, (u.slice0 + sl) * ocols);
     last_end = j - 1;
   }
 }
@@ -575,11 +622,12 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
 
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
-    const uint16_t* __restrict__ x16, const int* __restrict__ sorted_slot, int k,
-    const Chunk* __restrict__ chunks, const int* __restrict__ n_chunks,
-    const uint8_t* __restrict__ gate_codes, const uint8_t* __restrict__ up_codes,
-    const uint16_t* __restrict__ gate_scales, const uint16_t* __restrict__ up_scales, int H, int I,
-    int G, uint16_t* __restrict__ a16) {
+    const uint16_t* __restrict__ x16, const XInfo* __restrict__ xinfo,
+    const int* __restrict__ sorted_slot, int k, const Chunk* __restrict__ chunks,
+    const int* __restrict__ n_chunks, const uint8_t* __restrict__ gate_codes,
+    const uint8_t* __restrict__ up_codes, const uint16_t* __restrict__ gate_scales,
+    const uint16_t* __restrict__ up_scales, const strata_moe_expert_stats* __restrict__ stats,
+    int H, int I, int G, uint16_t* __restrict__ a16) {
   extern __shared__ __align__(16) uint8_t smem[];
   int* rows_lds = reinterpret_cast<int*>(smem + kGemmLds - kRowsBytes);
   int* dst_lds = rows_lds + kChunkRows;
@@ -591,10 +639,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
   const size_t row0 = (size_t)u.expert * I + 128 * u.slice0 + 64 * (wave & 1);
   const WeightTile wt = weight_tile<FMT>(wave < 2 ? gate_codes : up_codes,
                                          wave < 2 ? gate_scales : up_scales, row0, nkt);
-  for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads) {
-    const int rr = r < u.nrows ? r : 0;
-    rows_lds[r] = sorted_slot[u.row_start + rr] / k;
+  const strata_moe_expert_stats st = stats[u.expert];
+  XInfo xi{0, 0.0f};
+  if ((int)threadIdx.x < u.nfrag * 32) {  // one unit row per thread (at most 224)
+    const int r = threadIdx.x, rr = r < u.nrows ? r : 0;
+    const int t = sorted_slot[u.row_start + rr] / k;
+    rows_lds[r] = t;
     dst_lds[r] = u.row_start + rr;
+    xi = xinfo[t];  // (first used after run_unit's first stage barrier)
   }
   __syncthreads();
   // a slice is 128 gate (and up) rows = 32 groups of 4
@@ -603,7 +655,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
   const int ri = (wave & 1) * 32 + (threadIdx.x & 31);
 #define STRATA_UP_UNIT(NF)                                                                        \
   run_unit<FMT, NF, true>(u, x16, H, H, rows_lds, dst_lds, wt, wsl, ssl, wave >> 1, 2 + (wave >> 1), \
-                          ri, ri, a16, I, 128, smem)
+                          ri, ri, st.shift_gate, st.shift_up, xi, st, a16, I, 128, smem)
   switch (u.nfrag) {
     case 1: STRATA_UP_UNIT(1); break;
     case 2: STRATA_UP_UNIT(2); break;
@@ -622,10 +674,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
 
 template <int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
-    const uint16_t* __restrict__ a16, const int* __restrict__ sorted_slot,
-    const Chunk* __restrict__ chunks, const int* __restrict__ n_chunks,
-    const uint8_t* __restrict__ down_codes, const uint16_t* __restrict__ down_scales, int H, int I,
-    int G, uint16_t* __restrict__ expert_out) {
+    const uint16_t* __restrict__ a16, const XInfo* __restrict__ xinfo,
+    const int* __restrict__ sorted_slot, int k, const Chunk* __restrict__ chunks,
+    const int* __restrict__ n_chunks, const uint8_t* __restrict__ down_codes,
+    const uint16_t* __restrict__ down_scales, const strata_moe_expert_stats* __restrict__ stats,
+    int H, int I, int G, uint16_t* __restrict__ expert_out) {
   extern __shared__ __align__(16) uint8_t smem[];
   int* rows_lds = reinterpret_cast<int*>(smem + kGemmLds - kRowsBytes);
   int* dst_lds = rows_lds + kChunkRows;
@@ -636,10 +689,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
   // wave w copies rows 256 slice + 64 w .. + 63 of the expert
   const size_t row0 = (size_t)u.expert * H + 256 * u.slice0 + 64 * wave;
   const WeightTile wt = weight_tile<FMT>(down_codes, down_scales, row0, nkt);
-  for (int r = threadIdx.x; r < u.nfrag * 32; r += kGemmThreads) {
-    const int rr = r < u.nrows ? r : 0;
+  const strata_moe_expert_stats st = stats[u.expert];
+  XInfo xi{0, 0.0f};
+  if ((int)threadIdx.x < u.nfrag * 32) {  // one unit row per thread (at most 224)
+    const int r = threadIdx.x, rr = r < u.nrows ? r : 0;
+    const int slot = sorted_slot[u.row_start + rr];
     rows_lds[r] = u.row_start + rr;
-    dst_lds[r] = sorted_slot[u.row_start + rr];
+    dst_lds[r] = slot;
+    xi = xinfo[slot / k];  // (first used after run_unit's first stage barrier)
   }
   __syncthreads();
   // a slice is 256 rows = 64 groups of 4
@@ -648,7 +705,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
   const int ri = threadIdx.x & 31;
 #define STRATA_DOWN_UNIT(NF)                                                                      \
   run_unit<FMT, NF, false>(u, a16, I, I, rows_lds, dst_lds, wt, wsl, ssl, wave, wave, ri, 32 + ri, \
-                           expert_out, H, 256, smem)
+                           st.shift_down, st.shift_down, xi, st, expert_out, H, 256, smem)
   switch (u.nfrag) {
     case 1: STRATA_DOWN_UNIT(1); break;
     case 2: STRATA_DOWN_UNIT(2); break;
@@ -662,12 +719,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// x bf16 -> fp16 in P8 order (one thread per 8 values).
+// x bf16 -> fp16 in P8 order, scaled per token: one wave per row.  The row's largest |x| (bf16
+// magnitudes order as their bit patterns) fixes sx with max |x| 2^sx in [2^14, 2^15); each value
+// is then x 2^sx, exact in fp16 (8 significant bits, no overflow; values below 2^-17 of the
+// scaled maximum round into fp16's subnormals), and n2 = sum of the squares of the fp16 values.
 
-__global__ void x_to_f16_kernel(const uint16_t* __restrict__ x, size_t n8, uint16_t* __restrict__ x16) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const u32x4_t v = reinterpret_cast<const u32x4_t*>(x)[i];
+constexpr int kXRowsPerBlock = 4;
+constexpr int kXRegPieces = 8;  // 16-byte pieces a lane keeps in registers (rows up to 4096)
+
+STRATA_DEVICE uint32_t bf16_pair_max_mag(uint32_t v, uint32_t m) {
+  return max(m, max(v & 0x7FFFu, (v >> 16) & 0x7FFFu));
+}
+
+STRATA_DEVICE u32x4_t x_piece_to_f16(const u32x4_t v, int sx, float& n2) {
   uint16_t in[8];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -678,11 +742,52 @@ __global__ void x_to_f16_kernel(const uint16_t* __restrict__ x, size_t n8, uint1
   u32x4_t o;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const uint32_t lo = __builtin_bit_cast(uint16_t, f32_to_f16_sat(bf16_to_f32(in[P8[2 * m]])));
-    const uint32_t hi = __builtin_bit_cast(uint16_t, f32_to_f16_sat(bf16_to_f32(in[P8[2 * m + 1]])));
-    o[m] = lo | (hi << 16);
+    const _Float16 lo = (_Float16)__builtin_ldexpf(bf16_to_f32(in[P8[2 * m]]), sx);
+    const _Float16 hi = (_Float16)__builtin_ldexpf(bf16_to_f32(in[P8[2 * m + 1]]), sx);
+    const float flo = (float)lo, fhi = (float)hi;
+    n2 = __builtin_fmaf(flo, flo, n2);
+    n2 = __builtin_fmaf(fhi, fhi, n2);
+    o[m] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
-  reinterpret_cast<u32x4_t*>(x16)[i] = o;
+  return o;
+}
+
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                       uint16_t* __restrict__ x16,
+                                                       XInfo* __restrict__ xinfo) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kXRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int n8 = H / 8;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)t * H);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(x16 + (size_t)t * H);
+  u32x4_t v[kXRegPieces];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < kXRegPieces; ++j) {
+    const int i = lane + 64 * j;
+    v[j] = i < n8 ? src[i] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mx = bf16_pair_max_mag(v[j][m], mx);
+  }
+  for (int i = lane + 64 * kXRegPieces; i < n8; i += 64) {  // rows longer than 4096
+    const u32x4_t w = src[i];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mx = bf16_pair_max_mag(w[m], mx);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+  // max |x| in [2^(e-1), 2^e): sx = 15 - e
+  const int sx = mx ? 15 - __builtin_amdgcn_frexp_expf(bf16_to_f32((uint16_t)mx)) : 0;
+  float n2 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kXRegPieces; ++j) {
+    const int i = lane + 64 * j;
+    if (i < n8) dst[i] = x_piece_to_f16(v[j], sx, n2);
+  }
+  for (int i = lane + 64 * kXRegPieces; i < n8; i += 64) dst[i] = x_piece_to_f16(src[i], sx, n2);
+  n2 = wave_sum(n2);
+  if (lane == 0) xinfo[t] = XInfo{sx, n2};
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -803,17 +908,18 @@ static void allow_big_lds() {
   });
 }
 
-hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, hipStream_t s) {
-  const size_t n8 = (size_t)T * H / 8;
-  x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(x, n8, x16);
+hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo* xinfo,
+                           hipStream_t s) {
+  const unsigned grid = (unsigned)((T + kXRowsPerBlock - 1) / kXRowsPerBlock);
+  x_to_f16_kernel<<<grid, 256, 0, s>>>(x, T, H, x16, xinfo);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, int k, int64_t S,
-                         const Chunk* chunks, const int* n_chunks, int max_chunks_,
+hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const int* sorted_slot,
+                         int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_chunks_,
                          const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
-                         const uint16_t* up_scales, int E, int H, int I, uint16_t* a16,
-                         hipStream_t s) {
+                         const uint16_t* up_scales, const strata_moe_expert_stats* stats, int E,
+                         int H, int I, uint16_t* a16, hipStream_t s) {
   (void)E;
   const int G = slices_per_unit(I / 128, 1, S);
   const int grid = grid_for_units((int64_t)max_chunks_ * (I / 128 / G));
@@ -821,29 +927,34 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const int* sorted_slot, i
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
   allow_big_lds();
   if (fmt == 2)
-    ffn_up_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(x16, sorted_slot, k, chunks, n_chunks, gc,
-                                                          uc, gate_scales, up_scales, H, I, G, a16);
+    ffn_up_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(x16, xinfo, sorted_slot, k, chunks,
+                                                          n_chunks, gc, uc, gate_scales, up_scales,
+                                                          stats, H, I, G, a16);
   else
-    ffn_up_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(x16, sorted_slot, k, chunks, n_chunks, gc,
-                                                          uc, gate_scales, up_scales, H, I, G, a16);
+    ffn_up_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(x16, xinfo, sorted_slot, k, chunks,
+                                                          n_chunks, gc, uc, gate_scales, up_scales,
+                                                          stats, H, I, G, a16);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const int* sorted_slot, int64_t S,
-                           const Chunk* chunks, const int* n_chunks, int max_chunks_,
-                           const void* down_codes, const uint16_t* down_scales, int E, int H,
-                           int I, uint16_t* expert_out, hipStream_t s) {
+hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
+                           const int* sorted_slot, int k, int64_t S, const Chunk* chunks,
+                           const int* n_chunks, int max_chunks_, const void* down_codes,
+                           const uint16_t* down_scales, const strata_moe_expert_stats* stats,
+                           int E, int H, int I, uint16_t* expert_out, hipStream_t s) {
   (void)E;
   const int G = slices_per_unit(H / 256, 2, S);
   const int grid = grid_for_units((int64_t)max_chunks_ * (H / 256 / G));
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
   allow_big_lds();
   if (fmt == 2)
-    ffn_down_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(a16, sorted_slot, chunks, n_chunks, dc,
-                                                            down_scales, H, I, G, expert_out);
+    ffn_down_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(a16, xinfo, sorted_slot, k, chunks,
+                                                            n_chunks, dc, down_scales, stats, H, I,
+                                                            G, expert_out);
   else
-    ffn_down_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(a16, sorted_slot, chunks, n_chunks, dc,
-                                                            down_scales, H, I, G, expert_out);
+    ffn_down_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(a16, xinfo, sorted_slot, k, chunks,
+                                                            n_chunks, dc, down_scales, stats, H, I,
+                                                            G, expert_out);
   return hipGetLastError();
 }
 

@@ -84,6 +84,26 @@ typedef enum {
 } strata_qformat;
 
 /*
+ * Per-expert range statistics of a layer's weights (device array [E], written once by
+ * strata_moe_weight_stats).  The prefill path feeds fp16 operands to the matrix cores; these
+ * numbers let it place every operand inside fp16's range exactly, by powers of two, whatever
+ * the block scales and the activations' magnitude:
+ *   shift_gate, shift_up, shift_down: the exponent s of each matrix such that its largest
+ *     |d| * max|q - c0| times 2^s lies in (2^14, 2^15]; the GEMM uses fp16(d * 2^s * (q - c0))
+ *     and takes 2^-s back out of its fp32 sums (0 for an all-zero matrix);
+ *   norm_gate_up: an upper bound of (max over rows of the 2-norm of the shifted gate rows) times
+ *     (the same for the up rows).  With x's own 2-norm it bounds |SiLU(g) * u| by Cauchy-Schwarz,
+ *     and so fixes a per-row power of two that keeps the intermediate a below 2^15 in fp16.
+ * The decode path reads the scales directly and does not use these.
+ */
+typedef struct strata_moe_expert_stats {
+  int32_t shift_gate;
+  int32_t shift_up;
+  int32_t shift_down;
+  float norm_gate_up;
+} strata_moe_expert_stats;
+
+/*
  * One layer's expert weights, all device pointers, expert-major, each matrix in the tiled layout:
  *   gate W_g and up W_u: per expert an [I][H] matrix (rows = intermediate features, reduction
  *     along H): codes [E][I/4][H/64][4][2][cb], scales [E][I/4][H/64][4][2];
@@ -91,6 +111,11 @@ typedef enum {
  *     codes [E][H/4][I/64][4][2][cb], scales [E][H/4][I/64][4][2];
  * with cb = 8 (Q2) or 12 (Q3).  Expert e's arrays start at e times the per-expert size (the E
  * matrices of one kind are also one tiled matrix of E*R rows).
+ * Field order: format and sizes, then gate and up codes, gate and up scales, down codes, down
+ * scales (byte offsets on LP64: 0, 4, 8, 12, 16, 24, 32, 40, 48, 56), then stats (offset 64):
+ * the range statistics above, required by the prefill path (strata_moe_expert_ffn, and
+ * strata_moe_layer and its callers when they take it) and ignored by the decode path (may be
+ * NULL there).
  */
 typedef struct strata_moe_weights {
   int32_t fmt;          /* strata_qformat */
@@ -99,11 +124,21 @@ typedef struct strata_moe_weights {
   int32_t inter;        /* I: multiple of 128 */
   const void* gate_codes;
   const void* up_codes;
-  const void* down_codes;
   const uint16_t* gate_scales;
   const uint16_t* up_scales;
+  const void* down_codes;
   const uint16_t* down_scales;
+  const strata_moe_expert_stats* stats;
 } strata_moe_weights;
+
+/*
+ * Range statistics of w's tiled weights (see strata_moe_expert_stats): a one-time load step
+ * after strata_moe_pack_matrix, like the repack itself.  w->stats is not read.
+ *   stats  device array [w->num_experts] (written)
+ * Errors as for the compute calls (w's sizes and pointers are validated).
+ */
+strata_status strata_moe_weight_stats(const strata_moe_weights* w, strata_moe_expert_stats* stats,
+                                      hipStream_t stream);
 
 /*
  * Router: per-token top-k selection and weights.
@@ -148,10 +183,19 @@ strata_status strata_moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, 
  * The pages call the expert matrix multiply the heaviest computation and describe dequantizing
  * the low-bit blocks during the multiply ("Two-Day Port, 8x Faster Prefill: Strata Engine
  * Benchmarked", Where Strata Is Fast); the gate/up/SiLU-mul/down form is this library's
- * definition.  Precision: the products run on fp16 matrix cores with fp32 accumulation; each
- * dequantized weight d * (q - c0) is rounded once to fp16, x is converted to fp16 (saturating at
- * +-65504), a is rounded to fp16 and out to bf16.  The result stays within 5e-3 relative L2 of
- * the exact (fp64) layer for unit-scale activations.
+ * definition.  Precision: the products run on fp16 matrix cores with fp32 accumulation, every
+ * operand brought into fp16's range by exact powers of two that the fp32 epilogues take back out:
+ *  - x: each token row is scaled so that its largest |x| lies in [2^14, 2^15); the bf16 values
+ *    then convert to fp16 exactly (down to 2^-31 of the row's largest);
+ *  - weights: each dequantized weight is fp16(d * 2^s * (q - c0)), one rounding, with the
+ *    matrix's shift s from w->stats (no overflow for any finite scale; blocks within 2^28 of the
+ *    matrix's largest stay normal);
+ *  - a = SiLU(g) * u: rounded once to fp16 after scaling by a per-row power of two that puts the
+ *    row's Cauchy-Schwarz bound |x| * max|W_g row| * max|W_u row| just below 2^15;
+ *  - out is rounded to bf16.
+ * The result stays within 5e-3 per-row relative L2 of the exact (fp64) layer for activation
+ * rows whose largest |x| lies in [2^-100, 2^100] and any finite block scales (outside that the
+ * token scaling stops at 2^+-113 and tiny rows lose precision); w->stats must not be NULL.
  *
  *   x           bf16 [T][H] (uint16 bit patterns)
  *   offsets, sorted_slot  as produced by strata_moe_permute for this (T, k, E)
@@ -167,7 +211,10 @@ strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t*
 /*
  * Combine: y[t] = sum_{j = 0..k-1, ascending} topk_w[t][j] * expert_out[t*k + j]   (fp32),
  * and with accumulate != 0, y[t] += that sum instead (the residual add of a layer stack).
- * The pages do not spell the combine out; this is the weighted sum of the routed outputs.
+ * The pages say each token's output comes from the 10 experts it is routed to ("Strata vs
+ * Llama.cpp vs vLLM", transcript at 08:23; "Local AI Is Now 6x Faster on Your PC", key
+ * technological idea) without spelling the combination out; the router-weighted sum is this
+ * library's definition.
  *   expert_out bf16 [T*k][H], topk_w fp32 [T][k], y fp32 [T][H].
  */
 strata_status strata_moe_combine(const uint16_t* expert_out, const float* topk_w, int32_t T,
@@ -195,15 +242,21 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * One-call layer: y (=, or += with accumulate) MoE(x).  T <= 8 runs strata_moe_decode's path
- * when the shape is within its limits.  9 <= T <= 48 with opt_counts, opt_offsets and
- * opt_sorted_slot all NULL runs the same decode path on consecutive slices of at most 8 tokens
- * (the layer's tokens are independent; with few rows per expert, streaming each touched expert
- * once per slice is faster than the grouped GEMMs).  Otherwise route -> permute -> expert_ffn ->
- * combine.
- * Each opt_* pointer may be NULL; when given it receives that intermediate (same layout as the
- * staged calls).  opt_counts, opt_offsets and opt_sorted_slot are only produced on the T > 8
- * path and must be NULL for T <= 8 (STRATA_ERR_INVALID_ARGUMENT otherwise).
+ * One-call layer: y (=, or += with accumulate) MoE(x): route each token to k of the E experts,
+ * run the experts it picked, sum their outputs weighted by the router.  The pages' layer routes
+ * each token to 10 of 512 experts ("Strata vs Llama.cpp vs vLLM", transcript at 08:23; "Two-Day
+ * Port, 8x Faster Prefill: Strata Engine Benchmarked", Where Strata Is Fast); the steps and their
+ * definitions are those of strata_moe_route, strata_moe_permute, strata_moe_expert_ffn and
+ * strata_moe_combine.
+ * T <= 8 runs strata_moe_decode's path when the shape is within its limits.  9 <= T <= 48 runs
+ * the same decode path on consecutive slices of at most 8 tokens (the layer's tokens are
+ * independent; with few rows per expert, streaming each touched expert once per slice is faster
+ * than the grouped GEMMs).  Otherwise route -> permute -> expert_ffn -> combine.
+ * Each opt_* pointer may be NULL; when given it receives that intermediate in the layout of the
+ * staged calls: opt_topk_ids int32 [T][k], opt_topk_w fp32 [T][k], opt_counts int32 [E],
+ * opt_offsets int32 [E+1], opt_sorted_slot int32 [T*k].  On the decode paths the permutation is
+ * produced, when asked for, by one extra counting-sort launch over the routing result.
+ * Workspace: at least strata_moe_workspace_bytes(T, E, k, H, I).
  */
 strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, const float* logits,
                                int32_t T, int32_t k, float* y, int32_t accumulate,

@@ -4,6 +4,7 @@ made here: every call below fails validation or is the T = 0 no-op)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -37,8 +38,31 @@ def test_exports_every_declared_symbol(L):
     assert sorted(sm.EXPORTS) == names
 
 
-def weights(fmt=2, E=512, H=3072, I=768, ptr=A):
-    return sm.CWeights(fmt, E, H, I, ptr, ptr, ptr, ptr, ptr, ptr)
+def weights(fmt=2, E=512, H=3072, I=768, ptr=A, stats=A):
+    return sm.CWeights(fmt, E, H, I, ptr, ptr, ptr, ptr, ptr, ptr, stats)
+
+
+FIELDS = ["fmt", "num_experts", "hidden", "inter", "gate_codes", "up_codes", "gate_scales",
+          "up_scales", "down_codes", "down_scales", "stats"]
+
+
+def test_weights_struct_layout(tmp_path):
+    """The header's struct, compiled by the host C compiler, has the documented field order and
+    offsets, and the binding's ctypes mirror matches it field for field."""
+    src = tmp_path / "offsets.c"
+    body = ", ".join(f"offsetof(strata_moe_weights, {f})" for f in FIELDS)
+    fmt = " ".join(["%zu"] * (len(FIELDS) + 2))
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "strata_moe.h"\n'
+                   f'int main(void) {{ printf("{fmt}\\n", {body}, sizeof(strata_moe_weights), '
+                   'sizeof(strata_moe_expert_stats)); return 0; }\n')
+    exe = tmp_path / "offsets"
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                           "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)], text=True).split()]
+    assert got[:len(FIELDS)] == [0, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64]
+    assert got[len(FIELDS):] == [72, 16]
+    assert [getattr(sm.CWeights, f).offset for f in FIELDS] == got[:len(FIELDS)]
+    assert ctypes.sizeof(sm.CWeights) == 72 and ctypes.sizeof(sm.CExpertStats) == 16
 
 
 def test_status_strings(L):
@@ -81,9 +105,17 @@ def test_weights_validation(L):
     assert call(weights(), k=0) == INVAL
     assert call(weights(), wsb=ws - 1) == WS
     assert L.strata_moe_layer(None, A, A, 16, 4, A, 0, None, None, None, None, None, A, ws, None) == INVAL
-    # decode path: permutation outputs are not produced for T <= 8
+    # the prefill path needs the weights' range statistics (aligned)
+    assert call(weights(stats=0)) == INVAL
+    assert call(weights(stats=MIS)) == INVAL
+    assert L.strata_moe_expert_ffn(ctypes.byref(weights(stats=0)), A, 8192, 10, A, A, A, A, ws,
+                                   None) == INVAL
+    # the decode paths also produce the permutation on request: the workspace covers it
+    w4 = L.strata_moe_workspace_bytes(4, 512, 10, 3072, 768)
+    w48 = L.strata_moe_workspace_bytes(48, 512, 10, 3072, 768)
+    assert w4 >= 3 * 40 * 4 + 2 * 512 * 4 and w48 >= 3 * 480 * 4 + 2 * 512 * 4
     assert L.strata_moe_layer(ctypes.byref(weights()), A, A, 4, 10, A, 0, None, None, A, None, None,
-                              A, ws, None) == INVAL
+                              A, w4 - 1, None) == WS
     assert L.strata_moe_decode(ctypes.byref(weights()), A, A, 9, 10, A, 0, None, None, A, ws,
                                None) == UNSUP
     assert L.strata_moe_expert_ffn(ctypes.byref(weights()), A, 8192, 10, A, A, A, A, ws - 1,
@@ -129,6 +161,15 @@ def test_combine_and_rmsnorm_validation(L):
     assert L.strata_moe_rmsnorm(A, 4, 3072, ctypes.c_float(-1.0), A, None) == INVAL
     assert L.strata_moe_rmsnorm(A, 4, 3071, ctypes.c_float(1e-6), A, None) == UNSUP
     assert L.strata_moe_rmsnorm(MIS, 4, 3072, ctypes.c_float(1e-6), A, None) == INVAL
+
+
+def test_weight_stats_validation(L):
+    assert L.strata_moe_weight_stats(ctypes.byref(weights()), None, None) == INVAL
+    assert L.strata_moe_weight_stats(ctypes.byref(weights()), MIS, None) == INVAL
+    assert L.strata_moe_weight_stats(ctypes.byref(weights(fmt=4)), A, None) == INVAL
+    assert L.strata_moe_weight_stats(ctypes.byref(weights(I=800)), A, None) == UNSUP
+    assert L.strata_moe_weight_stats(ctypes.byref(weights(ptr=MIS)), A, None) == INVAL
+    assert L.strata_moe_weight_stats(None, A, None) == INVAL
 
 
 def test_pack_matrix_validation(L):
