@@ -19,7 +19,12 @@ value = whole-job layer-tokens/s = T * steps / timed seconds, inputs resident in
 roofline: HBM-bound decode (touched experts' packed bytes per layer call / call duration, peak
 8 TB/s) and MFMA-bound prefill (6*T*k*H*I FLOP per expert-FFN call / call duration, dense fp16
 peak 2.5 PFLOP/s), durations from HIP events on the stream the library launches on.
-cpu_baseline: the CPU oracle (single-threaded C, fp64) on a bounded sample of decode layers.
+Every timed leg is preceded by ~0.3 s of untimed back-to-back calls (--preroll-s) so that it
+measures the GPU's sustained clock rather than its ramp from idle, then by the warmup steps.
+
+cpu_baseline: the CPU oracle (single-threaded C, fp64, one pinned core) on bounded samples: whole
+decode layers (the headline workload), token samples of the prefill chunk and the skewed 3-bit
+layer, and two layers of the 48-layer stack extrapolated to 48 (key "configs").
 """
 from __future__ import annotations
 
@@ -99,6 +104,24 @@ def copy_calibration(mb, stream):
     log(f"copy calibration: 3 copies of {n} bytes")
 
 
+def preroll(fn, stream, seconds):
+    """Runs fn back to back for about `seconds` before a leg's warmup and timed steps (not part of
+    either): a GPU that was idle while the inputs were generated ramps its clock up over several
+    milliseconds, and a timed region of a few milliseconds would otherwise measure the ramp, not
+    the sustained rate (measured: 39.2 vs 37.2 us per decode layer, 1.72 vs 1.53 ms per prefill
+    layer)."""
+    import torch
+
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def bench_decode(args, stream, shape=None):
     import torch
 
@@ -152,6 +175,7 @@ def bench_decode(args, stream, shape=None):
     full, rem = divmod(args.steps, n_layers)
     graph = capture(0, n_layers)
     tail = capture(0, rem) if rem else None
+    preroll(lambda i: graph.replay(), stream, args.preroll_s)
     for _ in range(2):
         graph.replay()
     steps = args.steps
@@ -173,6 +197,7 @@ def bench_decode(args, stream, shape=None):
         "value": s.T / (ms_per_step * 1e-3),
         "touched_experts_mean": float(np.mean(touched)),
         "bytes_per_layer": algo_bytes,
+        "preroll_s": args.preroll_s,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("decode_t4_traffic.txt", "decode.hip"),
@@ -422,6 +447,7 @@ def bench_prefill(args, stream, name):
     def step(i):
         sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=stream)
 
+    preroll(step, stream, args.preroll_s)
     for i in range(max(2, args.warmup // 10)):
         step(i)
     steps = args.prefill_steps
@@ -441,7 +467,7 @@ def bench_prefill(args, stream, name):
     def ffn(i):
         sm.strata_moe_expert_ffn(L.w, L.x, s.k, offsets, ss, out, ws, stream=stream)
 
-    ffn(0)
+    preroll(ffn, stream, args.preroll_s)
     ms_ffn = event_time_ms(ffn, steps, stream) / steps
     tflops_ffn = flops / (ms_ffn * 1e-3) / 1e12
     tflops_layer = flops / (ms_per_step * 1e-3) / 1e12
@@ -514,7 +540,7 @@ def bench_stack(args, stream):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(torch.cuda.current_stream())
-            g.replay()
+            preroll(lambda i: g.replay(), stream, args.preroll_s)
             ms = event_time_ms(lambda i: g.replay(), steps, stream) / steps
             gbs = sum(touched) * s.expert_bytes / (ms * 1e-3) / 1e9
             out[tag] = {"T": s.T, "ms_per_step": ms, "stack_tokens_per_s": s.T / (ms * 1e-3),
@@ -530,6 +556,92 @@ def bench_stack(args, stream):
     return out
 
 
+def cpu_baseline(args, layers):
+    """The oracle (single-threaded C, fp64) on one pinned host core, on a bounded sample of each
+    workload: the decode layers of the headline (full layers), token samples of the prefill chunk
+    and of the skewed 3-bit layer (tokens are independent in the layer, so a sample's rate is the
+    layer's), and two layers of the 48-layer stack (RMSNorm + layer + residual per sampled token,
+    extrapolated to 48 layers).  Each entry states its sample."""
+    import moe_inputs as mi
+    import oracle
+
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    affinity = os.sched_getaffinity(0)
+    core = min(affinity)
+    where = f"{model}; pinned to core {core} of {len(affinity)} available"
+    budget = args.cpu_seconds
+    out = {}
+
+    def timed(fn):
+        os.sched_setaffinity(0, {core})  # the single-threaded oracle on one pinned core
+        try:
+            t1 = time.perf_counter()
+            r = fn()
+            return r, time.perf_counter() - t1
+        finally:
+            os.sched_setaffinity(0, affinity)  # (inputs are generated on every core)
+
+    try:
+        # headline workload: whole decode layers (T = 4), as many as fit in a third of the budget
+        s = mi.DECODE
+        n, t_dec = 0, 0.0
+        while n < len(layers) and t_dec < budget / 3:
+            w_np = mi.make_weights(s, args.seed, n)
+            L = layers[n]
+            _, dt = timed(lambda: oracle.layer(w_np, L.x_np, L.l_np, s.k))
+            t_dec += dt
+            n += 1
+        out["decode_t4"] = {"value": n * s.T / t_dec, "unit": "layer-tokens/s",
+                            "sample": f"{n} whole decode layers (T=4 each), {t_dec:.1f}s"}
+        # prefill chunk and skewed layer: token samples of the benchmark's own inputs
+        for name, ntok in (("prefill", 16), ("skewed", 8)):
+            sh = mi.SHAPES[name]
+            w_np = mi.make_weights(sh, args.seed)
+            x = mi.make_x(sh, args.seed)
+            lg = mi.make_logits(sh, args.seed)
+            rows = np.random.default_rng(17).choice(sh.T, size=ntok, replace=False)
+            _, dt = timed(lambda: oracle.layer_rows(w_np, x, lg, sh.k, rows))
+            out[name] = {"value": ntok / dt, "unit": "layer-tokens/s",
+                         "sample": f"{ntok} of the T={sh.T} tokens, {dt:.1f}s"}
+            del w_np, x, lg
+        # 48-layer stack: two layers on a token sample, extrapolated to 48
+        for tag, sh, ntok in (("stack_prefill", mi.STACK_PREFILL, 8), ("stack_decode", mi.STACK_DECODE, 4)):
+            h = mi.make_h0(sh, args.seed)
+            rows = np.arange(ntok) if sh.T == ntok else np.random.default_rng(19).choice(sh.T, size=ntok, replace=False)
+            hs = h[rows].astype(np.float32)
+            t_st = 0.0
+            for l in range(2):
+                w_np = mi.make_weights(sh, args.seed, l)
+                lg = mi.make_logits(sh, args.seed, l)[rows]
+
+                def one():
+                    xr = oracle.rmsnorm(hs, 1e-6)
+                    return oracle.layer(w_np, xr, lg, sh.k)
+
+                y, dt = timed(one)
+                hs = (hs.astype(np.float64) + y).astype(np.float32)
+                t_st += dt
+                del w_np
+            per_step = t_st / 2 * sh.layers
+            out[tag] = {"value": ntok / per_step, "unit": "stack-tokens/s",
+                        "sample": f"{ntok} tokens through 2 of the {sh.layers} layers ({t_st:.1f}s), "
+                                  f"extrapolated x{sh.layers // 2}"}
+    finally:
+        os.sched_setaffinity(0, affinity)
+    head = out["decode_t4"]
+    cpu = {"value": head["value"], "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
+           "cpu": where, "sample": head["sample"], "configs": out}
+    log("cpu oracle: " + ", ".join(f"{k} {v['value']:.3g} {v['unit']}" for k, v in out.items()))
+    return cpu
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -537,7 +649,9 @@ def main():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--decode-layers", type=int, default=16)
-    p.add_argument("--prefill-steps", type=int, default=10)
+    p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--preroll-s", type=float, default=0.3,
+                   help="seconds of untimed back-to-back calls before each leg's warmup")
     p.add_argument("--no-skewed", action="store_true")
     p.add_argument("--no-stack", action="store_true")
     p.add_argument("--stack-layers", type=int, default=48)
@@ -620,39 +734,7 @@ def main():
         torch.cuda.empty_cache()
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb, stream)
-    cpu = None
-    if not args.no_cpu:
-        s = mi.DECODE
-        model = "unknown"
-        try:
-            for line in open("/proc/cpuinfo"):
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-        except OSError:
-            pass
-        affinity = os.sched_getaffinity(0)
-        core = min(affinity)
-        os.sched_setaffinity(0, {core})  # the single-threaded oracle on one pinned core
-        t0 = time.time()
-        n = 0
-        cpu_time = 0.0
-        try:
-            while n < len(layers) and (time.time() - t0) < args.cpu_seconds:
-                w_np = mi.make_weights(s, args.seed, n)
-                L = layers[n]
-                t1 = time.perf_counter()
-                oracle.layer(w_np, L.x_np, L.l_np, s.k)
-                cpu_time += time.perf_counter() - t1
-                n += 1
-        finally:
-            os.sched_setaffinity(0, affinity)
-        cpu = {"value": n * s.T / cpu_time, "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
-               "cpu": f"{model}; pinned to core {core} of {len(affinity)} available",
-               "sample": f"{n} decode layers (T=4 each) of the benchmark's 16, full layer each, "
-                         f"{cpu_time:.1f}s of single-threaded oracle time"}
-        log(f"cpu oracle: {cpu['value']:.3g} layer-tokens/s over {n} layers ({cpu_time:.1f}s)")
-
+    cpu = None if args.no_cpu else cpu_baseline(args, layers)
     s = mi.DECODE
     line = {
         "metric": METRIC,

@@ -117,13 +117,13 @@ STRATA_DEVICE void matrix_range(const uint8_t* codes, const uint16_t* scales, in
   __syncthreads();
 }
 
-// Shift s with dmax * c0max * 2^s in [2^14, 2^15) (0 for an all-zero matrix).
-STRATA_DEVICE int range_shift(double dmax, double c0max) {
+// Shift s with dmax * c0max * 2^s in [2^14, 2^15) (0 for an all-zero matrix), at most smax.
+STRATA_DEVICE int range_shift(double dmax, double c0max, int smax) {
   const double m = dmax * c0max;
   if (!(m > 0.0)) return 0;
   int e;
   (void)frexp(m, &e);  // m in [2^(e-1), 2^e)
-  return 15 - e;
+  return 15 - e < smax ? 15 - e : smax;
 }
 
 template <int CB>
@@ -140,7 +140,10 @@ __global__ __launch_bounds__(256) void weight_stats_kernel(
   matrix_range<CB>(uc + e * gu_blocks * CB, us + e * gu_blocks, I, H, true, red, du, nu);
   matrix_range<CB>(dc + e * d_blocks * CB, ds + e * d_blocks, H, I, false, red, dd, nd);
   if (threadIdx.x == 0) {
-    const int sg = range_shift(dg, c0max), su = range_shift(du, c0max), sd = range_shift(dd, c0max);
+    // 2-bit: the GEMM scales its code-offset constants (exact in fp16 up to 2^15 * 1.5)
+    const int smax = CB == 8 ? 15 : 64;
+    const int sg = range_shift(dg, c0max, smax), su = range_shift(du, c0max, smax),
+              sd = range_shift(dd, c0max, smax);
     // fp16 rounding of the shifted weights grows a norm by at most 2^-11; 2^-9 of margin
     const double n = ldexp(ng, sg) * ldexp(nu, su) * (1.0 + 0x1p-9);
     out[e] = strata_moe_expert_stats{sg, su, sd, (float)n};

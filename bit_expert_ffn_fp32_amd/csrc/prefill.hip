@@ -116,12 +116,17 @@ struct Q2Tab {
   uint32_t lo, hi;  // byte q of lo/hi = low/high byte of fp16(d * (q - 1.5))
 };
 
-// sh: the matrix's range shift (d * 2^sh is exact unless it falls below fp16's normal range).
+// sh: the matrix's range shift (at most 15 for this format): the products are d times the code
+// offsets q - 1.5 scaled by 2^sh, which are exact fp16 constants (exponent field + sh), so each
+// entry is fp16(d 2^sh (q - 1.5)) with one rounding and no extra operation per block.
 STRATA_DEVICE Q2Tab q2_table(uint16_t dbits, int sh) {
-  const _Float16 d = __builtin_ldexpf16(__builtin_bit_cast(_Float16, dbits), sh);
+  const uint32_t e = (uint32_t)sh << 10;
+  const half2_t c01 = __builtin_bit_cast(half2_t, ((0xBE00u + e) & 0xFFFFu) | ((0xB800u + e) << 16));
+  const half2_t c23 = __builtin_bit_cast(half2_t, ((0x3800u + e) & 0xFFFFu) | ((0x3E00u + e) << 16));
+  const _Float16 d = __builtin_bit_cast(_Float16, dbits);
   const half2_t dd = {d, d};
-  const half2_t p01 = dd * half2_t{(_Float16)-1.5f, (_Float16)-0.5f};  // one rounding each
-  const half2_t p23 = dd * half2_t{(_Float16)0.5f, (_Float16)1.5f};
+  const half2_t p01 = dd * c01;  // one rounding each
+  const half2_t p23 = dd * c23;
   const uint32_t u01 = __builtin_bit_cast(uint32_t, p01), u23 = __builtin_bit_cast(uint32_t, p23);
   return Q2Tab{__builtin_amdgcn_perm(u23, u01, 0x06040200u), __builtin_amdgcn_perm(u23, u01, 0x07050301u)};
 }
@@ -548,16 +553,18 @@ STRATA_DEVICE void stage_barrier(int n) {
 // src/ld: the activation rows (rows_lds[r]: row of unit row r); wt: this lane's weight pieces of
 // slice 0, stage 0; wslice / sslice: byte / fp16 distance between slices in the tiled weights;
 // (ti, ri): this lane's B rows in the LDS weight tiles; sh0 / sh1: the range shifts of the two
-// weight streams; out/out_ld/ocols: destination and the columns per slice.  xi: the token range
-// of unit row threadIdx.x (if it has one), st: the expert's range statistics; once every wave
-// has taken its activation offsets from rows_lds, the rows' exponents (row_exponent) replace them
-// there for the epilogues.
+// weight streams; out/out_ld/ocols: destination and the columns per slice.  tok: the token of
+// unit row threadIdx.x (-1 past the unit's rows), whose range (xinfo) is copied into the
+// epilogue staging area (unused until the first slice ends) with the first stage; st: the
+// expert's range statistics.  Once every wave has taken its activation offsets from rows_lds,
+// the rows' exponents (row_exponent) replace them there for the epilogues.
 template <int FMT, int NF, bool UP>
 STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src, int ld, int K,
                             int* rows_lds, const int* dst_lds, const WeightTile& wt,
                             size_t wslice, size_t sslice, int ti0, int ti1, int ri0, int ri1,
-                            int sh0, int sh1, const XInfo& xi, const strata_moe_expert_stats& st,
-                            uint16_t* __restrict__ out, int out_ld, int ocols, uint8_t* lds) {
+                            int sh0, int sh1, const XInfo* __restrict__ xinfo, int tok,
+                            const strata_moe_expert_stats& st, uint16_t* __restrict__ out,
+                            int out_ld, int ocols, uint8_t* lds) {
   constexpr int kEpi = UP ? kUpEpiBytes : kDownEpiBytes;
   using P = Pipe<FMT, NF, kGemmLds - kRowsBytes - kEpi>;
   using EP = Epilogue<NF, UP>;
@@ -573,6 +580,14 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
     xoff[g] = rows_lds[r] * ld + (((lane & 7) ^ ((r >> 1) & 7)) << 3);
   }
   const int NKs = K / kKS, NT = u.nsl * NKs;
+  // the rows' token ranges: words sx at epi + 4 r, n2 at epi + 1024 + 4 r (copies without a
+  // register result, so no wait lands before the first stage barrier)
+  uint8_t* const xr = reinterpret_cast<uint8_t*>(epi);
+  if (tok >= 0) {
+    const int32_t* src_xi = reinterpret_cast<const int32_t*>(xinfo + tok);
+    __builtin_amdgcn_global_load_lds(src_xi, xr + wave * 256, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(src_xi + 1, xr + 1024 + wave * 256, 4, 0, 0);
+  }
   CopyCursor cc{0, 0, NT, NKs, 0, 0, wslice, sslice};
 #pragma unroll
   for (int j = 0; j < P::kPD; ++j)
@@ -583,7 +598,11 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
   stage_barrier<P::kPer * (P::kPD - 1)>(ops_after<P::kPer, P::kPD>(0, -1, NT, NKs, kSt));
   // (every wave has read rows_lds; the stage barriers of the first slice order these writes
   // before the epilogue's reads)
-  if ((int)threadIdx.x < NF * 32) rows_lds[threadIdx.x] = row_exponent<UP>(xi, st);
+  if ((int)threadIdx.x < NF * 32) {
+    const XInfo xi{reinterpret_cast<const int32_t*>(xr)[threadIdx.x],
+                   reinterpret_cast<const float*>(xr + 1024)[threadIdx.x]};
+    rows_lds[threadIdx.x] = row_exponent<UP>(xi, st);
+  }
   const Q2Sel ksel = q2_sel();
   StageState<FMT, NF> ss;
   stage_setup<FMT, NF>(ss, lds, ti0, ti1, ri0, ri1, sh0, sh1, ksel);
@@ -640,13 +659,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
   const WeightTile wt = weight_tile<FMT>(wave < 2 ? gate_codes : up_codes,
                                          wave < 2 ? gate_scales : up_scales, row0, nkt);
   const strata_moe_expert_stats st = stats[u.expert];
-  XInfo xi{0, 0.0f};
+  int tok = -1;
   if ((int)threadIdx.x < u.nfrag * 32) {  // one unit row per thread (at most 224)
     const int r = threadIdx.x, rr = r < u.nrows ? r : 0;
-    const int t = sorted_slot[u.row_start + rr] / k;
-    rows_lds[r] = t;
+    tok = sorted_slot[u.row_start + rr] / k;
+    rows_lds[r] = tok;
     dst_lds[r] = u.row_start + rr;
-    xi = xinfo[t];  // (first used after run_unit's first stage barrier)
   }
   __syncthreads();
   // a slice is 128 gate (and up) rows = 32 groups of 4
@@ -655,7 +673,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
   const int ri = (wave & 1) * 32 + (threadIdx.x & 31);
 #define STRATA_UP_UNIT(NF)                                                                        \
   run_unit<FMT, NF, true>(u, x16, H, H, rows_lds, dst_lds, wt, wsl, ssl, wave >> 1, 2 + (wave >> 1), \
-                          ri, ri, st.shift_gate, st.shift_up, xi, st, a16, I, 128, smem)
+                          ri, ri, st.shift_gate, st.shift_up, xinfo, tok, st, a16, I, 128, smem)
   switch (u.nfrag) {
     case 1: STRATA_UP_UNIT(1); break;
     case 2: STRATA_UP_UNIT(2); break;
@@ -690,13 +708,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
   const size_t row0 = (size_t)u.expert * H + 256 * u.slice0 + 64 * wave;
   const WeightTile wt = weight_tile<FMT>(down_codes, down_scales, row0, nkt);
   const strata_moe_expert_stats st = stats[u.expert];
-  XInfo xi{0, 0.0f};
+  int tok = -1;
   if ((int)threadIdx.x < u.nfrag * 32) {  // one unit row per thread (at most 224)
     const int r = threadIdx.x, rr = r < u.nrows ? r : 0;
     const int slot = sorted_slot[u.row_start + rr];
     rows_lds[r] = u.row_start + rr;
     dst_lds[r] = slot;
-    xi = xinfo[slot / k];  // (first used after run_unit's first stage barrier)
+    tok = slot / k;
   }
   __syncthreads();
   // a slice is 256 rows = 64 groups of 4
@@ -705,7 +723,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
   const int ri = threadIdx.x & 31;
 #define STRATA_DOWN_UNIT(NF)                                                                      \
   run_unit<FMT, NF, false>(u, a16, I, I, rows_lds, dst_lds, wt, wsl, ssl, wave, wave, ri, 32 + ri, \
-                           st.shift_down, st.shift_down, xi, st, expert_out, H, 256, smem)
+                           st.shift_down, st.shift_down, xinfo, tok, st, expert_out, H, 256, smem)
   switch (u.nfrag) {
     case 1: STRATA_DOWN_UNIT(1); break;
     case 2: STRATA_DOWN_UNIT(2); break;

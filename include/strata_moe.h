@@ -89,8 +89,9 @@ typedef enum {
  * numbers let it place every operand inside fp16's range exactly, by powers of two, whatever
  * the block scales and the activations' magnitude:
  *   shift_gate, shift_up, shift_down: the exponent s of each matrix such that its largest
- *     |d| * max|q - c0| times 2^s lies in (2^14, 2^15]; the GEMM uses fp16(d * 2^s * (q - c0))
- *     and takes 2^-s back out of its fp32 sums (0 for an all-zero matrix);
+ *     |d| * max|q - c0| times 2^s lies in [2^14, 2^15), capped at 15 for STRATA_Q2_B32; the GEMM
+ *     uses fp16(d * 2^s * (q - c0)) and takes 2^-s back out of its fp32 sums (0 for an all-zero
+ *     matrix);
  *   norm_gate_up: an upper bound of (max over rows of the 2-norm of the shifted gate rows) times
  *     (the same for the up rows).  With x's own 2-norm it bounds |SiLU(g) * u| by Cauchy-Schwarz,
  *     and so fixes a per-row power of two that keeps the intermediate a below 2^15 in fp16.

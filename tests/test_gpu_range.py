@@ -148,6 +148,8 @@ def stats_reference(w_np: dict):
             d = sc.view(np.float16).astype(np.float64)
             m = np.abs(d).max() * c0
             s = 0 if m == 0 else 15 - int(np.frexp(m)[1])
+            if fmt == 2:
+                s = min(s, 15)  # the 2-bit GEMM scales its code offsets (exact up to 2^15)
             sh.append(s)
             if name != "down":
                 if fmt == 2:
