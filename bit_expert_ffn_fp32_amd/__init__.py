@@ -25,7 +25,8 @@ EXPORTS = ["strata_moe_route", "strata_moe_permute", "strata_moe_expert_ffn", "s
            "strata_moe_decode", "strata_moe_layer", "strata_moe_rmsnorm", "strata_moe_pack_matrix",
            "strata_moe_router_logits", "strata_moe_shared_expert",
            "strata_moe_usage_update", "strata_moe_usage_rank", "strata_moe_layer_residual",
-           "strata_moe_weight_stats",
+           "strata_moe_weight_stats", "strata_moe_decode_static",
+           "strata_moe_decode_static_max_bytes",
            "strata_moe_residual_workspace_bytes", "strata_moe_block", "strata_moe_block_workspace_bytes",
            "strata_moe_permute_workspace_bytes", "strata_moe_workspace_bytes",
            "strata_moe_shared_workspace_bytes", "strata_status_string"]
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "strata_moe_layer_residual": [W, vp, vp, i32, i32, ctypes.c_float, vp, sz, vp],
             "strata_moe_block": [W, vp, i32, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
             "strata_moe_weight_stats": [W, vp, vp],
+            "strata_moe_decode_static": [W, vp, vp, i32, i32, vp, i32, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -96,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.strata_moe_residual_workspace_bytes.restype = sz
         L.strata_moe_shared_workspace_bytes.argtypes = [i32, i32]
         L.strata_moe_shared_workspace_bytes.restype = sz
+        L.strata_moe_decode_static_max_bytes.argtypes = []
+        L.strata_moe_decode_static_max_bytes.restype = sz
         L.strata_status_string.argtypes = [ctypes.c_int]
         L.strata_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -232,6 +236,16 @@ def strata_moe_decode(w: Weights, x, logits, k, y, accumulate=False, topk_ids=No
         ctypes.byref(cw), _p(x), _p(logits), x.shape[0], k, _p(y), int(accumulate), _p(topk_ids),
         _p(topk_w), _p(workspace), workspace.numel() if workspace is not None else 0,
         _stream(stream)))
+
+
+def strata_moe_decode_static(w: Weights, x, logits, k, y, accumulate=False, topk_ids=None,
+                             topk_w=None, stream=None) -> None:
+    """strata_moe_decode with the library's fixed scratch instead of a workspace (no allocation;
+    calls that overlap on one GPU race)."""
+    cw = w.c_struct()
+    _check("strata_moe_decode_static", lib().strata_moe_decode_static(
+        ctypes.byref(cw), _p(x), _p(logits), x.shape[0], k, _p(y), int(accumulate), _p(topk_ids),
+        _p(topk_w), _stream(stream)))
 
 
 def strata_moe_layer(w: Weights, x, logits, k, y, accumulate=False, topk_ids=None, topk_w=None,

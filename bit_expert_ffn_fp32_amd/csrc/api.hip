@@ -316,6 +316,35 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x, 
                                         y, accumulate, opt_topk_ids, opt_topk_w, workspace, stream));
 }
 
+strata_status strata_moe_decode_static(const strata_moe_weights* w, const uint16_t* x,
+                                       const float* logits, int32_t T, int32_t k, float* y,
+                                       int32_t accumulate, int32_t* opt_topk_ids,
+                                       float* opt_topk_w, hipStream_t stream) {
+  strata_status st = check_weights(w);
+  if (st != STRATA_OK) return st;
+  st = check_route_shape(T, w->num_experts, k);
+  if (st != STRATA_OK) return st;
+  if (T > kMaxDecodeT) return STRATA_ERR_UNSUPPORTED;
+  if (T == 0) return STRATA_OK;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (!strata::decode_fits(T, E, k, H, I)) return STRATA_ERR_UNSUPPORTED;
+  const void* ptrs[3] = {x, logits, y};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return STRATA_ERR_INVALID_ARGUMENT;
+  if ((opt_topk_ids && !aligned16(opt_topk_ids)) || (opt_topk_w && !aligned16(opt_topk_w)))
+    return STRATA_ERR_INVALID_ARGUMENT;
+  if (strata::decode_workspace_bytes(T, E, k, H, I) > strata::decode_static_scratch_bytes())
+    return STRATA_ERR_WORKSPACE_TOO_SMALL;
+  void* scratch = nullptr;
+  if (strata::decode_static_scratch(&scratch) != hipSuccess) return STRATA_ERR_HIP;
+  return from_hip(strata::launch_decode(w->fmt, x, nullptr, 0.0f, logits, T, E, k, H, I,
+                                        w->gate_codes, w->up_codes, w->down_codes, w->gate_scales,
+                                        w->up_scales, w->down_scales, y, accumulate, opt_topk_ids,
+                                        opt_topk_w, scratch, stream));
+}
+
+size_t strata_moe_decode_static_max_bytes(void) { return strata::decode_static_scratch_bytes(); }
+
 strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, const float* logits,
                                int32_t T, int32_t k, float* y, int32_t accumulate,
                                int32_t* opt_topk_ids, float* opt_topk_w, int32_t* opt_counts,

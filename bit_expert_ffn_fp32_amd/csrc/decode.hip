@@ -813,4 +813,35 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float e
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Fixed scratch for callers that cannot allocate (strata_moe_decode_static): the decode path's
+// workspace in a device array of this library, one per GPU, reused by every such call on it.
+
+// (every shape within the decode limits fits: the largest workspace they allow is 126,720 bytes)
+constexpr size_t kDecStaticScratch = 128 * 1024;
+static __device__ __align__(256) uint8_t scratch[kDecStaticScratch];
+
+size_t decode_static_scratch_bytes() { return kDecStaticScratch; }
+
+// The current device's address of `scratch`, looked up once per device (hipGetSymbolAddress with
+// that device current) and kept; host code never uses the array's name as an address.
+hipError_t decode_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace strata

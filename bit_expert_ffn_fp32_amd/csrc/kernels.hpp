@@ -108,6 +108,10 @@ hipError_t launch_decode(int fmt, const uint16_t* x, const float* h_res, float e
                          const uint16_t* a_sh = nullptr, const uint16_t* w_sd = nullptr,
                          int Is = 0);
 size_t decode_workspace_bytes(int T, int E, int k, int H, int I);
+// The decode path's fixed scratch (a device array of the library, one per GPU): its size, and
+// the current device's address of it (looked up on first use per device).
+size_t decode_static_scratch_bytes();
+hipError_t decode_static_scratch(void** ptr);
 // Whether the decode kernels take this shape (T <= 8, T*k <= 128, H <= 4096, I <= 4096 and the
 // staged activations fit in LDS).
 bool decode_fits(int T, int E, int k, int H, int I);

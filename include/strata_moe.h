@@ -243,6 +243,24 @@ strata_status strata_moe_decode(const strata_moe_weights* w, const uint16_t* x,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * strata_moe_decode without a workspace argument, for callers that cannot allocate device memory
+ * or pass one: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same computation, kernels and results as strata_moe_decode.  The scratch memory is
+ * a fixed device array inside the library, strata_moe_decode_static_max_bytes() bytes on each GPU
+ * it runs on (held until the process ends); the call allocates and frees nothing.  Every call on
+ * one GPU uses that GPU's array, so calls that overlap on one GPU (different streams, or
+ * different threads without ordering) race and must not be made; nothing in it needs to start
+ * zeroed.  Arguments and limits as strata_moe_decode.  The array holds 128 KiB, enough for every
+ * shape within those limits (the largest needs 126,720 bytes); a shape whose decode workspace did
+ * not fit would return STRATA_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ */
+strata_status strata_moe_decode_static(const strata_moe_weights* w, const uint16_t* x,
+                                       const float* logits, int32_t T, int32_t k, float* y,
+                                       int32_t accumulate, int32_t* opt_topk_ids,
+                                       float* opt_topk_w, hipStream_t stream);
+size_t strata_moe_decode_static_max_bytes(void);
+
+/*
  * One-call layer: y (=, or += with accumulate) MoE(x): route each token to k of the E experts,
  * run the experts it picked, sum their outputs weighted by the router.  The pages' layer routes
  * each token to 10 of 512 experts ("Strata vs Llama.cpp vs vLLM", transcript at 08:23; "Two-Day
