@@ -8,6 +8,9 @@
 * stack:   two layers of h <- h + MoE(RMSNorm(h)) at the prefill shape, each layer checked
            teacher-forced (the oracle gets the GPU's h and x of that layer).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -22,6 +25,42 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 def log(msg):
     print(msg, flush=True)
+
+
+CHUNK_ROWS, FRAG = 224, 32  # rows of one grouped-GEMM work unit, rows of a matrix-core fragment
+
+
+def oracle_rows(w_np, x_np, l_np, k, rows):
+    """oracle.layer_rows over many tokens on the host's cores (the C call releases the GIL; the
+    rows are independent)."""
+    rows = np.asarray(rows)
+    n = max(1, min(16, os.cpu_count() or 1))
+    parts = [p for p in np.array_split(rows, n) if p.size]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        out = list(ex.map(lambda r: oracle.layer_rows(w_np, x_np, l_np, k, r), parts))
+    return np.concatenate(out)
+
+
+def coverage_rows(counts, offsets, sorted_slot, k, rng, n_random):
+    """Tokens whose rows reach every expert's first and last (ragged) fragment and both ends of
+    every GEMM work unit (the chunks of at most 224 rows an expert's segment is cut into, split
+    into balanced 32-row fragments), plus random tokens."""
+    pos = []
+    for e in np.nonzero(counts)[0]:
+        cnt, row = int(counts[e]), int(offsets[e])
+        nfrag = -(-cnt // FRAG)
+        nch = -(-nfrag // (CHUNK_ROWS // FRAG))
+        fb, extra = divmod(nfrag, nch)
+        used = 0
+        for c in range(nch):
+            nf = fb + (1 if c < extra else 0)
+            rows = min(nf * FRAG, cnt - used * FRAG)
+            pos += [row, row + rows - 1, row + rows - 1 - (rows - 1) % FRAG]  # ends, last fragment
+            row += rows
+            used += nf
+    tokens = set(int(sorted_slot[p]) // k for p in pos)
+    tokens |= set(int(t) for t in rng.choice(len(sorted_slot) // k, size=n_random, replace=False))
+    return np.array(sorted(tokens))
 
 
 def run_layer(L: Layer, x=None, logits=None, y=None, accumulate=False, perm=None):
@@ -57,7 +96,7 @@ def test_decode_full_size(T):
     assert err.max() <= TOL_REL_L2
 
 
-@pytest.mark.parametrize("name,n_rows", [("prefill", 12), ("skewed", 12)])
+@pytest.mark.parametrize("name,n_rows", [("prefill", 256), ("skewed", 128)])
 def test_prefill_full_size(name, n_rows):
     s = mi.SHAPES[name]
     log(f"{name} full size: generating")
@@ -70,13 +109,8 @@ def test_prefill_full_size(name, n_rows):
     assert np.array_equal(extra["counts"].cpu().numpy(), counts)
     assert np.array_equal(extra["offsets"].cpu().numpy(), offsets)
     assert np.array_equal(extra["sorted_slot"].cpu().numpy(), ss)
-    rows = np.random.default_rng(2024).choice(s.T, size=n_rows, replace=False)
-    if name == "skewed":  # include tokens of the hottest experts and of the coldest touched one
-        hot = int(np.argmax(counts))
-        cold = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-        rows = np.concatenate([rows, np.nonzero((ids_ref == hot).any(axis=1))[0][:2],
-                               np.nonzero((ids_ref == cold).any(axis=1))[0][:2]])
-    y_ref = oracle.layer_rows(L.w_np, L.x_np, L.l_np, s.k, rows)
+    rows = coverage_rows(counts, offsets, ss, s.k, np.random.default_rng(2024), n_rows)
+    y_ref = oracle_rows(L.w_np, L.x_np, L.l_np, s.k, rows)
     err = rel_l2_rows(y.cpu().numpy()[rows], y_ref)
     log(f"{name} full size: sampled rows {len(rows)}, max rel-L2 {err.max():.3e}")
     assert err.max() <= TOL_REL_L2
@@ -88,7 +122,7 @@ def test_stack_two_layers_teacher_forced():
     s = mi.PREFILL
     h = to_dev(mi.make_h0(s))
     x = torch.empty((s.T, s.H), dtype=torch.int16, device=dev())
-    rows = np.random.default_rng(7).choice(s.T, size=6, replace=False)
+    rows = np.random.default_rng(7).choice(s.T, size=64, replace=False)
     for layer in range(2):
         log(f"stack layer {layer}: generating")
         L = Layer(s, layer=layer)
@@ -101,7 +135,7 @@ def test_stack_two_layers_teacher_forced():
         assert d.max() <= 1 and np.mean(d == 0) > 0.999
         run_layer(L, x=x, y=h, accumulate=True)
         y_rows = h.cpu().numpy()[rows] - h_in[rows]
-        y_ref = oracle.layer_rows(L.w_np, x_np, L.l_np, s.k, rows)  # teacher-forced on the GPU's x
+        y_ref = oracle_rows(L.w_np, x_np, L.l_np, s.k, rows)  # teacher-forced on the GPU's x
         err = rel_l2_rows(y_rows, y_ref)
         log(f"stack layer {layer}: max rel-L2 {err.max():.3e}")
         assert err.max() <= TOL_REL_L2
