@@ -317,12 +317,37 @@ STRATA_DEVICE void row_dots(RowChunks<FMT, MC> (&rc)[NR], int nchunk, int c0, in
   }
 }
 
-// Contiguous range of work items of this workgroup.
-STRATA_DEVICE void item_range(int n_items, int& begin, int& end) {
+// Contiguous range of K1's items (distinct expert d, block of rows) of this workgroup, balanced by
+// work: an item's dot products are done once per token of its expert, so item (d, q) weighs
+// dtp[d], and workgroup b takes the items whose weight prefix falls in [b W / G, (b + 1) W / G),
+// W = blocks * S.  (With equal item counts, the workgroups holding an expert that two tokens
+// picked took twice as long, and the slowest workgroup sets the kernel's end.)  Every wave finds
+// its range with a scan across its lanes (two distinct experts a lane: nd <= 128), not a walk
+// through the table.
+STRATA_DEVICE void item_range(const RouteTable& rt, int blocks, int S, int& begin, int& end) {
   const int G = kGrid, b = blockIdx.x;  // the launch grid (a constant: no dispatch-packet read)
-  const int per = n_items / G, extra = n_items % G;
-  begin = b * per + (b < extra ? b : extra);
-  end = begin + per + (b < extra ? 1 : 0);
+  const int lane = threadIdx.x & 63, nd = rt.nd;
+  const int t0 = 2 * lane < nd ? rt.dtp[2 * lane] : 0;
+  const int t1 = 2 * lane + 1 < nd ? rt.dtp[2 * lane + 1] : 0;
+  int inc = t0 + t1;  // tokens of the distinct experts 0 .. 2 lane + 1
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
+  // the first item whose weight prefix is >= target
+  auto item_at = [&](int target) {
+    const uint64_t hit = __ballot(2 * lane < nd && inc * blocks >= target);
+    if (hit == 0) return nd * blocks;
+    const int l = __ffsll((unsigned long long)hit) - 1;
+    const int ta = __shfl(t0, l), tb = __shfl(t1, l), ex = __shfl(inc, l) - ta - tb;
+    const bool first = (ex + ta) * blocks >= target;
+    const int d = first ? 2 * l : 2 * l + 1, cum = first ? ex : ex + ta, tp = first ? ta : tb;
+    return d * blocks + (target - cum * blocks + tp - 1) / tp;
+  };
+  const int W = blocks * S;
+  begin = item_at((b * W + G - 1) / G);
+  end = item_at(((b + 1) * W + G - 1) / G);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   }
   const int blocks = I / kUpRows;
   int it, end;
-  item_range(rt.nd * blocks, it, end);
+  item_range(rt, blocks, S, it, end);
   if (it >= end) return;
   constexpr int CB = FMT == 2 ? 8 : 12;
   constexpr int kGroups = kUpThreads / 256;  // four waves (16 rows) per item
