@@ -403,7 +403,7 @@ def bench_sweep(args, stream, layers):
         return tot / n * s.expert_bytes
 
     dec, pre, lay = [], [], []
-    for T in (9, 12, 16, 24, 32, 48, 64):  # the layer call's own choice
+    for T in (9, 12, 16, 24, 32, 48, 64, 65, 80):  # the layer call's own choice
         us = graph_us(decode_path(T))
         lay.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6)})
     for T in t_dec:

@@ -28,7 +28,7 @@ constexpr int kMaxDecodeT = 8;
 // Up to this many tokens the one-call layer runs the decode path on slices of at most
 // kMaxDecodeT tokens: the tokens of a layer are independent, and streaming each touched expert
 // once per slice still beats the grouped GEMMs while experts see only a few rows each.
-constexpr int kSplitDecodeMaxT = 48;
+constexpr int kSplitDecodeMaxT = 64;
 
 size_t round_up(size_t b) { return (b + 255) & ~(size_t)255; }
 
