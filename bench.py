@@ -13,7 +13,8 @@ dimensions; a step is one whole-layer call.  Keys "block_decode" and "prefill.bl
 layers on either side of the routed experts (router projection x W_r^T, shared SwiGLU expert),
 alone and as the whole block router -> routed layer -> + shared expert.  Key "pruned": the same
 decode and prefill legs with 256 experts per layer (the pages' pruned coder variant).  Key
-"sweep": the decode path at T = 1 .. 8 and the prefill path at T = 1 .. 256 (crossover).
+"sweep": the decode path at T = 1 .. 8, the prefill path at T = 1 .. 1024 (crossover) and the
+one-call layer's own choice at T = 9 .. 80.
 
 value = whole-job layer-tokens/s = T * steps / timed seconds, inputs resident in HBM.
 roofline: HBM-bound decode (touched experts' packed bytes per layer call / call duration, peak
@@ -345,7 +346,7 @@ def bench_sweep(args, stream, layers):
     s = mi.DECODE
     n = len(layers)
     t_dec = list(range(1, 9))
-    t_pre = t_dec + [16, 32, 64, 128, 256, 512, 1024]
+    t_pre = t_dec + [16, 32, 40, 48, 64, 128, 256, 512, 1024]
     tmax = max(t_pre)
     xs = [to_dev_bf16(mi.make_x(s, args.seed, l, tmax)) for l in range(n)]
     lg_np = [mi.make_logits(s, args.seed, l, tmax) for l in range(n)]
@@ -403,7 +404,7 @@ def bench_sweep(args, stream, layers):
         return tot / n * s.expert_bytes
 
     dec, pre, lay = [], [], []
-    for T in (9, 12, 16, 24, 32, 48, 64, 65, 80):  # the layer call's own choice
+    for T in (9, 12, 16, 24, 32, 40, 41, 48, 64, 80):  # the layer call's own choice
         us = graph_us(decode_path(T))
         lay.append({"T": T, "us": us, "tokens_per_s": T / (us * 1e-6)})
     for T in t_dec:
@@ -417,7 +418,7 @@ def bench_sweep(args, stream, layers):
     out_d = {"decode_path": dec, "prefill_path": pre, "layer_call": lay,
              "crossover_T": min(faster) if faster else None,
              "note": "strata_moe_layer runs the decode path for T <= 8, and on slices of at most "
-                     "8 tokens for T <= 64; layer_call times that choice"}
+                     "8 tokens for T <= 40; layer_call times that choice"}
     log("sweep: decode path " + ", ".join(f"T={d['T']} {d['us']:.1f}us" for d in dec))
     log("sweep: prefill path " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in pre))
     log("sweep: layer call " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in lay))

@@ -28,7 +28,7 @@ constexpr int kMaxDecodeT = 8;
 // Up to this many tokens the one-call layer runs the decode path on slices of at most
 // kMaxDecodeT tokens: the tokens of a layer are independent, and streaming each touched expert
 // once per slice still beats the grouped GEMMs while experts see only a few rows each.
-constexpr int kSplitDecodeMaxT = 64;
+constexpr int kSplitDecodeMaxT = 40;
 
 size_t round_up(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -84,14 +84,18 @@ struct PrefillWs {
   uint16_t* a16;
   uint16_t* expert_out;
   size_t bytes;
-  int max_chunks;
+  strata::ChunkList cl;  // the chunk list's parts: chunks, n_chunks, small_rows, min_small, max_small
+  int max_large;
 };
 
 PrefillWs carve_prefill(void* base, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
   PrefillWs p{};
   const size_t S = (size_t)T * k;
   const size_t ntiles = (S + strata::kPermTile - 1) / strata::kPermTile;
-  p.max_chunks = (int)strata::max_chunks((int64_t)S, E);
+  p.cl.small_rows = strata::small_chunk_rows((int64_t)S, E);
+  p.cl.min_small = strata::min_small_experts(I);
+  p.cl.max_small = (int)strata::max_small_chunks((int64_t)S, E, p.cl.small_rows);
+  p.max_large = (int)strata::max_large_chunks((int64_t)S, E, p.cl.small_rows, p.cl.min_small);
   uint8_t* c = static_cast<uint8_t*>(base);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -107,8 +111,10 @@ PrefillWs carve_prefill(void* base, int32_t T, int32_t E, int32_t k, int32_t H, 
   p.slot_pos = static_cast<int*>(take(S * 4));
   p.tile_hist = static_cast<int*>(take(ntiles * E * 4));
   p.tile_base = static_cast<int*>(take(ntiles * E * 4));
-  p.chunks = static_cast<Chunk*>(take((size_t)p.max_chunks * sizeof(Chunk)));
+  p.chunks = static_cast<Chunk*>(take((size_t)(p.cl.max_small + p.max_large) * sizeof(Chunk)));
   p.n_chunks = static_cast<int*>(take(16));
+  p.cl.chunks = p.chunks;
+  p.cl.n_chunks = p.n_chunks;
   p.xinfo = static_cast<strata::XInfo*>(take((size_t)T * sizeof(strata::XInfo)));
   p.x16 = static_cast<uint16_t*>(take((size_t)T * H * 2));
   p.a16 = static_cast<uint16_t*>(take(S * I * 2));
@@ -117,41 +123,6 @@ PrefillWs carve_prefill(void* base, int32_t T, int32_t E, int32_t k, int32_t H, 
   return p;
 }
 
-__global__ void chunks_from_offsets_kernel(const int* offsets, int E, Chunk* chunks, int* n_chunks) {
-  // one workgroup of 1024 threads, thread e = expert (E <= 1024)
-  __shared__ int wsum[16];
-  const int e = threadIdx.x;
-  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-  const int nfrag = (cnt + 31) / 32;
-  const int per = strata::kChunkRows / 32;
-  const int nch = (nfrag + per - 1) / per;
-  const int lane = e & 63, wv = e >> 6;
-  int inc = nch;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  if (lane == 63) wsum[wv] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < 16; ++i) {
-    if (i < wv) base += wsum[i];
-    tot += wsum[i];
-  }
-  base += inc - nch;
-  if (e < E && nch > 0) {
-    const int fb = nfrag / nch, extra = nfrag % nch;
-    int row = offsets[e], used = 0;
-    for (int c = 0; c < nch; ++c) {
-      const int nf = fb + (c < extra ? 1 : 0);
-      const int rows = min(nf * 32, cnt - used * 32);
-      chunks[base + c] = Chunk{e, row, rows, 0};
-      row += rows;
-      used += nf;
-    }
-  }
-  if (e == 0) *n_chunks = tot;
-}
 
 // Decode paths (T <= kSplitDecodeMaxT): the decode kernels' workspace for slices of at most
 // kMaxDecodeT tokens, then, for a caller that asks strata_moe_layer for the permutation, the
@@ -246,7 +217,7 @@ strata_status strata_moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, 
   int* hist = static_cast<int*>(workspace);
   int* base = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + round_up(ntiles * E * 4));
   return from_hip(strata::launch_permute(topk_ids, T, E, k, counts, offsets, sorted_slot, slot_pos,
-                                         hist, base, nullptr, nullptr, stream));
+                                         hist, base, strata::ChunkList{}, stream));
 }
 
 strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t* x, int32_t T,
@@ -266,16 +237,15 @@ strata_status strata_moe_expert_ffn(const strata_moe_weights* w, const uint16_t*
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
   if (workspace_bytes < strata_moe_workspace_bytes(T, E, k, H, I)) return STRATA_ERR_WORKSPACE_TOO_SMALL;
   PrefillWs p = carve_prefill(workspace, T, E, k, H, I);
-  chunks_from_offsets_kernel<<<1, 1024, 0, stream>>>(offsets, E, p.chunks, p.n_chunks);
-  hipError_t e = hipGetLastError();
+  hipError_t e = strata::launch_chunks_from_offsets(offsets, E, p.cl, stream);
   if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, p.xinfo, stream);
   if (e == hipSuccess)
     e = strata::launch_ffn_up(w->fmt, p.x16, p.xinfo, sorted_slot, k, (int64_t)T * k, p.chunks,
-                              p.n_chunks, p.max_chunks, w->gate_codes, w->up_codes,
+                              p.n_chunks, p.cl.max_small, p.max_large, w->gate_codes, w->up_codes,
                               w->gate_scales, w->up_scales, w->stats, E, H, I, p.a16, stream);
   if (e == hipSuccess)
     e = strata::launch_ffn_down(w->fmt, p.a16, p.xinfo, sorted_slot, k, (int64_t)T * k, p.chunks,
-                                p.n_chunks, p.max_chunks, w->down_codes, w->down_scales, w->stats,
+                                p.n_chunks, p.cl.max_small, p.max_large, w->down_codes, w->down_scales, w->stats,
                                 E, H, I, expert_out, stream);
   return from_hip(e);
 }
@@ -391,7 +361,7 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
       e = strata::launch_permute(ids, T, E, k, opt_counts ? opt_counts : q.counts,
                                  opt_offsets ? opt_offsets : q.offsets,
                                  opt_sorted_slot ? opt_sorted_slot : q.sorted_slot, q.slot_pos,
-                                 q.tile_hist, q.tile_base, nullptr, nullptr, stream);
+                                 q.tile_hist, q.tile_base, strata::ChunkList{}, stream);
     return from_hip(e);
   }
   st = check_stats(w);
@@ -405,15 +375,15 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   hipError_t e = strata::launch_route(logits, T, E, k, ids, rw, stream);
   if (e == hipSuccess)
     e = strata::launch_permute(ids, T, E, k, counts, offsets, sorted, p.slot_pos, p.tile_hist,
-                               p.tile_base, p.chunks, p.n_chunks, stream);
+                               p.tile_base, p.cl, stream);
   if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, p.xinfo, stream);
   if (e == hipSuccess)
     e = strata::launch_ffn_up(w->fmt, p.x16, p.xinfo, sorted, k, (int64_t)T * k, p.chunks,
-                              p.n_chunks, p.max_chunks, w->gate_codes, w->up_codes,
+                              p.n_chunks, p.cl.max_small, p.max_large, w->gate_codes, w->up_codes,
                               w->gate_scales, w->up_scales, w->stats, E, H, I, p.a16, stream);
   if (e == hipSuccess)
     e = strata::launch_ffn_down(w->fmt, p.a16, p.xinfo, sorted, k, (int64_t)T * k, p.chunks,
-                                p.n_chunks, p.max_chunks, w->down_codes, w->down_scales, w->stats,
+                                p.n_chunks, p.cl.max_small, p.max_large, w->down_codes, w->down_scales, w->stats,
                                 E, H, I, p.expert_out, stream);
   if (e == hipSuccess) e = strata::launch_combine(p.expert_out, rw, T, k, H, y, accumulate, stream);
   return from_hip(e);

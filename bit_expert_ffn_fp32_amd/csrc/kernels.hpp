@@ -18,12 +18,61 @@ struct Chunk {
   int32_t pad;
 };
 
-constexpr int kChunkRows = 224;  // rows of one GEMM work unit (at most 7 fragments of 32)
-constexpr int kPermTile = 1024;  // slots per permute tile
+constexpr int kChunkRows = 224;      // rows of one GEMM work unit (at most 7 fragments of 32)
+constexpr int kChunkRowsSmall = 64;  // the same for the small-fragment GEMMs (at most 2)
+constexpr int kPermTile = 1024;      // slots per permute tile
 
-// Upper bound of the number of chunks for S slots over E experts.
-inline int64_t max_chunks(int64_t S, int64_t E) {
-  return S / kChunkRows + (E < S ? E : S) + 1;
+// The grouped GEMMs' chunk list has two parts.  An expert with at most small_rows rows gets one
+// chunk in the small part, run by the small-fragment GEMMs (two workgroups per CU, so that one's
+// stage barriers and copy waits overlap the other's matrix work); an expert with more rows gets
+// chunks of up to kChunkRows rows (32-row fragments spread evenly) in the large part, whose units
+// read the expert's weights once for up to 224 rows.  The two parts run as two launches, so a
+// small part of few units would run alone at low occupancy: the list builder uses it only when
+// at least min_small experts qualify (enough units to fill the CUs once), else every expert goes
+// to the large part.  small_rows is kChunkRowsSmall while the slots average at most 128 rows per
+// expert, else 0 (no small part).  Measured at H = 3072, E = 512, k = 10: small chunks for every
+// expert beat the large ones up to T = 3072 (60 rows per expert) and lose at T = 4096 (80); with
+// skewed routing the large part keeps the hot experts' weights from being re-read per 64 rows.
+inline int small_chunk_rows(int64_t S, int64_t E) { return S <= 128 * E ? kChunkRowsSmall : 0; }
+// Experts the small part needs: units (one per 128 gate/up outputs) for two workgroups per CU.
+inline int min_small_experts(int I) { return (2 * 256 + I / 128 - 1) / (I / 128); }
+inline int64_t max_small_chunks(int64_t S, int64_t E, int small_rows) {
+  return small_rows ? (E < S ? E : S) : 0;
+}
+inline int64_t max_large_chunks(int64_t S, int64_t E, int small_rows, int min_small) {
+  // experts in the large part: those with more than small_rows rows, plus (when the small part
+  // is not used) fewer than min_small others
+  int64_t n = S / (small_rows + 1) + (small_rows ? min_small : 0);
+  n = n < E ? n : E;
+  return S / kChunkRows + (n < S ? n : S) + 1;
+}
+
+// Number of chunks of an expert with cnt rows in the small and in the large part.
+__device__ __forceinline__ int small_chunks_of(int cnt, int small_rows) { return cnt > 0 && cnt <= small_rows ? 1 : 0; }
+__device__ __forceinline__ int large_chunks_of(int cnt, int small_rows) {
+  if (cnt <= small_rows) return 0;
+  const int nfrag = (cnt + 31) / 32;
+  return (nfrag + kChunkRows / 32 - 1) / (kChunkRows / 32);
+}
+// Writes the chunks of expert e, whose rows are sorted positions [off, off + cnt): at small[sb]
+// or at large[lb ..].
+__device__ __forceinline__ void write_expert_chunks(int e, int off, int cnt, int small_rows,
+                                                   Chunk* small, int sb, Chunk* large, int lb) {
+  if (cnt <= 0) return;
+  if (cnt <= small_rows) {
+    small[sb] = Chunk{e, off, cnt, 0};
+    return;
+  }
+  const int nfrag = (cnt + 31) / 32, nch = large_chunks_of(cnt, small_rows);
+  const int fb = nfrag / nch, extra = nfrag % nch;
+  int row = off, used = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int nf = fb + (c < extra ? 1 : 0);
+    const int rows = min(nf * 32, cnt - used * 32);
+    large[lb + c] = Chunk{e, row, rows, 0};
+    row += rows;
+    used += nf;
+  }
 }
 
 // Row-major -> tiled weight layout for n_mat matrices of R x K (R a multiple of 4, K of 64).
@@ -33,10 +82,24 @@ hipError_t launch_pack(int fmt, int n_mat, int R, int K, const void* codes, cons
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
                         hipStream_t s);
 
-// Stable counting sort; also writes the GEMM chunk list (chunks, *n_chunks) when chunks != NULL.
+// Where the chunk list goes and how it is split (small_chunk_rows, min_small_experts,
+// max_small_chunks): the small part at chunks[0 ..) with its count in n_chunks[0], the large part
+// at chunks[max_small ..) with its count in n_chunks[1].
+struct ChunkList {
+  Chunk* chunks;
+  int* n_chunks;
+  int small_rows;
+  int min_small;
+  int max_small;
+};
+
+// Stable counting sort; also writes the GEMM chunk list when cl.chunks != NULL.
 hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int* offsets,
                           int* sorted_slot, int* slot_pos, int* tile_hist, int* tile_base,
-                          Chunk* chunks, int* n_chunks, hipStream_t s);
+                          const ChunkList& cl, hipStream_t s);
+
+// The GEMM chunk list from the offsets [E + 1] of a counting sort (E <= 1024).
+hipError_t launch_chunks_from_offsets(const int* offsets, int E, const ChunkList& cl, hipStream_t s);
 
 // Per-token range of the fp16 activations of the grouped GEMM: x16 = x * 2^sx with the row's
 // largest |x| in [2^14, 2^15) (sx = 0 for an all-zero row), n2 = sum of x16^2 in fp32.
@@ -51,17 +114,21 @@ hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo
                            hipStream_t s);
 
 // S: the number of slots (sizes the work units; the chunk list itself is read on the device).
+// chunks / n_chunks: the two-part list of launch_permute, with max_small and max_large its parts'
+// capacities; the small part runs on the small-fragment GEMMs (if max_small > 0), then the large.
 hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const int* sorted_slot,
-                         int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_chunks,
+                         int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_small,
+                         int max_large,
                          const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
                          const uint16_t* up_scales, const strata_moe_expert_stats* stats, int E,
                          int H, int I, uint16_t* a16, hipStream_t s);
 
 hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
                            const int* sorted_slot, int k, int64_t S, const Chunk* chunks,
-                           const int* n_chunks, int max_chunks, const void* down_codes,
-                           const uint16_t* down_scales, const strata_moe_expert_stats* stats,
-                           int E, int H, int I, uint16_t* expert_out, hipStream_t s);
+                           const int* n_chunks, int max_small, int max_large,
+                           const void* down_codes, const uint16_t* down_scales,
+                           const strata_moe_expert_stats* stats, int E, int H, int I,
+                           uint16_t* expert_out, hipStream_t s);
 
 // Range statistics of a layer's tiled weights, one strata_moe_expert_stats per expert.
 hipError_t launch_weight_stats(int fmt, int E, int H, int I, const void* gate_codes,

@@ -10,7 +10,8 @@
 //              (LDS integer atomics: the result is order independent).
 //  2. scan:    one workgroup turns the histograms into counts, offsets (exclusive prefix sum)
 //              and each tile's starting position per expert; it also cuts every expert's segment
-//              into GEMM chunks of at most kChunkRows rows, balanced in 32-row fragments.
+//              into the GEMM chunk list (one chunk per expert of at most kChunkRowsSmall rows, chunks
+//              of up to kChunkRows rows for the others, balanced in 32-row fragments).
 //  3. scatter: each tile ranks its slots stably in one round of 1024 threads: a slot's rank is the
 //              number of equal ids in earlier lanes of its wave (an LDS broadcast loop), plus the
 //              counts of the earlier waves, plus the tile's starting position for its expert.
@@ -62,6 +63,23 @@ __device__ int block_exclusive_scan(int v, int* lds16, int& total) {
   return wbase + inc - v;
 }
 
+// The two-part GEMM chunk list (see ChunkList), built by a whole 1024-thread workgroup; a thread
+// with mine holds expert e, its rows at sorted positions [off, off + cnt).  The small part is used
+// only when at least cl.min_small experts qualify for it.
+__device__ void build_chunk_list(bool mine, int e, int off, int cnt, const ChunkList& cl, int* lds16) {
+  int nsmall;
+  (void)block_exclusive_scan(mine ? small_chunks_of(cnt, cl.small_rows) : 0, lds16, nsmall);
+  const int sr = nsmall >= cl.min_small ? cl.small_rows : 0;
+  int stotal, ltotal;
+  const int sb = block_exclusive_scan(mine ? small_chunks_of(cnt, sr) : 0, lds16, stotal);
+  const int lb = block_exclusive_scan(mine ? large_chunks_of(cnt, sr) : 0, lds16, ltotal);
+  if (mine) write_expert_chunks(e, off, cnt, sr, cl.chunks, sb, cl.chunks + cl.max_small, lb);
+  if (threadIdx.x == 0) {
+    cl.n_chunks[0] = stotal;
+    cl.n_chunks[1] = ltotal;
+  }
+}
+
 // hist[t][e] summed over the tiles [t0, t1) of one expert, 16 loads in flight at a time.
 __device__ int tile_sum(const int* __restrict__ hist, int E, int e, int t0, int t1) {
   int acc = 0;
@@ -80,8 +98,7 @@ __device__ int tile_sum(const int* __restrict__ hist, int E, int e, int t0, int 
 // threads.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     const int* __restrict__ hist, int ntiles, int E, int P, int* __restrict__ tile_base,
-    int* __restrict__ counts, int* __restrict__ offsets, Chunk* __restrict__ chunks,
-    int* __restrict__ n_chunks) {
+    int* __restrict__ counts, int* __restrict__ offsets, ChunkList cl) {
   __shared__ int lds16[16];
   __shared__ int psum[1024];  // [part][e]
   const int Ep = 1024 / P;    // threads of one part (>= E)
@@ -123,24 +140,8 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
       }
     }
   }
-  if (chunks == nullptr) return;
-  // GEMM chunks: ceil(cnt / kChunkRows) per expert, fragments of 32 rows spread evenly.
-  const int nfrag = (cnt + 31) / 32;
-  const int nch = (nfrag + (kChunkRows / 32) - 1) / (kChunkRows / 32);
-  int ctotal;
-  const int cbase = block_exclusive_scan(q == 0 && mine ? nch : 0, lds16, ctotal);
-  if (q == 0 && mine && nch > 0) {
-    const int fb = nfrag / nch, extra = nfrag % nch;
-    int row = off, frag_used = 0;
-    for (int c = 0; c < nch; ++c) {
-      const int nf = fb + (c < extra ? 1 : 0);
-      const int rows = min(nf * 32, cnt - frag_used * 32);
-      chunks[cbase + c] = Chunk{e, row, rows, 0};
-      row += rows;
-      frag_used += nf;
-    }
-  }
-  if (threadIdx.x == 0) *n_chunks = ctotal;
+  if (cl.chunks == nullptr) return;
+  build_chunk_list(q == 0 && mine, e, off, cnt, cl, lds16);
 }
 
 // One workgroup of 1024 threads (16 waves) per tile of kPermTile = 1024 slots, in one round: a
@@ -186,17 +187,32 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
 
 hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int* offsets,
                           int* sorted_slot, int* slot_pos, int* tile_hist, int* tile_base,
-                          Chunk* chunks, int* n_chunks, hipStream_t s) {
+                          const ChunkList& cl, hipStream_t s) {
   const int S = T * k;
   const int ntiles = (S + kPermTile - 1) / kPermTile;
   permute_count_kernel<<<ntiles, kPermThreads, E * sizeof(int), s>>>(ids, S, E, tile_hist);
   int Ep = 1;
   while (Ep < E) Ep <<= 1;  // E <= 1024
   permute_scan_kernel<<<1, 1024, 0, s>>>(tile_hist, ntiles, E, 1024 / Ep, tile_base, counts,
-                                         offsets, chunks, n_chunks);
+                                         offsets, cl);
   const size_t scatter_lds = kScatterThreads * sizeof(int) + ((size_t)kScatterWaves * E + 3) / 4 * 4;
   permute_scatter_kernel<<<ntiles, kScatterThreads, scatter_lds, s>>>(ids, S, E, tile_base,
                                                                       sorted_slot, slot_pos);
+  return hipGetLastError();
+}
+
+// One workgroup of 1024 threads, thread e = expert.
+__global__ __launch_bounds__(1024) void chunks_from_offsets_kernel(const int* __restrict__ offsets,
+                                                                  int E, ChunkList cl) {
+  __shared__ int lds16[16];
+  const int e = threadIdx.x;
+  const bool mine = e < E;
+  const int off = mine ? offsets[e] : 0, cnt = mine ? offsets[e + 1] - off : 0;
+  build_chunk_list(mine, e, off, cnt, cl, lds16);
+}
+
+hipError_t launch_chunks_from_offsets(const int* offsets, int E, const ChunkList& cl, hipStream_t s) {
+  chunks_from_offsets_kernel<<<1, 1024, 0, s>>>(offsets, E, cl);
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ constexpr int kKS = 64;                           // reduction indices per pipel
 constexpr int kFrags = kChunkRows / 32;           // 32-row fragments per chunk
 constexpr int kWScaleBytes = 256 * 2 * 2;         // 256 weight rows x 2 fp16 scales per stage
 constexpr int kGemmLds = 160 * 1024;              // the whole LDS of a CU
+constexpr int kGemmLdsSmall = 80 * 1024;          // half of it: two small-fragment workgroups per CU
 constexpr int kRowsBytes = 2 * kChunkRows * 4;    // a unit's source and destination rows
 // Output staging: two 32-row buffers (one fragment each) with padded rows.
 constexpr int kUpOutRow = 128 + 8;                // halfs per row: 128 outputs
@@ -558,7 +559,7 @@ STRATA_DEVICE void stage_barrier(int n) {
 // epilogue staging area (unused until the first slice ends) with the first stage; st: the
 // expert's range statistics.  Once every wave has taken its activation offsets from rows_lds,
 // the rows' exponents (row_exponent) replace them there for the epilogues.
-template <int FMT, int NF, bool UP>
+template <int FMT, int NF, bool UP, int LDSB>
 STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src, int ld, int K,
                             int* rows_lds, const int* dst_lds, const WeightTile& wt,
                             size_t wslice, size_t sslice, int ti0, int ti1, int ri0, int ri1,
@@ -566,7 +567,7 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
                             const strata_moe_expert_stats& st, uint16_t* __restrict__ out,
                             int out_ld, int ocols, uint8_t* lds) {
   constexpr int kEpi = UP ? kUpEpiBytes : kDownEpiBytes;
-  using P = Pipe<FMT, NF, kGemmLds - kRowsBytes - kEpi>;
+  using P = Pipe<FMT, NF, LDSB - kRowsBytes - kEpi>;
   using EP = Epilogue<NF, UP>;
   constexpr int kSt = EP::kStores * NF;  // stores per wave per slice
   constexpr int kPre = (NF + 1) / 2;     // step-3 fragments issued before the stage barrier
@@ -638,17 +639,22 @@ STRATA_DEVICE void run_unit(const UnitInfo& u, const uint16_t* __restrict__ src,
 // ---------------------------------------------------------------------------------------------
 // Up projection: A[p][n] = SiLU(x_t . W_g[n]) * (x_t . W_u[n]) for the chunk's rows p.
 // Slice = 128 outputs; wave w owns outputs slice*128 + w*32 + (lane % 32), gate and up.
+//
+// NFMAX: the most fragments a unit holds, 7 (chunks of up to 224 rows; one workgroup per CU with
+// the whole LDS) or 2 (chunks of up to 64 rows; half the LDS and at most 256 registers a wave, so
+// that two workgroups share a CU).
 
-template <int FMT>
-__global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
+template <int FMT, int NFMAX>
+__global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_up_kernel(
     const uint16_t* __restrict__ x16, const XInfo* __restrict__ xinfo,
     const int* __restrict__ sorted_slot, int k, const Chunk* __restrict__ chunks,
     const int* __restrict__ n_chunks, const uint8_t* __restrict__ gate_codes,
     const uint8_t* __restrict__ up_codes, const uint16_t* __restrict__ gate_scales,
     const uint16_t* __restrict__ up_scales, const strata_moe_expert_stats* __restrict__ stats,
     int H, int I, int G, uint16_t* __restrict__ a16) {
+  constexpr int LDSB = NFMAX <= 2 ? kGemmLdsSmall : kGemmLds;
   extern __shared__ __align__(16) uint8_t smem[];
-  int* rows_lds = reinterpret_cast<int*>(smem + kGemmLds - kRowsBytes);
+  int* rows_lds = reinterpret_cast<int*>(smem + LDSB - kRowsBytes);
   int* dst_lds = rows_lds + kChunkRows;
   UnitInfo u;
   if (!pick_unit(chunks, n_chunks, I / 128 / G, G, u)) return;
@@ -672,16 +678,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
   // LDS weight tiles 0, 1 = gate rows 0-63, 64-127 of the slice; 2, 3 = the same up rows
   const int ri = (wave & 1) * 32 + (threadIdx.x & 31);
 #define STRATA_UP_UNIT(NF)                                                                        \
-  run_unit<FMT, NF, true>(u, x16, H, H, rows_lds, dst_lds, wt, wsl, ssl, wave >> 1, 2 + (wave >> 1), \
-                          ri, ri, st.shift_gate, st.shift_up, xinfo, tok, st, a16, I, 128, smem)
-  switch (u.nfrag) {
-    case 1: STRATA_UP_UNIT(1); break;
-    case 2: STRATA_UP_UNIT(2); break;
-    case 3: STRATA_UP_UNIT(3); break;
-    case 4: STRATA_UP_UNIT(4); break;
-    case 5: STRATA_UP_UNIT(5); break;
-    case 6: STRATA_UP_UNIT(6); break;
-    default: STRATA_UP_UNIT(7); break;
+  run_unit<FMT, NF, true, LDSB>(u, x16, H, H, rows_lds, dst_lds, wt, wsl, ssl, wave >> 1,           \
+                                2 + (wave >> 1), ri, ri, st.shift_gate, st.shift_up, xinfo, tok, st, \
+                                a16, I, 128, smem)
+  if constexpr (NFMAX <= 2) {
+    if (u.nfrag == 1) STRATA_UP_UNIT(1);
+    else STRATA_UP_UNIT(2);
+  } else {
+    switch (u.nfrag) {
+      case 1: STRATA_UP_UNIT(1); break;
+      case 2: STRATA_UP_UNIT(2); break;
+      case 3: STRATA_UP_UNIT(3); break;
+      case 4: STRATA_UP_UNIT(4); break;
+      case 5: STRATA_UP_UNIT(5); break;
+      case 6: STRATA_UP_UNIT(6); break;
+      default: STRATA_UP_UNIT(7); break;
+    }
   }
 #undef STRATA_UP_UNIT
 }
@@ -690,15 +702,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_up_kernel(
 // Down projection: out[slot(p)][h] = A[p] . W_d[h] for the chunk's rows p, written as bf16 in
 // slot order.  Slice = 256 outputs; wave w owns h = slice*256 + w*64 + nf*32 + (lane % 32).
 
-template <int FMT>
-__global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
+template <int FMT, int NFMAX>
+__global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_down_kernel(
     const uint16_t* __restrict__ a16, const XInfo* __restrict__ xinfo,
     const int* __restrict__ sorted_slot, int k, const Chunk* __restrict__ chunks,
     const int* __restrict__ n_chunks, const uint8_t* __restrict__ down_codes,
     const uint16_t* __restrict__ down_scales, const strata_moe_expert_stats* __restrict__ stats,
     int H, int I, int G, uint16_t* __restrict__ expert_out) {
+  constexpr int LDSB = NFMAX <= 2 ? kGemmLdsSmall : kGemmLds;
   extern __shared__ __align__(16) uint8_t smem[];
-  int* rows_lds = reinterpret_cast<int*>(smem + kGemmLds - kRowsBytes);
+  int* rows_lds = reinterpret_cast<int*>(smem + LDSB - kRowsBytes);
   int* dst_lds = rows_lds + kChunkRows;
   UnitInfo u;
   if (!pick_unit(chunks, n_chunks, H / 256 / G, G, u)) return;
@@ -722,16 +735,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_down_kernel(
   // LDS weight tile w = rows 64 w .. 64 w + 63 of the slice
   const int ri = threadIdx.x & 31;
 #define STRATA_DOWN_UNIT(NF)                                                                      \
-  run_unit<FMT, NF, false>(u, a16, I, I, rows_lds, dst_lds, wt, wsl, ssl, wave, wave, ri, 32 + ri, \
-                           st.shift_down, st.shift_down, xinfo, tok, st, expert_out, H, 256, smem)
-  switch (u.nfrag) {
-    case 1: STRATA_DOWN_UNIT(1); break;
-    case 2: STRATA_DOWN_UNIT(2); break;
-    case 3: STRATA_DOWN_UNIT(3); break;
-    case 4: STRATA_DOWN_UNIT(4); break;
-    case 5: STRATA_DOWN_UNIT(5); break;
-    case 6: STRATA_DOWN_UNIT(6); break;
-    default: STRATA_DOWN_UNIT(7); break;
+  run_unit<FMT, NF, false, LDSB>(u, a16, I, I, rows_lds, dst_lds, wt, wsl, ssl, wave, wave, ri,    \
+                                 32 + ri, st.shift_down, st.shift_down, xinfo, tok, st, expert_out, \
+                                 H, 256, smem)
+  if constexpr (NFMAX <= 2) {
+    if (u.nfrag == 1) STRATA_DOWN_UNIT(1);
+    else STRATA_DOWN_UNIT(2);
+  } else {
+    switch (u.nfrag) {
+      case 1: STRATA_DOWN_UNIT(1); break;
+      case 2: STRATA_DOWN_UNIT(2); break;
+      case 3: STRATA_DOWN_UNIT(3); break;
+      case 4: STRATA_DOWN_UNIT(4); break;
+      case 5: STRATA_DOWN_UNIT(5); break;
+      case 6: STRATA_DOWN_UNIT(6); break;
+      default: STRATA_DOWN_UNIT(7); break;
+    }
   }
 #undef STRATA_DOWN_UNIT
 }
@@ -906,8 +925,8 @@ static int grid_for_units(int64_t max_units) { return (int)(8 * ((max_units + 7)
 // units per CU for the fewest chunks S slots can make.  More slices per unit pay the unit's fixed
 // costs (launch, row tables, pipeline fill) once for several slices; fewer keep enough units to
 // fill and balance the CUs (a skewed routing concentrates the slots in few chunks).
-static int slices_per_unit(int n_slices, int gmax, int64_t S) {
-  const int64_t min_chunks = (S + kChunkRows - 1) / kChunkRows;
+static int slices_per_unit(int n_slices, int gmax, int64_t S, int chunk_rows) {
+  const int64_t min_chunks = (S + chunk_rows - 1) / chunk_rows;
   for (int g = gmax; g > 1; --g)
     if (n_slices % g == 0 && min_chunks * (n_slices / g) >= 2 * 256) return g;
   return 1;
@@ -917,12 +936,18 @@ static int slices_per_unit(int n_slices, int gmax, int64_t S) {
 static void allow_big_lds() {
   static std::once_flag once;
   std::call_once(once, [] {
-    const void* ks[4] = {reinterpret_cast<const void*>(ffn_up_kernel<2>),
-                         reinterpret_cast<const void*>(ffn_up_kernel<3>),
-                         reinterpret_cast<const void*>(ffn_down_kernel<2>),
-                         reinterpret_cast<const void*>(ffn_down_kernel<3>)};
-    for (const void* k : ks)
+    const void* big[4] = {reinterpret_cast<const void*>(ffn_up_kernel<2, 7>),
+                          reinterpret_cast<const void*>(ffn_up_kernel<3, 7>),
+                          reinterpret_cast<const void*>(ffn_down_kernel<2, 7>),
+                          reinterpret_cast<const void*>(ffn_down_kernel<3, 7>)};
+    const void* small[4] = {reinterpret_cast<const void*>(ffn_up_kernel<2, 2>),
+                            reinterpret_cast<const void*>(ffn_up_kernel<3, 2>),
+                            reinterpret_cast<const void*>(ffn_down_kernel<2, 2>),
+                            reinterpret_cast<const void*>(ffn_down_kernel<3, 2>)};
+    for (const void* k : big)
       (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    for (const void* k : small)
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLdsSmall);
   });
 }
 
@@ -934,45 +959,57 @@ hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo
 }
 
 hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const int* sorted_slot,
-                         int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_chunks_,
-                         const void* gate_codes, const void* up_codes, const uint16_t* gate_scales,
-                         const uint16_t* up_scales, const strata_moe_expert_stats* stats, int E,
-                         int H, int I, uint16_t* a16, hipStream_t s) {
+                         int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_small,
+                         int max_large, const void* gate_codes, const void* up_codes,
+                         const uint16_t* gate_scales, const uint16_t* up_scales,
+                         const strata_moe_expert_stats* stats, int E, int H, int I, uint16_t* a16,
+                         hipStream_t s) {
   (void)E;
-  const int G = slices_per_unit(I / 128, 1, S);
-  const int grid = grid_for_units((int64_t)max_chunks_ * (I / 128 / G));
   const uint8_t* gc = static_cast<const uint8_t*>(gate_codes);
   const uint8_t* uc = static_cast<const uint8_t*>(up_codes);
   allow_big_lds();
-  if (fmt == 2)
-    ffn_up_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(x16, xinfo, sorted_slot, k, chunks,
-                                                          n_chunks, gc, uc, gate_scales, up_scales,
-                                                          stats, H, I, G, a16);
-  else
-    ffn_up_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(x16, xinfo, sorted_slot, k, chunks,
-                                                          n_chunks, gc, uc, gate_scales, up_scales,
-                                                          stats, H, I, G, a16);
+#define STRATA_LAUNCH_UP(F, NFM, LDSB, CH, NCH, G, GRID)                                          \
+  ffn_up_kernel<F, NFM><<<GRID, kGemmThreads, LDSB, s>>>(x16, xinfo, sorted_slot, k, CH, NCH, gc, uc, \
+                                                         gate_scales, up_scales, stats, H, I, G, a16)
+  if (max_small > 0) {  // the small part: one slice per unit
+    const int grid = grid_for_units((int64_t)max_small * (I / 128));
+    if (fmt == 2) STRATA_LAUNCH_UP(2, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
+    else STRATA_LAUNCH_UP(3, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int G = slices_per_unit(I / 128, 1, S, kChunkRows);
+  const int grid = grid_for_units((int64_t)max_large * (I / 128 / G));
+  if (fmt == 2) STRATA_LAUNCH_UP(2, 7, kGemmLds, chunks + max_small, n_chunks + 1, G, grid);
+  else STRATA_LAUNCH_UP(3, 7, kGemmLds, chunks + max_small, n_chunks + 1, G, grid);
+#undef STRATA_LAUNCH_UP
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
                            const int* sorted_slot, int k, int64_t S, const Chunk* chunks,
-                           const int* n_chunks, int max_chunks_, const void* down_codes,
-                           const uint16_t* down_scales, const strata_moe_expert_stats* stats,
-                           int E, int H, int I, uint16_t* expert_out, hipStream_t s) {
+                           const int* n_chunks, int max_small, int max_large,
+                           const void* down_codes, const uint16_t* down_scales,
+                           const strata_moe_expert_stats* stats, int E, int H, int I,
+                           uint16_t* expert_out, hipStream_t s) {
   (void)E;
-  const int G = slices_per_unit(H / 256, 2, S);
-  const int grid = grid_for_units((int64_t)max_chunks_ * (H / 256 / G));
   const uint8_t* dc = static_cast<const uint8_t*>(down_codes);
   allow_big_lds();
-  if (fmt == 2)
-    ffn_down_kernel<2><<<grid, kGemmThreads, kGemmLds, s>>>(a16, xinfo, sorted_slot, k, chunks,
-                                                            n_chunks, dc, down_scales, stats, H, I,
-                                                            G, expert_out);
-  else
-    ffn_down_kernel<3><<<grid, kGemmThreads, kGemmLds, s>>>(a16, xinfo, sorted_slot, k, chunks,
-                                                            n_chunks, dc, down_scales, stats, H, I,
-                                                            G, expert_out);
+#define STRATA_LAUNCH_DOWN(F, NFM, LDSB, CH, NCH, G, GRID)                                        \
+  ffn_down_kernel<F, NFM><<<GRID, kGemmThreads, LDSB, s>>>(a16, xinfo, sorted_slot, k, CH, NCH, dc, \
+                                                           down_scales, stats, H, I, G, expert_out)
+  if (max_small > 0) {  // the small part: one slice per unit
+    const int grid = grid_for_units((int64_t)max_small * (H / 256));
+    if (fmt == 2) STRATA_LAUNCH_DOWN(2, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
+    else STRATA_LAUNCH_DOWN(3, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int G = slices_per_unit(H / 256, 2, S, kChunkRows);
+  const int grid = grid_for_units((int64_t)max_large * (H / 256 / G));
+  if (fmt == 2) STRATA_LAUNCH_DOWN(2, 7, kGemmLds, chunks + max_small, n_chunks + 1, G, grid);
+  else STRATA_LAUNCH_DOWN(3, 7, kGemmLds, chunks + max_small, n_chunks + 1, G, grid);
+#undef STRATA_LAUNCH_DOWN
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ def log(msg):
 
 
 CHUNK_ROWS, FRAG = 224, 32  # rows of one grouped-GEMM work unit, rows of a matrix-core fragment
+SMALL_CHUNK_ROWS = 64        # the most rows of an expert whose segment is one small-fragment unit
 
 
 def oracle_rows(w_np, x_np, l_np, k, rows):
@@ -43,13 +44,15 @@ def oracle_rows(w_np, x_np, l_np, k, rows):
 
 def coverage_rows(counts, offsets, sorted_slot, k, rng, n_random):
     """Tokens whose rows reach every expert's first and last (ragged) fragment and both ends of
-    every GEMM work unit (the chunks of at most 224 rows an expert's segment is cut into, split
-    into balanced 32-row fragments), plus random tokens."""
+    every GEMM work unit (an expert's segment is one chunk of the small-fragment GEMMs when it has
+    at most 64 rows and the slots average at most 128 rows per expert, else chunks of at most 224
+    rows, split into balanced 32-row fragments), plus random tokens."""
     pos = []
+    small_rows = SMALL_CHUNK_ROWS if len(sorted_slot) <= 128 * len(counts) else 0
     for e in np.nonzero(counts)[0]:
         cnt, row = int(counts[e]), int(offsets[e])
         nfrag = -(-cnt // FRAG)
-        nch = -(-nfrag // (CHUNK_ROWS // FRAG))
+        nch = 1 if cnt <= small_rows else -(-nfrag // (CHUNK_ROWS // FRAG))
         fb, extra = divmod(nfrag, nch)
         used = 0
         for c in range(nch):

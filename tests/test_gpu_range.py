@@ -1,6 +1,6 @@
 """GPU parity over the input range the C ABI accepts: activations far from unit scale, block
 scales near the edges of fp16, sparse activation rows, on the prefill path (grouped fp16 GEMMs,
-T >= 65) and on the decode path, against the fp64 oracle at 5e-3 per-row relative L2.
+T >= 41) and on the decode path, against the fp64 oracle at 5e-3 per-row relative L2.
 
 The pages say GPU and CPU expert results differ only at noise level ("Two-Day Port, 8x Faster
 Prefill: Strata Engine Benchmarked", Deployment and Three Pitfalls You Must Know); the layer's
@@ -68,7 +68,7 @@ MID3 = mi.Shape("mid3", T=80, H=1024, E=32, k=4, I=256, fmt=3)
 @pytest.mark.parametrize("shape", [MID, MID3], ids=lambda s: s.name)
 @pytest.mark.parametrize("xs", [2.0 ** -30, 2.0 ** -12, 2.0 ** -9, 2.0 ** 6, 2.0 ** 8, 2.0 ** 30])
 def test_activation_scales(shape, xs):
-    """x scaled by powers of two: T = 80 runs the grouped GEMMs, T = 48 the sliced decode path,
+    """x scaled by powers of two: T = 80 runs the grouped GEMMs, T = 40 the sliced decode path,
     both against the oracle on the same rows."""
     log(f"activation scale {xs:g} {shape.name}")
     w_np = mi.make_weights(shape, seed=1)
@@ -77,10 +77,10 @@ def test_activation_scales(shape, xs):
     l = mi.make_logits(shape, seed=1)
     ref = oracle.layer(w_np, x, l, shape.k)
     err = rel_l2_rows(run_layer(w, x, l, shape.k, shape.H), ref)
-    err48 = rel_l2_rows(run_layer(w, x[:48], l[:48], shape.k, shape.H), ref[:48])
-    log(f"  prefill path max rel-L2 {err.max():.3e}, decode slices {err48.max():.3e}")
+    err40 = rel_l2_rows(run_layer(w, x[:40], l[:40], shape.k, shape.H), ref[:40])
+    log(f"  prefill path max rel-L2 {err.max():.3e}, decode slices {err40.max():.3e}")
     assert err.max() <= TOL_REL_L2
-    assert err48.max() <= TOL_REL_L2
+    assert err40.max() <= TOL_REL_L2
 
 
 @pytest.mark.parametrize("shape", [MID, MID3], ids=lambda s: s.name)
