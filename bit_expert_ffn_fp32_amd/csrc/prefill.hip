@@ -503,6 +503,18 @@ STRATA_DEVICE void stage_steps(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], Stage
     read_frags<NF>(xt, m, hh, s + 1, ss.a[(s + 1) & 1]);
     decode_step<FMT>(ss.sw, s + 1, ss.b[(s + 1) & 1], ksel);
     mfma_step<NF>(acc0, acc1, ss.a[s & 1], ss.b[s & 1], 0, NF);
+    // One wave per SIMD issues in order: spread the step's other instructions (copies, fragment
+    // reads, decode) between its matrix ops, four after each, so that neither waits behind a
+    // long run of the other.  (2-bit: T = 8192 expert FFN 819 -> 855 TFLOP/s; group sizes 3-8
+    // measured, 4 best.  The 3-bit decode, with more VALU work per step, measured slower with
+    // any group size and keeps the compiler's order.)
+    if constexpr (FMT == 2) {
+#pragma unroll
+      for (int i = 0; i < 2 * NF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // a matrix op
+        __builtin_amdgcn_sched_group_barrier(0x002 | 0x004 | 0x020 | 0x100, 4, 0);  // VALU, SALU, VMEM and DS reads
+      }
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   mfma_step<NF>(acc0, acc1, ss.a[1], ss.b[1], 0, PRE);
