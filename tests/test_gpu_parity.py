@@ -230,6 +230,43 @@ def test_layer_against_oracle(s):
     np.testing.assert_allclose(ya, y0 + y, rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("n_small", [70, 60], ids=["split", "fallback"])
+def test_chunk_list_boundaries(n_small):
+    """Routing crafted so that experts hold exactly 1, 31, 32, 33, 63 and 64 rows (one chunk each in
+    the small-fragment part of the GEMM chunk list) and 65, 96, 97, 224, 225, 300 and 449 rows (the
+    large part: 224 is one 7-fragment chunk, 225 two, 449 three), plus untouched experts.  With
+    I = 1024 the small part needs 64 such experts: 70 use it, 60 fall back to the large part for
+    every expert.  Rows at both ends of every expert's segment and at its fragment boundaries,
+    plus random rows, against the oracle."""
+    small = [1, 2, 31, 32, 33, 63, 64]
+    large = [65, 96, 97, 224, 225, 300, 449]
+    counts = [small[i % len(small)] for i in range(n_small)] + large + [0] * 4
+    E = len(counts)
+    T = sum(counts)
+    s = mi.Shape(f"chunks_{n_small}", T=T, H=256, E=E, k=1, I=1024)
+    rng = np.random.default_rng(11 + n_small)
+    target = rng.permutation(np.repeat(np.arange(E), counts))
+    L = Layer(s)
+    L.l_np = (rng.standard_normal((T, E)) * 0.01).astype(np.float32)
+    L.l_np[np.arange(T), target] = 1.0
+    L.logits = to_dev(L.l_np)
+    log(f"chunk list boundaries: {n_small} small experts, T = {T}")
+    y, ids, _ = gpu_layer(L)
+    assert np.array_equal(ids[:, 0], target)
+    rows = set(rng.choice(T, size=64, replace=False).tolist())
+    for e in range(E):
+        toks = np.nonzero(target == e)[0]  # slot order = token order (k = 1)
+        for p in (0, 30, 31, 32, 33, 63, 64, 65, 223, 224, 225, len(toks) - 1):
+            if 0 <= p < len(toks):
+                rows.add(int(toks[p]))
+    rows = np.array(sorted(rows))
+    err = rel_l2_rows(y[rows], oracle.layer_rows(L.w_np, L.x_np, L.l_np, 1, rows))
+    log(f"  {len(rows)} rows, max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL_REL_L2
+    y2, _, _ = gpu_layer(L)
+    assert np.array_equal(y, y2), "second call differs"
+
+
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_decode_crowded_routing(T):
     """Routing inside the decode kernel where more than 64 entries reach the k-th largest lane
