@@ -1010,10 +1010,11 @@ hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
 #define STRATA_LAUNCH_DOWN(F, NFM, LDSB, CH, NCH, G, GRID)                                        \
   ffn_down_kernel<F, NFM><<<GRID, kGemmThreads, LDSB, s>>>(a16, xinfo, sorted_slot, k, CH, NCH, dc, \
                                                            down_scales, stats, H, I, G, expert_out)
-  if (max_small > 0) {  // the small part: one slice per unit
-    const int grid = grid_for_units((int64_t)max_small * (H / 256));
-    if (fmt == 2) STRATA_LAUNCH_DOWN(2, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
-    else STRATA_LAUNCH_DOWN(3, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
+  if (max_small > 0) {  // the small part: two slices per unit (24 stages: K = I is short)
+    const int Gs = (H / 256) % 2 == 0 ? 2 : 1;
+    const int grid = grid_for_units((int64_t)max_small * (H / 256 / Gs));
+    if (fmt == 2) STRATA_LAUNCH_DOWN(2, 2, kGemmLdsSmall, chunks, n_chunks, Gs, grid);
+    else STRATA_LAUNCH_DOWN(3, 2, kGemmLdsSmall, chunks, n_chunks, Gs, grid);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
