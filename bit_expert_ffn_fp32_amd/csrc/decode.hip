@@ -193,15 +193,17 @@ STRATA_DEVICE void load_row_chunks(RowChunks<FMT, MC>& rc, const uint8_t* row_co
     if (ch < nchunk) {
       const uint8_t* cp = row_codes + (size_t)ch * (8 * CB);
       if constexpr (FMT == 2) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cp);
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp));
         rc.w[i][0] = v[0]; rc.w[i][1] = v[1]; rc.w[i][2] = v[2]; rc.w[i][3] = v[3];
       } else {
-        const uint2* p = reinterpret_cast<const uint2*>(cp);
-        const uint2 a = p[0], b = p[1], d = p[2];
-        rc.w[i][0] = a.x; rc.w[i][1] = a.y; rc.w[i][2] = b.x; rc.w[i][3] = b.y;
-        rc.w[i][4] = d.x; rc.w[i][5] = d.y;
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t* p = reinterpret_cast<const u32x2_t*>(cp);
+        const u32x2_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1),
+                      d = __builtin_nontemporal_load(p + 2);
+        rc.w[i][0] = a[0]; rc.w[i][1] = a[1]; rc.w[i][2] = b[0]; rc.w[i][3] = b[1];
+        rc.w[i][4] = d[0]; rc.w[i][5] = d[1];
       }
-      rc.sc[i] = *reinterpret_cast<const uint32_t*>(row_scales + (size_t)ch * 8);
+      rc.sc[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row_scales + (size_t)ch * 8));
     }
   }
 }
