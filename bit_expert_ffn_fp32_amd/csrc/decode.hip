@@ -10,7 +10,7 @@
 // costs far more, because the per-XCD L2s must be written back and invalidated):
 //  K1 up:   one 16-wave workgroup per CU.  Every workgroup routes all T tokens itself (one wave
 //           per token), lists the distinct experts and the (token, slot) pairs of each, and works
-//           through a contiguous range of items (distinct expert, 16 rows of I), four waves per
+//           through a contiguous range of items (distinct expert, 4 rows of I), one wave per
 //           item: a = SiLU(g) * u per token, rounded to bf16.  Workgroup 0 publishes the routing
 //           for K2 and the caller.
 //  K2 down: workgroup b owns rows [b R, (b+1) R) of H (R = H / 256) for ALL distinct experts, so it
@@ -41,7 +41,7 @@ constexpr int kGrid = 256;         // one workgroup per CU
 constexpr int kDecMaxT = 8;
 constexpr int kDecMaxS = 128;      // T * k <= 8 * 16
 constexpr int kDecMaxR = 16;       // rows of H per K2 workgroup (H <= 4096)
-constexpr int kUpRows = 16;        // rows of I per K1 item (4 per wave, 16 lanes per row)
+constexpr int kUpRows = 4;         // rows of I per K1 item: one wave, 16 lanes per row
 constexpr int kDnPieces = 9;       // K2: 16-byte pieces of staged a per thread (<= 144 KB of LDS)
 
 
@@ -331,18 +331,14 @@ STRATA_DEVICE void item_range(const RouteTable& rt, int blocks, int S, int& begi
   const int lane = threadIdx.x & 63, nd = rt.nd;
   const int t0 = 2 * lane < nd ? rt.dtp[2 * lane] : 0;
   const int t1 = 2 * lane + 1 < nd ? rt.dtp[2 * lane + 1] : 0;
-  int inc = t0 + t1;  // tokens of the distinct experts 0 .. 2 lane + 1
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o);
-    if (lane >= o) inc += v;
-  }
-  // the first item whose weight prefix is >= target
+  const int inc = wave_scan_dpp(t0 + t1);  // tokens of the distinct experts 0 .. 2 lane + 1
+  // the first item whose weight prefix is >= target (l is uniform: lane reads, no shuffles)
   auto item_at = [&](int target) {
     const uint64_t hit = __ballot(2 * lane < nd && inc * blocks >= target);
     if (hit == 0) return nd * blocks;
     const int l = __ffsll((unsigned long long)hit) - 1;
-    const int ta = __shfl(t0, l), tb = __shfl(t1, l), ex = __shfl(inc, l) - ta - tb;
+    const int ta = __builtin_amdgcn_readlane(t0, l), tb = __builtin_amdgcn_readlane(t1, l);
+    const int ex = __builtin_amdgcn_readlane(inc, l) - ta - tb;
     const bool first = (ex + ta) * blocks >= target;
     const int d = first ? 2 * l : 2 * l + 1, cum = first ? ex : ex + ta, tp = first ? ta : tb;
     return d * blocks + (target - cum * blocks + tp - 1) / tp;
@@ -353,7 +349,8 @@ STRATA_DEVICE void item_range(const RouteTable& rt, int blocks, int S, int& begi
 }
 
 // ---------------------------------------------------------------------------------------------
-// K1: route + gate/up GEMV + SiLU*mul.  Items (distinct expert d, block of 16 rows of I).
+// K1: route + gate/up GEMV + SiLU*mul.  Items (distinct expert d, block of 4 rows of I), one wave
+// each (16 lanes per row).
 //
 // RES (layer stacks): the input is the residual stream h (fp32) and x = bf16(h / rms(h)) is formed
 // here.  While the routing waves route, every other thread loads its blocks of h (at most two:
@@ -495,15 +492,14 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   item_range(rt, blocks, S, it, end);
   if (it >= end) return;
   constexpr int CB = FMT == 2 ? 8 : 12;
-  constexpr int kGroups = kUpThreads / 256;  // four waves (16 rows) per item
-  const int lane = tid & 63, wave = tid >> 6, c = lane & 15;
-  const int grp = wave >> 2, rsub = (wave & 3) * 4 + (lane >> 4);
+  constexpr int kGroups = kUpThreads / 64;  // one wave per item
+  const int lane = tid & 63, wave = tid >> 6, c = lane & 15, rl = lane >> 4;
   // (gate row, up row) of one item in flight per wave: a second batch of loads would only queue
   // behind the first (the load pipeline is already full), and costs registers
   constexpr bool kTwo = false;
   RowChunks<FMT, MC> gu[kTwo ? 2 : 1][2];
   auto load_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
-    const int d = item / blocks, n = (item % blocks) * kUpRows + rsub;
+    const int d = item / blocks, n = (item % blocks) * kUpRows + rl;
     const size_t row = (size_t)rt.dexp[d] * I + n;
     load_row_chunks<FMT, MC>(rr[0], tiled_row_codes<FMT>(gate_codes, row, nchunk),
                              tiled_row_scales(gate_scales, row, nchunk), nchunk, c, 16);
@@ -513,10 +509,10 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   // a = SiLU(g) u, rounded to bf16, goes out already in K2's staged layout without the chunk
   // padding: row n = 16 q + rsub is value rsub of word q & 3 of chunk q >> 2, i.e. half rsub >> 3
   // of pair m = rsub & 7, multiplied by that pair's power of two (exact).
-  const int m_a = rsub & 7;
-  const float sc_a = FMT == 2 ? (m_a % 3 == 0 ? 64.0f : m_a % 3 == 1 ? 16.0f : 4.0f) : 2.0f;
   auto compute_item = [&](int item, RowChunks<FMT, MC> (&rr)[2]) {
-    const int d = item / blocks, q = item % blocks;
+    const int d = item / blocks, n = (item % blocks) * kUpRows + rl;
+    const int q = n >> 4, rsub = n & 15, m_a = rsub & 7;
+    const float sc_a = FMT == 2 ? (m_a % 3 == 0 ? 64.0f : m_a % 3 == 1 ? 16.0f : 4.0f) : 2.0f;
     const int Tp = rt.dtp[d];
     for (int tt = 0; tt < Tp; ++tt) {
       const int t = rt.dtok[d][tt];
@@ -564,7 +560,7 @@ __global__ __launch_bounds__(kUpThreads) void decode_up_kernel(
   if constexpr (RES && kStageEarly) stage_res();
   // (no barrier after the first weight loads: they are accepted only as fast as data returns, so
   // a barrier would hold every wave until the whole first batch had been issued)
-  it += grp;
+  it += wave;
   if (it < end) load_item(it, gu[0]);
   if constexpr (RES && !kStageEarly) stage_res();
   if constexpr (kTwo) {

@@ -59,6 +59,27 @@ STRATA_DEVICE int wave_min_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Wave-wide float sum, result uniform: row sums by DPP, then the rows folded into lane 63 by the
+// two row broadcasts (no LDS round trip, unlike a shuffle butterfly).
+STRATA_DEVICE float wave_sum_dpp(float v) {
+  v = sum16(v);
+  v += __builtin_bit_cast(float, dpp_u<0x142, 0xA>(__builtin_bit_cast(uint32_t, v), 0u));  // row_bcast:15
+  v += __builtin_bit_cast(float, dpp_u<0x143, 0xC>(__builtin_bit_cast(uint32_t, v), 0u));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Inclusive prefix sum of ints across the wave's lanes: shifts within each row of 16 lanes, then
+// the row broadcasts carry each row's total into the rows above it.
+STRATA_DEVICE int wave_scan_dpp(int v) {
+  v += (int)dpp_u<0x111>((uint32_t)v, 0u);  // row_shr:1
+  v += (int)dpp_u<0x112>((uint32_t)v, 0u);  // row_shr:2
+  v += (int)dpp_u<0x114>((uint32_t)v, 0u);  // row_shr:4
+  v += (int)dpp_u<0x118>((uint32_t)v, 0u);  // row_shr:8
+  v += (int)dpp_u<0x142, 0xA>((uint32_t)v, 0u);  // row_bcast:15 into rows 1 and 3
+  v += (int)dpp_u<0x143, 0xC>((uint32_t)v, 0u);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Order-preserving map of a logit to an unsigned key (-0 is first made +0, so equal logits get
 // equal keys; every finite logit maps to a key above 0, which marks an empty entry), and back.
 STRATA_DEVICE uint32_t route_key(float v) {
@@ -210,7 +231,7 @@ STRATA_DEVICE void select_token_wave(TokenKeys<NPL>& tk, int E, int k, int* ids_
   if (!select_threshold<NPL>(tk.c, k, lds, my_key, my_i)) select_rounds<NPL>(tk.c, k, my_key, my_i);
   const float top = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
   const float ex = lane < k ? expf(key_value(my_key) - top) : 0.0f;
-  const float den = wave_sum(ex);
+  const float den = wave_sum_dpp(ex);
   if (lane < k) {
     ids_out[lane] = my_i;
     w_out[lane] = ex / den;
