@@ -659,11 +659,13 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
                                                                      : 2.0f + 1.5f / 4.0f)
                       : 11.5f / 2.0f;
     }
+    // (row, position) of piece q, stepped from piece to piece instead of divided out each time
+    const int rstep = kDnThreads / ppr, pstep = kDnThreads - rstep * ppr;
+    int row = tid / ppr, pr = tid - row * ppr;
 #pragma unroll
     for (int i = 0; i < kDnPieces; ++i) {
       const int q = tid + kDnThreads * i;
       if (q - (q & 3) < ncp) {  // the whole quad is in range or out (ncp is a multiple of 4)
-        const int row = q / ppr, pr = q - row * ppr;
         *reinterpret_cast<u32x4_t*>(pairs + row * rs + kChunkDwords * (pr >> 3) + 4 * (pr & 7)) = cv[i];
         float c = 0.0f;
 #pragma unroll
@@ -673,6 +675,12 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
         }
         c = sum4(c);
         if ((q & 3) == 0) cs[q >> 2] = c;
+      }
+      row += rstep;
+      pr += pstep;
+      if (pr >= ppr) {
+        pr -= ppr;
+        ++row;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
