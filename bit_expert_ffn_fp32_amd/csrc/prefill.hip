@@ -441,7 +441,9 @@ STRATA_DEVICE void write_slice(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], uint1
       const int p = threadIdx.x + i * kGemmThreads;
       const int r = p / EP::kPieces, c = p % EP::kPieces;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rb + r * EP::kRow + c * 8);
-      *reinterpret_cast<u32x4_t*>(out + (size_t)dst_lds[f * 32 + r] * out_ld + col0 + c * 8) = v;
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)dst_lds[f * 32 + r] * out_ld + col0 + c * 8);
+      if constexpr (UP) *dst = v;                         // a: read again by the down GEMM
+      else __builtin_nontemporal_store(v, dst);           // expert outputs: read once, by the combine
     }
   }
 }
@@ -815,7 +817,7 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < kXRegPieces; ++j) {
     const int i = lane + 64 * j;
-    v[j] = i < n8 ? src[i] : u32x4_t{0, 0, 0, 0};
+    v[j] = i < n8 ? __builtin_nontemporal_load(src + i) : u32x4_t{0, 0, 0, 0};  // x is read once
 #pragma unroll
     for (int m = 0; m < 4; ++m) mx = bf16_pair_max_mag(v[j][m], mx);
   }
@@ -865,7 +867,7 @@ __global__ void combine_kernel(const uint16_t* __restrict__ out, const float* __
   for (int j = 0; j < kCombineMaxK; ++j) {
     if (j < k) {
       wj[j] = w[(size_t)t * k + j];
-      v[j] = *reinterpret_cast<const u32x4_t*>(out + ((size_t)t * k + j) * H + c * 8);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(out + ((size_t)t * k + j) * H + c * 8));
     }
   }
 #pragma unroll
