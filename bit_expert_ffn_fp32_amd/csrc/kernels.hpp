@@ -21,6 +21,7 @@ struct Chunk {
 constexpr int kChunkRows = 224;      // rows of one GEMM work unit (at most 7 fragments of 32)
 constexpr int kChunkRowsSmall = 64;  // the same for the small-fragment GEMMs (at most 2)
 constexpr int kPermTile = 1024;      // slots per permute tile
+constexpr int kSkinnyRows = 32;      // rows of a chunk the skinny GEMMs take (one fragment)
 
 // The grouped GEMMs' chunk list has two parts.  An expert with at most small_rows rows gets one
 // chunk in the small part, run by the small-fragment GEMMs (two workgroups per CU, so that one's
@@ -84,7 +85,9 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 
 // Where the chunk list goes and how it is split (small_chunk_rows, min_small_experts,
 // max_small_chunks): the small part at chunks[0 ..) with its count in n_chunks[0], the large part
-// at chunks[max_small ..) with its count in n_chunks[1].
+// at chunks[max_small ..) with its count in n_chunks[1].  The small part lists its chunks of at
+// most kSkinnyRows rows first (their count in n_chunks[2]); those run on the skinny GEMMs, the
+// rest of the small part on the small-fragment GEMMs.
 struct ChunkList {
   Chunk* chunks;
   int* n_chunks;
@@ -115,7 +118,8 @@ hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo
 
 // S: the number of slots (sizes the work units; the chunk list itself is read on the device).
 // chunks / n_chunks: the two-part list of launch_permute, with max_small and max_large its parts'
-// capacities; the small part runs on the small-fragment GEMMs (if max_small > 0), then the large.
+// capacities; the small part runs on the skinny and the small-fragment GEMMs (if max_small > 0),
+// then the large.
 hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const int* sorted_slot,
                          int k, int64_t S, const Chunk* chunks, const int* n_chunks, int max_small,
                          int max_large,

@@ -10,8 +10,9 @@
 //              (LDS integer atomics: the result is order independent).
 //  2. scan:    one workgroup turns the histograms into counts, offsets (exclusive prefix sum)
 //              and each tile's starting position per expert; it also cuts every expert's segment
-//              into the GEMM chunk list (one chunk per expert of at most kChunkRowsSmall rows, chunks
-//              of up to kChunkRows rows for the others, balanced in 32-row fragments).
+//              into the GEMM chunk list (one chunk per expert of at most kChunkRowsSmall rows, those
+//              of at most kSkinnyRows first; chunks of up to kChunkRows rows for the others,
+//              balanced in 32-row fragments).
 //  3. scatter: each tile ranks its slots stably in one round of 1024 threads: a slot's rank is the
 //              number of equal ids in earlier lanes of its wave (an LDS broadcast loop), plus the
 //              counts of the earlier waves, plus the tile's starting position for its expert.
@@ -65,18 +66,25 @@ __device__ int block_exclusive_scan(int v, int* lds16, int& total) {
 
 // The two-part GEMM chunk list (see ChunkList), built by a whole 1024-thread workgroup; a thread
 // with mine holds expert e, its rows at sorted positions [off, off + cnt).  The small part is used
-// only when at least cl.min_small experts qualify for it.
+// only when at least cl.min_small experts qualify for it; within it the chunks of at most
+// kSkinnyRows rows come first, each group in expert order.
 __device__ void build_chunk_list(bool mine, int e, int off, int cnt, const ChunkList& cl, int* lds16) {
   int nsmall;
   (void)block_exclusive_scan(mine ? small_chunks_of(cnt, cl.small_rows) : 0, lds16, nsmall);
   const int sr = nsmall >= cl.min_small ? cl.small_rows : 0;
-  int stotal, ltotal;
-  const int sb = block_exclusive_scan(mine ? small_chunks_of(cnt, sr) : 0, lds16, stotal);
+  const int small = mine ? small_chunks_of(cnt, sr) : 0;
+  const bool skinny = small && cnt <= kSkinnyRows;
+  int nskinny, nrest, ltotal;
+  const int kb = block_exclusive_scan(skinny ? 1 : 0, lds16, nskinny);
+  const int rb = block_exclusive_scan(skinny ? 0 : small, lds16, nrest);
   const int lb = block_exclusive_scan(mine ? large_chunks_of(cnt, sr) : 0, lds16, ltotal);
-  if (mine) write_expert_chunks(e, off, cnt, sr, cl.chunks, sb, cl.chunks + cl.max_small, lb);
+  if (mine)
+    write_expert_chunks(e, off, cnt, sr, cl.chunks, skinny ? kb : nskinny + rb,
+                        cl.chunks + cl.max_small, lb);
   if (threadIdx.x == 0) {
-    cl.n_chunks[0] = stotal;
+    cl.n_chunks[0] = nskinny + nrest;
     cl.n_chunks[1] = ltotal;
+    cl.n_chunks[2] = nskinny;
   }
 }
 

@@ -188,16 +188,19 @@ struct UnitInfo {
 
 // Maps blockIdx to a unit (a chunk and G consecutive column slices of it); false if this
 // workgroup has none.  The units of XCD x (blockIdx % 8, with the usual round-robin dispatch) are
-// a contiguous range, so the slice groups of one chunk run side by side on one L2.
+// a contiguous range, so the slice groups of one chunk run side by side on one L2.  SMALL: the
+// list is the small part, whose first n_chunks[2] chunks belong to the skinny GEMMs.
+template <bool SMALL>
 STRATA_DEVICE bool pick_unit(const Chunk* chunks, const int* n_chunks, int n_groups, int G,
                              UnitInfo& u) {
-  const int U = *n_chunks * n_groups;
+  const int skip = SMALL ? n_chunks[2] : 0;
+  const int U = (*n_chunks - skip) * n_groups;
   const int per = (U + 7) >> 3;
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
   if (i >= per) return false;
   const int unit = xcd * per + i;
   if (unit >= U) return false;
-  const Chunk ch = chunks[unit / n_groups];
+  const Chunk ch = chunks[skip + unit / n_groups];
   u.expert = ch.expert;
   u.row_start = ch.row_start;
   u.nrows = ch.nrows;
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_up_kerne
   int* rows_lds = reinterpret_cast<int*>(smem + LDSB - kRowsBytes);
   int* dst_lds = rows_lds + kChunkRows;
   UnitInfo u;
-  if (!pick_unit(chunks, n_chunks, I / 128 / G, G, u)) return;
+  if (!pick_unit<NFMAX <= 2>(chunks, n_chunks, I / 128 / G, G, u)) return;
   constexpr int GB = 8 * (FMT == 2 ? 8 : 12);
   const int wave = threadIdx.x >> 6, nkt = H / 64;
   // wave w copies gate (w < 2) or up rows 128 slice + 64 (w & 1) .. + 63 of the expert
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_down_ker
   int* rows_lds = reinterpret_cast<int*>(smem + LDSB - kRowsBytes);
   int* dst_lds = rows_lds + kChunkRows;
   UnitInfo u;
-  if (!pick_unit(chunks, n_chunks, H / 256 / G, G, u)) return;
+  if (!pick_unit<NFMAX <= 2>(chunks, n_chunks, H / 256 / G, G, u)) return;
   constexpr int GB = 8 * (FMT == 2 ? 8 : 12);
   const int wave = threadIdx.x >> 6, nkt = I / 64;
   // wave w copies rows 256 slice + 64 w .. + 63 of the expert
@@ -767,6 +770,241 @@ __global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_down_ker
     }
   }
 #undef STRATA_DOWN_UNIT
+}
+
+// ---------------------------------------------------------------------------------------------
+// Skinny grouped GEMMs: the small part's chunks of at most 32 rows (experts few tokens picked).
+//
+// With one fragment of rows every weight byte feeds one 32 x 32 tile of matrix work, so these
+// units are bound by how fast they stream the expert's weights, not by the matrix cores.  Instead
+// of the LDS stage ring of the kernels above (whose per-stage copies and barriers cap a thin
+// unit's stream), each wave loads its own weights straight into registers, kSkDepth stages ahead
+// of its matrix ops, with two 8-wave workgroups (16 waves) per CU; the chunk's activation rows
+// are staged once in LDS, in phases of the reduction where all of them do not fit.
+//
+// Operand layout.  A stage is 128 reduction indices, two 64-index tiles of the tiled layout.
+// Lane (n, h) (n = lane % 32, h = lane / 32) loads weight row n's codes of tile 2j + h (both its
+// blocks, 16 or 24 contiguous bytes) and their two scales, and feeds them as the B operand of
+// steps 0..7 (steps 0-3 block 0, steps 4-7 block 1, 8 indices each in P8 order); the A operand of
+// lane (m, h) holds the same 8 indices of activation row m, 16 contiguous bytes of the P8-ordered
+// rows.  So every lane of a half-wave covers the same reduction indices, as the matrix op
+// requires, and one wave load reads 8 row groups x 128 contiguous bytes (both tiles).
+
+constexpr int kSkWaves = 8;
+constexpr int kSkThreads = kSkWaves * 64;
+constexpr int kSkXBytes = 32 * (1024 + 8) * 2;  // staged rows: 32 rows of 1024 indices, padded
+constexpr int kSkDepth2 = 3;                    // stages of weights in flight per wave: 2-bit
+constexpr int kSkDepth3 = 2;                    // 3-bit (larger stages, more registers each)
+
+template <int FMT>
+struct SkStage {
+  static constexpr int kW = FMT == 2 ? 4 : 6;  // code words of one row's two blocks
+  uint32_t c0[kW], c1[kW];                     // the two streams' rows
+  uint32_t s0, s1;                             // their two block scales (fp16, block 0 low)
+};
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Weights are read once per call: nontemporal loads.
+template <int FMT>
+STRATA_DEVICE void sk_load(SkStage<FMT>& r, const uint8_t* c0, const uint8_t* c1,
+                           const uint16_t* s0, const uint16_t* s1) {
+  if constexpr (FMT == 2) {
+    const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(c0));
+    const u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(c1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.c0[i] = a[i];
+      r.c1[i] = b[i];
+    }
+  } else {  // 24 bytes at 8-byte alignment
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(c0) + i);
+      const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(c1) + i);
+      r.c0[2 * i] = a[0];
+      r.c0[2 * i + 1] = a[1];
+      r.c1[2 * i] = b[0];
+      r.c1[2 * i + 1] = b[1];
+    }
+  }
+  r.s0 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(s0));
+  r.s1 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(s1));
+}
+
+// One stage's 16 matrix ops; ap: this lane's 128 staged bytes of the stage (row m, tile 2j + h).
+template <int FMT>
+STRATA_DEVICE void sk_compute(f32x16_t& acc0, f32x16_t& acc1, const SkStage<FMT>& r,
+                              const uint8_t* ap, int sh0, int sh1, const Q2Sel& ksel) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if constexpr (FMT == 2) {
+      const Q2Tab t0 = q2_table((uint16_t)(r.s0 >> (16 * b)), sh0);
+      const Q2Tab t1 = q2_table((uint16_t)(r.s1 >> (16 * b)), sh1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const half8_t a = *reinterpret_cast<const half8_t*>(ap + (4 * b + s) * 16);
+        const half8_t w0 = q2_decode(r.c0[2 * b], r.c0[2 * b + 1], s, t0, ksel);
+        const half8_t w1 = q2_decode(r.c1[2 * b], r.c1[2 * b + 1], s, t1, ksel);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w1, acc1, 0, 0, 0);
+      }
+    } else {
+      const _Float16 e0 = __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)(r.s0 >> (16 * b))), sh0 + 2);
+      const _Float16 e1 = __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)(r.s1 >> (16 * b))), sh1 + 2);
+      const half2_t d40 = {e0, e0}, d41 = {e1, e1};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const half8_t a = *reinterpret_cast<const half8_t*>(ap + (4 * b + s) * 16);
+        const half8_t w0 = q3_decode(r.c0[3 * b], r.c0[3 * b + 1], r.c0[3 * b + 2], s, d40);
+        const half8_t w1 = q3_decode(r.c1[3 * b], r.c1[3 * b + 1], r.c1[3 * b + 2], s, d41);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w1, acc1, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Stages the reduction indices [k0, k0 + klen) of the chunk's nr rows (source row row_src[m] of
+// src, ld values long) into xs, rows rs bytes apart; four 16-byte pieces a thread per round.
+STRATA_DEVICE void sk_stage_rows(uint8_t* xs, const uint16_t* __restrict__ src, int ld,
+                                 const int* row_src, int nr, int k0, int klen, int rs) {
+  const int per_row = klen >> 3, np = nr * per_row;
+  for (int p0 = threadIdx.x; p0 < np; p0 += 4 * kSkThreads) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + i * kSkThreads;
+      if (p < np) {
+        const int m = p / per_row, c = p - m * per_row;
+        v[i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)row_src[m] * ld + k0 + c * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + i * kSkThreads;
+      if (p < np) {
+        const int m = p / per_row, c = p - m * per_row;
+        *reinterpret_cast<u32x4_t*>(xs + m * rs + c * 16) = v[i];
+      }
+    }
+  }
+}
+
+// UP: a16 rows of the chunk = SiLU(x W_g^T) * (x W_u^T) for 256 outputs of I per unit (wave w:
+// outputs 32 w .. 32 w + 31 of the unit, gate rows as stream 0 and up rows as stream 1), NI = 1.
+// !UP: expert_out rows = a W_d^T for 8 NI items of 64 rows of H per unit (wave w, item i: rows
+// 64 (8 (unit part * NI + i) + w) .. + 63, its halves as the two streams).  upc: units per chunk.
+// An item past the matrix's end repeats the last one and is not stored.
+template <int FMT, bool UP, int P>
+__global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void ffn_skinny_kernel(
+    const uint16_t* __restrict__ src, const XInfo* __restrict__ xinfo,
+    const int* __restrict__ sorted_slot, int k, const Chunk* __restrict__ chunks,
+    const int* __restrict__ n_chunks, const uint8_t* __restrict__ codes0,
+    const uint8_t* __restrict__ codes1, const uint16_t* __restrict__ scales0,
+    const uint16_t* __restrict__ scales1, const strata_moe_expert_stats* __restrict__ stats,
+    int H, int I, int upc, int NI, uint16_t* __restrict__ out) {
+  constexpr int CB = FMT == 2 ? 8 : 12;
+  constexpr int GB = 8 * CB;  // code bytes of a 4-row group's 64-index tile
+  __shared__ int row_src[kSkinnyRows], row_dst[kSkinnyRows], row_ex[kSkinnyRows];
+  extern __shared__ __align__(16) uint8_t xs[];
+  const int U = n_chunks[2] * upc;
+  const int per = (U + 7) >> 3, bi = blockIdx.x >> 3;
+  if (bi >= per) return;
+  const int unit = (blockIdx.x & 7) * per + bi;  // consecutive units on one XCD
+  if (unit >= U) return;
+  const Chunk ch = chunks[unit / upc];
+  const int part = unit % upc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int K = UP ? H : I, nkt = K / 64, NS = K / 128, nr = ch.nrows;
+  const strata_moe_expert_stats st = stats[ch.expert];
+  if (tid < nr) {
+    const int slot = sorted_slot[ch.row_start + tid], tok = slot / k;
+    row_src[tid] = UP ? tok : ch.row_start + tid;
+    row_dst[tid] = UP ? ch.row_start + tid : slot;
+    row_ex[tid] = row_exponent<UP>(xinfo[tok], st);
+  }
+  // phases: the longest run of whole stages whose nr rows fit, spread evenly over the phases
+  const int kfit = (kSkXBytes / (2 * nr) - 8) & ~127;
+  const int nph = (K + kfit - 1) / kfit, sp = (NS + nph - 1) / nph;  // stages per phase
+  const int rs = (sp * 128 + 8) * 2;                                  // bytes per staged row
+  const int NT = NI * NS;
+  const int sh0 = UP ? st.shift_gate : st.shift_down, sh1 = UP ? st.shift_up : st.shift_down;
+  const int R = UP ? I : H;  // rows of one expert's matrix
+  // this lane's weight rows of item it (and the item's first output), clamped to the matrix
+  auto item = [&](int it, size_t& r0, size_t& r1, int& first) {
+    if constexpr (UP) {
+      first = part * 256 + wave * 32;
+      const int o = min(first, I - 32) + n;
+      r0 = r1 = (size_t)ch.expert * I + o;
+    } else {
+      first = 64 * ((part * NI + it) * kSkWaves + wave);
+      const int hr = min(first, H - 64) + n;
+      r0 = (size_t)ch.expert * H + hr;
+      r1 = r0 + 32;
+    }
+  };
+  auto load = [&](SkStage<FMT>& r, int j) {
+    const int it = j / NS, js = j - it * NS;
+    size_t r0, r1;
+    int first;
+    item(it, r0, r1, first);
+    const size_t t0 = (r0 >> 2) * nkt + 2 * js + h, t1 = (r1 >> 2) * nkt + 2 * js + h;
+    sk_load<FMT>(r, codes0 + t0 * GB + (r0 & 3) * 2 * CB, codes1 + t1 * GB + (r1 & 3) * 2 * CB,
+                 scales0 + t0 * 8 + (r0 & 3) * 2, scales1 + t1 * 8 + (r1 & 3) * 2);
+  };
+  __syncthreads();  // row tables
+  sk_stage_rows(xs, src, K, row_src, nr, 0, min(K, sp * 128), rs);
+  SkStage<FMT> ring[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (i < NT) load(ring[i], i);
+  __syncthreads();  // staged rows
+  const Q2Sel ksel = q2_sel();
+  // rows past the chunk read row nr - 1 (their results are not stored)
+  const uint8_t* arow = xs + min(n, nr - 1) * rs + h * 128;
+  f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+  for (int j0 = 0; j0 < NT; j0 += P) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int j = j0 + i;
+      if (j < NT) {
+        const int it = j / NS, js = j - it * NS;
+        if (sp < NS && j > 0 && js % sp == 0) {  // next phase (uniform across the workgroup)
+          __syncthreads();
+          sk_stage_rows(xs, src, K, row_src, nr, js * 128, min(K - js * 128, sp * 128), rs);
+          __syncthreads();
+        }
+        sk_compute<FMT>(acc0, acc1, ring[i], arow + (js % sp) * 256, sh0, sh1, ksel);
+        if (j + P < NT) load(ring[i], j + P);
+        if (js == NS - 1) {  // the item's outputs
+          size_t r0, r1;
+          int first;
+          item(it, r0, r1, first);
+          if (first < R) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = acc_row(r, h);
+              if (m < nr) {
+                const int ex = row_ex[m];
+                if constexpr (UP) {
+                  const int o = first + n;
+                  out[(size_t)row_dst[m] * I + (o & ~7) + p8inv(o & 7)] = __builtin_bit_cast(
+                      uint16_t, silu_mul_scaled(acc0[r], acc1[r], (int)(int16_t)(ex & 0xFFFF), ex >> 16));
+                } else {
+                  uint16_t* d = out + (size_t)row_dst[m] * H + first + n;
+                  __builtin_nontemporal_store(f32_to_bf16(__builtin_ldexpf(acc0[r], ex)), d);
+                  __builtin_nontemporal_store(f32_to_bf16(__builtin_ldexpf(acc1[r], ex)), d + 32);
+                }
+              }
+            }
+          }
+          acc0 = f32x16_t{};
+          acc1 = f32x16_t{};
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -962,6 +1200,12 @@ static void allow_big_lds() {
       (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
     for (const void* k : small)
       (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLdsSmall);
+    const void* skinny[4] = {reinterpret_cast<const void*>(ffn_skinny_kernel<2, true, kSkDepth2>),
+                             reinterpret_cast<const void*>(ffn_skinny_kernel<3, true, kSkDepth3>),
+                             reinterpret_cast<const void*>(ffn_skinny_kernel<2, false, kSkDepth2>),
+                             reinterpret_cast<const void*>(ffn_skinny_kernel<3, false, kSkDepth3>)};
+    for (const void* k : skinny)
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkXBytes);
   });
 }
 
@@ -985,7 +1229,21 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const
 #define STRATA_LAUNCH_UP(F, NFM, LDSB, CH, NCH, G, GRID)                                          \
   ffn_up_kernel<F, NFM><<<GRID, kGemmThreads, LDSB, s>>>(x16, xinfo, sorted_slot, k, CH, NCH, gc, uc, \
                                                          gate_scales, up_scales, stats, H, I, G, a16)
-  if (max_small > 0) {  // the small part: one slice per unit
+  if (max_small > 0) {  // the small part's skinny chunks: 256 outputs per unit
+    const int upc = (I + 255) / 256;
+    const int grid = grid_for_units((int64_t)max_small * upc);
+    if (fmt == 2)
+      ffn_skinny_kernel<2, true, kSkDepth2><<<grid, kSkThreads, kSkXBytes, s>>>(
+          x16, xinfo, sorted_slot, k, chunks, n_chunks, gc, uc, gate_scales, up_scales, stats, H, I,
+          upc, 1, a16);
+    else
+      ffn_skinny_kernel<3, true, kSkDepth3><<<grid, kSkThreads, kSkXBytes, s>>>(
+          x16, xinfo, sorted_slot, k, chunks, n_chunks, gc, uc, gate_scales, up_scales, stats, H, I,
+          upc, 1, a16);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (max_small > 0) {  // the rest of the small part: one slice per unit
     const int grid = grid_for_units((int64_t)max_small * (I / 128));
     if (fmt == 2) STRATA_LAUNCH_UP(2, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
     else STRATA_LAUNCH_UP(3, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
@@ -1012,7 +1270,25 @@ hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
 #define STRATA_LAUNCH_DOWN(F, NFM, LDSB, CH, NCH, G, GRID)                                        \
   ffn_down_kernel<F, NFM><<<GRID, kGemmThreads, LDSB, s>>>(a16, xinfo, sorted_slot, k, CH, NCH, dc, \
                                                            down_scales, stats, H, I, G, expert_out)
-  if (max_small > 0) {  // the small part: two slices per unit (24 stages: K = I is short)
+  if (max_small > 0) {  // the small part's skinny chunks
+    // items of 64 rows of H; about 16 per wave (two units per chunk) while one phase holds a's
+    // rows (the items of a wave then share the staged rows), else one
+    const int items = H / 64;
+    const int NI = kSkinnyRows * (I + 8) * 2 <= kSkXBytes ? (items + 15) / 16 : 1;
+    const int upc = (items + kSkWaves * NI - 1) / (kSkWaves * NI);
+    const int grid = grid_for_units((int64_t)max_small * upc);
+    if (fmt == 2)
+      ffn_skinny_kernel<2, false, kSkDepth2><<<grid, kSkThreads, kSkXBytes, s>>>(
+          a16, xinfo, sorted_slot, k, chunks, n_chunks, dc, dc, down_scales, down_scales, stats, H,
+          I, upc, NI, expert_out);
+    else
+      ffn_skinny_kernel<3, false, kSkDepth3><<<grid, kSkThreads, kSkXBytes, s>>>(
+          a16, xinfo, sorted_slot, k, chunks, n_chunks, dc, dc, down_scales, down_scales, stats, H,
+          I, upc, NI, expert_out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (max_small > 0) {  // the rest of the small part: two slices per unit (24 stages: K = I is short)
     const int Gs = (H / 256) % 2 == 0 ? 2 : 1;
     const int grid = grid_for_units((int64_t)max_small * (H / 256 / Gs));
     if (fmt == 2) STRATA_LAUNCH_DOWN(2, 2, kGemmLdsSmall, chunks, n_chunks, Gs, grid);

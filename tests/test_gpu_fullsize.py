@@ -5,11 +5,15 @@
            slots; layer output rows on a seeded sample of tokens (the oracle computes those rows
            one by one; tokens are independent in the layer).
 * skewed:  T=2048, 3-bit, Zipf-biased routing: same checks.
+* mid-size chunks at the full dims (T = 256 and 1024, 2-bit; T = 512, 3-bit): about 5, 20 and 10
+           rows per expert, the skinny GEMMs with their activation rows staged in one or in
+           several phases of the reduction; same checks.
 * stack:   two layers of h <- h + MoE(RMSNorm(h)) at the prefill shape, each layer checked
            teacher-forced (the oracle gets the GPU's h and x of that layer).
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -99,9 +103,17 @@ def test_decode_full_size(T):
     assert err.max() <= TOL_REL_L2
 
 
-@pytest.mark.parametrize("name,n_rows", [("prefill", 256), ("skewed", 128)])
+MID_SHAPES = {
+    "mid256": replace(mi.PREFILL, name="mid256", T=256),
+    "mid1024": replace(mi.PREFILL, name="mid1024", T=1024),
+    "mid512_q3": replace(mi.PREFILL, name="mid512_q3", T=512, fmt=mi.Q3),
+}
+
+
+@pytest.mark.parametrize("name,n_rows", [("prefill", 256), ("skewed", 128), ("mid256", 64),
+                                         ("mid1024", 64), ("mid512_q3", 64)])
 def test_prefill_full_size(name, n_rows):
-    s = mi.SHAPES[name]
+    s = MID_SHAPES[name] if name in MID_SHAPES else mi.SHAPES[name]
     log(f"{name} full size: generating")
     L = Layer(s)
     y, ids, rw, extra = run_layer(L)
