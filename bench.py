@@ -418,7 +418,7 @@ def bench_sweep(args, stream, layers):
     out_d = {"decode_path": dec, "prefill_path": pre, "layer_call": lay,
              "crossover_T": min(faster) if faster else None,
              "note": "strata_moe_layer runs the decode path for T <= 8, and on slices of at most "
-                     "8 tokens for T <= 40; layer_call times that choice"}
+                     "8 tokens for T <= 32; layer_call times that choice"}
     log("sweep: decode path " + ", ".join(f"T={d['T']} {d['us']:.1f}us" for d in dec))
     log("sweep: prefill path " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in pre))
     log("sweep: layer call " + ", ".join(f"T={p['T']} {p['us']:.1f}us" for p in lay))

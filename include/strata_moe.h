@@ -267,7 +267,7 @@ size_t strata_moe_decode_static_max_bytes(void);
  * Port, 8x Faster Prefill: Strata Engine Benchmarked", Where Strata Is Fast); the steps and their
  * definitions are those of strata_moe_route, strata_moe_permute, strata_moe_expert_ffn and
  * strata_moe_combine.
- * T <= 8 runs strata_moe_decode's path when the shape is within its limits.  9 <= T <= 40 runs
+ * T <= 8 runs strata_moe_decode's path when the shape is within its limits.  9 <= T <= 32 runs
  * the same decode path on consecutive slices of at most 8 tokens (the layer's tokens are
  * independent; with few rows per expert, streaming each touched expert once per slice is faster
  * than the grouped GEMMs).  Otherwise route -> permute -> expert_ffn -> combine.
