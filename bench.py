@@ -497,6 +497,64 @@ def bench_prefill(args, stream, name):
     return res
 
 
+def bench_mid(args, stream):
+    """Mid-size chunks at the full dims (T = 256 and 1024, 2-bit; about 5 and 20 rows per expert,
+    all 512 experts touched): the layer call and the expert-FFN entry point, whose work is
+    streaming the touched experts' packed weights (HBM-bound; the skinny GEMMs)."""
+    import torch
+
+    import bit_expert_ffn_fp32_amd as sm
+    import moe_inputs as mi
+    from gpu_helpers import Layer
+
+    res = []
+    for name in ("mid256", "mid1024"):
+        s = mi.SHAPES[name]
+        L = Layer(s, seed=args.seed)
+        del L.w_np
+        ids_host = np.argsort(-L.l_np.astype(np.float64), axis=1, kind="stable")[:, :s.k]
+        touched = len(np.unique(ids_host))
+        ws = L.workspace()
+        y = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+        S = s.T * s.k
+
+        def step(i):
+            sm.strata_moe_layer(L.w, L.x, L.logits, s.k, y, workspace=ws, stream=stream)
+
+        preroll(step, stream, args.preroll_s)
+        steps = args.prefill_steps
+        ms = event_time_ms(step, steps, stream) / steps
+        ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+        rw = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+        counts = torch.empty(s.E, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(s.E + 1, dtype=torch.int32, device="cuda")
+        ss = torch.empty(S, dtype=torch.int32, device="cuda")
+        sp = torch.empty(S, dtype=torch.int32, device="cuda")
+        out = torch.empty((S, s.H), dtype=torch.int16, device="cuda")
+        sm.strata_moe_route(L.logits, s.k, ids, rw, stream=stream)
+        sm.strata_moe_permute(ids, s.E, counts, offsets, ss, sp, ws, stream=stream)
+
+        def ffn(i):
+            sm.strata_moe_expert_ffn(L.w, L.x, s.k, offsets, ss, out, ws, stream=stream)
+
+        preroll(ffn, stream, args.preroll_s)
+        ms_ffn = event_time_ms(ffn, steps, stream) / steps
+        gbs = touched * s.expert_bytes / (ms_ffn * 1e-3) / 1e9
+        res.append({"workload": f"{s.name} T={s.T} H={s.H} E={s.E} k={s.k} I={s.I} Q2-block experts",
+                    "T": s.T, "touched_experts": touched, "ms_per_step": ms,
+                    "value": s.T / (ms * 1e-3), "unit": "layer-tokens/s",
+                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                 "kernel": "strata_moe_expert_ffn (x to fp16, skinny gate/up and down GEMMs)",
+                                 "ms_per_call": ms_ffn,
+                                 "unit_of_work": "touched experts' packed bytes per call"}})
+        log(f"{name}: layer {ms * 1e3:.1f} us, expert FFN {ms_ffn * 1e3:.1f} us = {gbs:.0f} GB/s "
+            f"of the {touched} touched experts ({gbs / HBM_PEAK_GBS * 100:.1f}% of HBM peak)")
+        del L, ws, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_stack(args, stream):
     """48-layer expert stack, all experts resident: h <- h + MoE(RMSNorm(h)) per layer with fresh
     seeded logits, one T=4 decode step and one T=8192 prefill chunk through all layers."""
@@ -658,6 +716,8 @@ def main():
     p.add_argument("--stack-layers", type=int, default=48)
     p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-mid", action="store_true",
+                   help="skip the mid-size chunks (T = 256 and 1024)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-sweep", action="store_true",
@@ -729,6 +789,13 @@ def main():
             log(f"skewed: {skw['ms_per_step']:.3f} ms/layer, {skw['touched_experts']} experts touched, "
                 f"expert FFN {skw['roofline']['achieved']:.0f} TFLOP/s")
             torch.cuda.empty_cache()
+    mid = None
+    if not args.no_mid:
+        for L in layers:
+            if hasattr(L, "w"):
+                del L.w
+        torch.cuda.empty_cache()
+        mid = bench_mid(args, stream)
     stack = None
     if not args.no_stack:
         stack = bench_stack(args, stream)
@@ -770,6 +837,8 @@ def main():
         line["prefill"] = pre
     if skw is not None:
         line["skewed"] = skw
+    if mid is not None:
+        line["mid"] = mid
     if stack is not None:
         line["stack"] = stack
     print(json.dumps(line), flush=True)

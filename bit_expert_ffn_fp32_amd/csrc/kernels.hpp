@@ -22,6 +22,11 @@ constexpr int kChunkRows = 224;      // rows of one GEMM work unit (at most 7 fr
 constexpr int kChunkRowsSmall = 64;  // the same for the small-fragment GEMMs (at most 2)
 constexpr int kPermTile = 1024;      // slots per permute tile
 constexpr int kSkinnyRows = 32;      // rows of a chunk the skinny GEMMs take (one fragment)
+// When at most this many experts of the small part have more than kSkinnyRows rows, each of them
+// becomes two skinny chunks (its weights are streamed twice) instead of a small-fragment chunk: a
+// small-fragment launch of a few units runs alone after the skinny one (at T = 1024, about 3 such
+// experts cost 36 + 23 us), while streaming their weights once more costs well under 1 us each.
+constexpr int kSkinnySplitMax = 64;
 
 // The grouped GEMMs' chunk list has two parts.  An expert with at most small_rows rows gets one
 // chunk in the small part, run by the small-fragment GEMMs (two workgroups per CU, so that one's
@@ -38,7 +43,9 @@ inline int small_chunk_rows(int64_t S, int64_t E) { return S <= 128 * E ? kChunk
 // Experts the small part needs: units (one per 128 gate/up outputs) for two workgroups per CU.
 inline int min_small_experts(int I) { return (2 * 256 + I / 128 - 1) / (I / 128); }
 inline int64_t max_small_chunks(int64_t S, int64_t E, int small_rows) {
-  return small_rows ? (E < S ? E : S) : 0;
+  if (!small_rows) return 0;
+  const int64_t split = S / (kSkinnyRows + 1) < kSkinnySplitMax ? S / (kSkinnyRows + 1) : kSkinnySplitMax;
+  return (E < S ? E : S) + split;  // one chunk per expert, plus the second halves of split ones
 }
 inline int64_t max_large_chunks(int64_t S, int64_t E, int small_rows, int min_small) {
   // experts in the large part: those with more than small_rows rows, plus (when the small part
@@ -86,8 +93,9 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 // Where the chunk list goes and how it is split (small_chunk_rows, min_small_experts,
 // max_small_chunks): the small part at chunks[0 ..) with its count in n_chunks[0], the large part
 // at chunks[max_small ..) with its count in n_chunks[1].  The small part lists its chunks of at
-// most kSkinnyRows rows first (their count in n_chunks[2]); those run on the skinny GEMMs, the
-// rest of the small part on the small-fragment GEMMs.
+// most kSkinnyRows rows first (their count in n_chunks[2]; an expert split under kSkinnySplitMax
+// gives two consecutive ones); those run on the skinny GEMMs, the rest of the small part on the
+// small-fragment GEMMs.
 struct ChunkList {
   Chunk* chunks;
   int* n_chunks;

@@ -67,20 +67,28 @@ __device__ int block_exclusive_scan(int v, int* lds16, int& total) {
 // The two-part GEMM chunk list (see ChunkList), built by a whole 1024-thread workgroup; a thread
 // with mine holds expert e, its rows at sorted positions [off, off + cnt).  The small part is used
 // only when at least cl.min_small experts qualify for it; within it the chunks of at most
-// kSkinnyRows rows come first, each group in expert order.
+// kSkinnyRows rows come first (with the experts of up to 2 kSkinnyRows rows split in two when at
+// most kSkinnySplitMax of them exist), each group in expert order.
 __device__ void build_chunk_list(bool mine, int e, int off, int cnt, const ChunkList& cl, int* lds16) {
   int nsmall;
   (void)block_exclusive_scan(mine ? small_chunks_of(cnt, cl.small_rows) : 0, lds16, nsmall);
   const int sr = nsmall >= cl.min_small ? cl.small_rows : 0;
   const int small = mine ? small_chunks_of(cnt, sr) : 0;
-  const bool skinny = small && cnt <= kSkinnyRows;
+  int nwide;  // small-part experts of more than kSkinnyRows rows
+  (void)block_exclusive_scan(small && cnt > kSkinnyRows ? 1 : 0, lds16, nwide);
+  // skinny chunks of this expert: one, two halves of a split one, or none
+  const int nsk = !small ? 0 : cnt <= kSkinnyRows ? 1 : nwide <= kSkinnySplitMax ? 2 : 0;
   int nskinny, nrest, ltotal;
-  const int kb = block_exclusive_scan(skinny ? 1 : 0, lds16, nskinny);
-  const int rb = block_exclusive_scan(skinny ? 0 : small, lds16, nrest);
+  const int kb = block_exclusive_scan(nsk, lds16, nskinny);
+  const int rb = block_exclusive_scan(small && !nsk ? 1 : 0, lds16, nrest);
   const int lb = block_exclusive_scan(mine ? large_chunks_of(cnt, sr) : 0, lds16, ltotal);
-  if (mine)
-    write_expert_chunks(e, off, cnt, sr, cl.chunks, skinny ? kb : nskinny + rb,
+  if (nsk == 2) {
+    cl.chunks[kb] = Chunk{e, off, kSkinnyRows, 0};
+    cl.chunks[kb + 1] = Chunk{e, off + kSkinnyRows, cnt - kSkinnyRows, 0};
+  } else if (mine) {
+    write_expert_chunks(e, off, cnt, sr, cl.chunks, nsk ? kb : nskinny + rb,
                         cl.chunks + cl.max_small, lb);
+  }
   if (threadIdx.x == 0) {
     cl.n_chunks[0] = nskinny + nrest;
     cl.n_chunks[1] = ltotal;

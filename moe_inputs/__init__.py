@@ -188,8 +188,12 @@ STACK_DECODE = replace(DECODE, name="stack_decode", layers=48)
 # the pruned coder variant keeps 256 of a layer's 512 experts
 PRUNED_DECODE = replace(DECODE, name="pruned_decode", E=256)
 PRUNED_PREFILL = replace(PREFILL, name="pruned_prefill", E=256)
+# mid-size chunks at the full dims (prompt-lookup verify, short prefill chunks): ~5 and ~20 rows
+# per expert
+MID256 = replace(PREFILL, name="mid256", T=256)
+MID1024 = replace(PREFILL, name="mid1024", T=1024)
 SHAPES = {s.name: s for s in (TINY, DECODE, PREFILL, SKEWED, STACK_PREFILL, STACK_DECODE,
-                              PRUNED_DECODE, PRUNED_PREFILL)}
+                              PRUNED_DECODE, PRUNED_PREFILL, MID256, MID1024)}
 
 
 def zipf_bias(seed: int, layer: int, E: int, s: float = 1.1, strength: float = 2.0) -> np.ndarray:

@@ -103,11 +103,7 @@ def test_decode_full_size(T):
     assert err.max() <= TOL_REL_L2
 
 
-MID_SHAPES = {
-    "mid256": replace(mi.PREFILL, name="mid256", T=256),
-    "mid1024": replace(mi.PREFILL, name="mid1024", T=1024),
-    "mid512_q3": replace(mi.PREFILL, name="mid512_q3", T=512, fmt=mi.Q3),
-}
+MID_SHAPES = {"mid512_q3": replace(mi.PREFILL, name="mid512_q3", T=512, fmt=mi.Q3)}
 
 
 @pytest.mark.parametrize("name,n_rows", [("prefill", 256), ("skewed", 128), ("mid256", 64),

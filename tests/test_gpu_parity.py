@@ -230,14 +230,16 @@ def test_layer_against_oracle(s):
     np.testing.assert_allclose(ya, y0 + y, rtol=1e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("n_small", [70, 60], ids=["split", "fallback"])
+@pytest.mark.parametrize("n_small", [70, 161, 60], ids=["split", "small", "fallback"])
 def test_chunk_list_boundaries(n_small):
-    """Routing crafted so that experts hold exactly 1, 31, 32, 33, 63 and 64 rows (one chunk each in
-    the small-fragment part of the GEMM chunk list) and 65, 96, 97, 224, 225, 300 and 449 rows (the
-    large part: 224 is one 7-fragment chunk, 225 two, 449 three), plus untouched experts.  With
-    I = 1024 the small part needs 64 such experts: 70 use it, 60 fall back to the large part for
-    every expert.  Rows at both ends of every expert's segment and at its fragment boundaries,
-    plus random rows, against the oracle."""
+    """Routing crafted so that experts hold exactly 1, 2, 31, 32, 33, 63 and 64 rows (the small part
+    of the GEMM chunk list) and 65, 96, 97, 224, 225, 300 and 449 rows (the large part: 224 is one
+    7-fragment chunk, 225 two, 449 three), plus untouched experts.  With I = 1024 the small part
+    needs 64 such experts: 70 use it, with the 30 experts of 33-64 rows split into two skinny
+    chunks each (all 70 on the skinny GEMMs); 161 use it with 69 such experts, more than are split,
+    so those run on the small-fragment GEMMs; 60 fall back to the large part for every expert.
+    Rows at both ends of every expert's segment and at its fragment boundaries, plus random rows,
+    against the oracle."""
     small = [1, 2, 31, 32, 33, 63, 64]
     large = [65, 96, 97, 224, 225, 300, 449]
     counts = [small[i % len(small)] for i in range(n_small)] + large + [0] * 4
