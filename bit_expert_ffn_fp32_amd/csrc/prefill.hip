@@ -793,7 +793,10 @@ __global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_down_ker
 
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * 64;
-constexpr int kSkXBytes = 32 * (1024 + 8) * 2;  // staged rows: 32 rows of 1024 indices, padded
+// Dynamic LDS of a workgroup: the staged rows and, beside them, the output staging of 8 waves x 32
+// rows x 80 bytes (two workgroups per CU with the 384 bytes of row tables).
+constexpr int kSkLds = 81408;
+constexpr int kSkOutRow = 80;  // bytes per row of a wave's output staging: 32 values + 16 pad
 constexpr int kSkDepth2 = 3;                    // stages of weights in flight per wave: 2-bit
 constexpr int kSkDepth3 = 2;                    // 3-bit (larger stages, more registers each)
 
@@ -927,9 +930,12 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
     row_ex[tid] = row_exponent<UP>(xinfo[tok], st);
   }
   // phases: the longest run of whole stages whose nr rows fit, spread evenly over the phases
-  const int kfit = (kSkXBytes / (2 * nr) - 8) & ~127;
+  const int kfit = (kSkLds / (2 * nr) - 8) & ~127;
   const int nph = (K + kfit - 1) / kfit, sp = (NS + nph - 1) / nph;  // stages per phase
   const int rs = (sp * 128 + 8) * 2;                                  // bytes per staged row
+  // output staging beside the staged rows when the items share them (NI > 1: one phase, and the
+  // launch checks that 32 rows and the 8 regions fit)
+  uint8_t* const ep_tail = xs + ((nr * rs + 15) & ~15);
   const int NT = NI * NS;
   const int sh0 = UP ? st.shift_gate : st.shift_down, sh1 = UP ? st.shift_up : st.shift_down;
   const int R = UP ? I : H;  // rows of one expert's matrix
@@ -1001,22 +1007,52 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
     ++jp;
     if (++js == NS) {  // the item's outputs
       const int first = item_first(it);
+      // Through this wave's LDS region, so that every store is a 16-byte piece (2-byte stores
+      // from 32 lanes cost a write request each).  Items that share the staged rows (NI > 1)
+      // use the space beside them; a single item's region overlays the rows once every wave is
+      // done with them.
+      uint8_t* reg;
+      if (NI > 1) {
+        reg = ep_tail + wave * nr * kSkOutRow;
+      } else {
+        __syncthreads();
+        reg = xs + wave * nr * kSkOutRow;
+      }
       if (first < R) {
+        // register q of this lane holds row 8 (q >> 2) + 4 h + (q & 3): one base per lane and
+        // constant offsets (the base is opaque so that nothing of it is held across the loop)
+        int lim = nr - 4 * h;  // rows 4 h + d exist for d < lim
+        uint32_t lo = (uint32_t)(4 * h * kSkOutRow) + 2u * (UP ? (n & ~7) + p8inv(n & 7) : n);
+        asm volatile("" : "+v"(lo), "+v"(lim));
+        uint8_t* const lb = reg + lo;
+        const int* const exr = row_ex + 4 * h;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = acc_row(q, h);
-          if (m < nr) {
-            const int ex = row_ex[m];
-            if constexpr (UP) {
-              const int o = first + n;
-              out[(size_t)row_dst[m] * I + (o & ~7) + p8inv(o & 7)] = __builtin_bit_cast(
-                  uint16_t, silu_mul_scaled(acc0[q], acc1[q], (int)(int16_t)(ex & 0xFFFF), ex >> 16));
-            } else {
-              uint16_t* d = out + (size_t)row_dst[m] * H + first + n;
-              __builtin_nontemporal_store(f32_to_bf16(__builtin_ldexpf(acc0[q], ex)), d);
-              __builtin_nontemporal_store(f32_to_bf16(__builtin_ldexpf(acc1[q], ex)), d + 32);
+        for (int pass = 0; pass < (UP ? 1 : 2); ++pass) {  // down: the two 32-row halves
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int d = 8 * (q >> 2) + (q & 3);
+            if (d < lim) {
+              const int ex = exr[d];
+              uint16_t v;
+              if constexpr (UP)
+                v = __builtin_bit_cast(uint16_t, silu_mul_scaled(acc0[q], acc1[q], (int)(int16_t)(ex & 0xFFFF), ex >> 16));
+              else
+                v = f32_to_bf16(__builtin_ldexpf(pass ? acc1[q] : acc0[q], ex));
+              *reinterpret_cast<uint16_t*>(lb + d * kSkOutRow) = v;
             }
           }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's values are in place
+          for (int pc = lane; pc < 4 * nr; pc += 64) {  // 4 pieces of 8 values per row
+            const int m = pc >> 2, c = pc & 3;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reg + m * kSkOutRow + c * 16);
+            if constexpr (UP) {
+              *reinterpret_cast<u32x4_t*>(out + (size_t)row_dst[m] * I + first + 8 * c) = v;
+            } else {  // expert outputs: read once, by the combine
+              __builtin_nontemporal_store(
+                  v, reinterpret_cast<u32x4_t*>(out + (size_t)row_dst[m] * H + first + 32 * pass + 8 * c));
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next pass writes
         }
       }
       acc0 = f32x16_t{};
@@ -1234,7 +1270,7 @@ static void allow_big_lds() {
                              reinterpret_cast<const void*>(ffn_skinny_kernel<2, false, kSkDepth2>),
                              reinterpret_cast<const void*>(ffn_skinny_kernel<3, false, kSkDepth3>)};
     for (const void* k : skinny)
-      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkXBytes);
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkLds);
   });
 }
 
@@ -1262,11 +1298,11 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const
     const int upc = (I + 255) / 256;
     const int grid = grid_for_units((int64_t)max_small * upc);
     if (fmt == 2)
-      ffn_skinny_kernel<2, true, kSkDepth2><<<grid, kSkThreads, kSkXBytes, s>>>(
+      ffn_skinny_kernel<2, true, kSkDepth2><<<grid, kSkThreads, kSkLds, s>>>(
           x16, xinfo, sorted_slot, k, chunks, n_chunks, gc, uc, gate_scales, up_scales, stats, H, I,
           upc, 1, a16);
     else
-      ffn_skinny_kernel<3, true, kSkDepth3><<<grid, kSkThreads, kSkXBytes, s>>>(
+      ffn_skinny_kernel<3, true, kSkDepth3><<<grid, kSkThreads, kSkLds, s>>>(
           x16, xinfo, sorted_slot, k, chunks, n_chunks, gc, uc, gate_scales, up_scales, stats, H, I,
           upc, 1, a16);
     const hipError_t e = hipGetLastError();
@@ -1303,17 +1339,19 @@ hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
                                                            down_scales, stats, H, I, G, expert_out)
   if (max_small > 0) {  // the small part's skinny chunks
     // items of 64 rows of H; about 16 per wave (two units per chunk) while one phase holds a's
-    // rows (the items of a wave then share the staged rows), else one
+    // rows and the output staging beside them (the items of a wave then share the staged rows),
+    // else one
     const int items = H / 64;
-    const int NI = kSkinnyRows * (I + 8) * 2 <= kSkXBytes ? (items + 15) / 16 : 1;
+    const bool share = kSkinnyRows * (I + 8) * 2 + 16 + kSkWaves * kSkinnyRows * kSkOutRow <= kSkLds;
+    const int NI = share ? (items + 15) / 16 : 1;
     const int upc = (items + kSkWaves * NI - 1) / (kSkWaves * NI);
     const int grid = grid_for_units((int64_t)max_small * upc);
     if (fmt == 2)
-      ffn_skinny_kernel<2, false, kSkDepth2><<<grid, kSkThreads, kSkXBytes, s>>>(
+      ffn_skinny_kernel<2, false, kSkDepth2><<<grid, kSkThreads, kSkLds, s>>>(
           a16, xinfo, sorted_slot, k, chunks, n_chunks, dc, dc, down_scales, down_scales, stats, H,
           I, upc, NI, expert_out);
     else
-      ffn_skinny_kernel<3, false, kSkDepth3><<<grid, kSkThreads, kSkXBytes, s>>>(
+      ffn_skinny_kernel<3, false, kSkDepth3><<<grid, kSkThreads, kSkLds, s>>>(
           a16, xinfo, sorted_slot, k, chunks, n_chunks, dc, dc, down_scales, down_scales, stats, H,
           I, upc, NI, expert_out);
     const hipError_t e = hipGetLastError();

@@ -154,6 +154,10 @@ SMALL_SHAPES = [
     # up to 24 rows per expert on average: the small-fragment GEMMs, chunks of at most 64 rows
     shape("small_split", T=96, H=256, E=8, k=2, I=128),     # ~24 rows per expert, some split
     shape("hot_q3", T=300, H=256, E=4, k=2, I=128, fmt=3),  # large-chunk GEMMs, 3-bit
+    # ~20 rows per expert on the skinny GEMMs with I = 2048: the down projection's a rows exceed
+    # the LDS, so it reduces in phases with one 64-row item a wave
+    shape("skinny_phases", T=800, H=256, E=40, k=1, I=2048),
+    shape("skinny_phases_q3", T=800, H=256, E=40, k=1, I=2048, fmt=3),
 ]
 
 
