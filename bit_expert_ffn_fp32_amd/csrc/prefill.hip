@@ -994,8 +994,8 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
   f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
   int it = 0, js = 0, jp = 0;  // compute cursor: item, stage, stage within the staged phase
   // one stage from ring slot r: the next phase first if due, the item's outputs after its last
-  // stage; LOAD: refill the slot
-  auto stage = [&](SkStage<FMT>& r, bool load) {
+  // stage
+  auto stage = [&](SkStage<FMT>& r) {
     if (jp == sp) {  // the next phase (uniform across the workgroup)
       jp = 0;
       __syncthreads();
@@ -1003,7 +1003,6 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
       __syncthreads();
     }
     sk_compute<FMT>(acc0, acc1, r, arow + jp * 256, sh0, sh1, ksel);
-    if (load) load_next(r);
     ++jp;
     if (++js == NS) {  // the item's outputs
       const int first = item_first(it);
@@ -1062,14 +1061,16 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
       jp = sp < NS ? sp : 0;  // several phases: the next item restages the first
     }
   };
-  int j = 0;
-  for (; j + P <= NT; j += P) {  // whole groups of P stages
+  // whole groups of P stages, the last one computing only the stages that exist; every slot is
+  // refilled (past the end from the activation line), so that no path holds fewer loads in flight
+  // and no separate tail keeps values alive across the loop
+  for (int j0 = 0; j0 < NT; j0 += P) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) stage(ring[i], true);
+    for (int i = 0; i < P; ++i) {
+      if (j0 + i < NT) stage(ring[i]);
+      load_next(ring[i]);
+    }
   }
-#pragma unroll
-  for (int i = 0; i < P; ++i)  // the last NT % P stages
-    if (j + i < NT) stage(ring[i], false);
 }
 
 // ---------------------------------------------------------------------------------------------
