@@ -923,12 +923,6 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
   const int K = UP ? H : I, nkt = K / 64, NS = K / 128, nr = ch.nrows;
   const strata_moe_expert_stats st = stats[ch.expert];
-  if (tid < nr) {
-    const int slot = sorted_slot[ch.row_start + tid], tok = slot / k;
-    row_src[tid] = UP ? tok : ch.row_start + tid;
-    row_dst[tid] = UP ? ch.row_start + tid : slot;
-    row_ex[tid] = row_exponent<UP>(xinfo[tok], st);
-  }
   // phases: the longest run of whole stages whose nr rows fit, spread evenly over the phases
   const int kfit = (kSkLds / (2 * nr) - 8) & ~127;
   const int nph = (K + kfit - 1) / kfit, sp = (NS + nph - 1) / nph;  // stages per phase
@@ -982,11 +976,18 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
       if (++lit < NI) lane_offsets(lit, oc0, oc1, os0, os1);
     }
   };
-  __syncthreads();  // row tables
-  sk_stage_rows(xs, src, K, row_src, nr, 0, min(K, sp * 128), rs);
+  // the first stages' weights first, so that their latency overlaps the row tables' dependent loads
   SkStage<FMT> ring[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) load_next(ring[i]);
+  if (tid < nr) {
+    const int slot = sorted_slot[ch.row_start + tid], tok = slot / k;
+    row_src[tid] = UP ? tok : ch.row_start + tid;
+    row_dst[tid] = UP ? ch.row_start + tid : slot;
+    row_ex[tid] = row_exponent<UP>(xinfo[tok], st);
+  }
+  __syncthreads();  // row tables
+  sk_stage_rows(xs, src, K, row_src, nr, 0, min(K, sp * 128), rs);
   __syncthreads();  // staged rows
   const Q2Sel ksel = q2_sel();
   // rows past the chunk read row nr - 1 (their results are not stored)
