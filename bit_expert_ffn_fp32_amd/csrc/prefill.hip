@@ -779,9 +779,10 @@ __global__ __launch_bounds__(kGemmThreads, NFMAX <= 2 ? 2 : 1) void ffn_down_ker
 // With one fragment of rows every weight byte feeds one 32 x 32 tile of matrix work, so these
 // units are bound by how fast they stream the expert's weights, not by the matrix cores.  Instead
 // of the LDS stage ring of the kernels above (whose per-stage copies and barriers cap a thin
-// unit's stream), each wave loads its own weights straight into registers, kSkDepth stages ahead
-// of its matrix ops, with two 8-wave workgroups (16 waves) per CU; the chunk's activation rows
-// are staged once in LDS, in phases of the reduction where all of them do not fit.
+// unit's stream), each wave loads its own weights straight into registers, a ring of kSkDepth2
+// (2-bit) or kSkDepth3 (3-bit) stages ahead of its matrix ops, with two 8-wave workgroups (16
+// waves) per CU; the chunk's activation rows are staged once in LDS, in phases of the reduction
+// where all of them do not fit.
 //
 // Operand layout.  A stage is 128 reduction indices, two 64-index tiles of the tiled layout.
 // Lane (n, h) (n = lane % 32, h = lane / 32) loads weight row n's codes of tile 2j + h (both its
@@ -797,8 +798,8 @@ constexpr int kSkThreads = kSkWaves * 64;
 // rows x 80 bytes (two workgroups per CU with the 384 bytes of row tables).
 constexpr int kSkLds = 81408;
 constexpr int kSkOutRow = 80;  // bytes per row of a wave's output staging: 32 values + 16 pad
-constexpr int kSkDepth2 = 3;                    // stages of weights in flight per wave: 2-bit
-constexpr int kSkDepth3 = 2;                    // 3-bit (larger stages, more registers each)
+constexpr int kSkDepth2 = 3;   // stages of weights in flight per wave: 2-bit
+constexpr int kSkDepth3 = 2;   // 3-bit (larger stages, more registers each)
 
 template <int FMT>
 struct SkStage {
