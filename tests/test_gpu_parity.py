@@ -158,6 +158,9 @@ SMALL_SHAPES = [
     # the LDS, so it reduces in phases with one 64-row item a wave
     shape("skinny_phases", T=800, H=256, E=40, k=1, I=2048),
     shape("skinny_phases_q3", T=800, H=256, E=40, k=1, I=2048, fmt=3),
+    # skinny GEMMs with I = 384 and H = 256: the second gate/up unit of a chunk and half the waves
+    # of the down units hold items past the matrix (computed, not stored)
+    shape("skinny_i384", T=900, H=256, E=200, k=2, I=384),
 ]
 
 
