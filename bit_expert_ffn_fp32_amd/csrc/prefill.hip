@@ -44,11 +44,11 @@ constexpr int kWScaleBytes = 256 * 2 * 2;         // 256 weight rows x 2 fp16 sc
 constexpr int kGemmLds = 160 * 1024;              // the whole LDS of a CU
 constexpr int kGemmLdsSmall = 80 * 1024;          // half of it: two small-fragment workgroups per CU
 constexpr int kRowsBytes = 2 * kChunkRows * 4;    // a unit's source and destination rows
-// Output staging: two 32-row buffers (one fragment each) with padded rows.
-constexpr int kUpOutRow = 128 + 8;                // halfs per row: 128 outputs
-constexpr int kDownOutRow = 256 + 8;              // halfs per row: 256 outputs
-constexpr int kUpEpiBytes = 2 * 32 * kUpOutRow * 2;
-constexpr int kDownEpiBytes = 2 * 32 * kDownOutRow * 2;
+// Output staging: a 32-row region per wave (one fragment at a time) with padded rows.
+constexpr int kUpOutRow = 32 + 8;                 // halfs per row: a wave's 32 outputs
+constexpr int kDownOutRow = 64 + 8;               // halfs per row: a wave's 64 outputs
+constexpr int kUpEpiBytes = 4 * 32 * kUpOutRow * 2;
+constexpr int kDownEpiBytes = 4 * 32 * kDownOutRow * 2;
 
 // Byte layout of one stage buffer of a unit with NF fragments.
 template <int FMT, int NF>
@@ -377,19 +377,29 @@ STRATA_DEVICE int row_exponent(const XInfo& xi, const strata_moe_expert_stats& s
   else return -(es + 2 * xi.sx + st.shift_gate + st.shift_up + st.shift_down);
 }
 
-// Writes one slice's outputs, fragment by fragment, through two LDS staging buffers, with 16-byte
-// stores.  Up: out = A (fp16, [rows][I], columns in P8 order within groups of 8), 128 outputs per
-// slice, lane c < 16 of a tile holding the gate and lane c + 16 the up value of output 16 w + c ...
-// (acc0 = gate, acc1 = up columns); down: out = expert outputs (bf16, [slots][H]), 256 per slice.
-// dst_lds[r]: the destination row of unit row r (rows past the chunk repeat row 0, whose values
-// they equal, so every lane stores); exps[r]: its exponents (row_exponent).  Each wave issues
-// kStores stores per fragment.
+// Two fp32 values as a bf16 pair (low half a), each rounded to nearest even: one packed hardware
+// conversion (the same rounding as f32_to_bf16 for finite values).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+STRATA_DEVICE uint32_t bf16_pair_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// Writes one slice's outputs, fragment by fragment, with 16-byte stores through a private LDS region
+// of each wave (the columns a wave computes are the columns it stores, so no wave waits for the
+// others; a staging buffer shared by the four waves needed a workgroup barrier per fragment).  Up: out = A (fp16, [rows][I],
+// columns in P8 order within groups of 8), 128 outputs per slice, wave w holding outputs
+// 32 w + n (acc0 = gate, acc1 = up); down: out = expert outputs (bf16, [slots][H]), 256 per
+// slice, wave w holding columns 64 w + n (acc0) and 64 w + 32 + n (acc1).  dst_lds[r]: the
+// destination row of unit row r (rows past the chunk repeat row 0, whose values they equal, so
+// every lane stores); exps[r]: its exponents (row_exponent).  Each wave issues kStores stores per
+// fragment.
 template <int NF, bool UP>
 struct Epilogue {
-  static constexpr int kRow = UP ? kUpOutRow : kDownOutRow;        // halfs per staged row
-  static constexpr int kPieces = UP ? 16 : 32;                     // 16-byte pieces per row
-  static constexpr int kStores = 32 * kPieces / kGemmThreads;      // per thread per fragment
-  static constexpr int kBuf = 32 * kRow;                           // halfs per staging buffer
+  static constexpr int kCols = UP ? 32 : 64;                        // a wave's columns
+  static constexpr int kRow = kCols + 8;                            // halfs per staged row
+  static constexpr int kPieces = kCols / 8;                         // 16-byte pieces per row
+  static constexpr int kStores = 32 * kPieces / kWave;              // per lane per fragment
+  static constexpr int kRegion = 32 * kRow;                         // halfs per wave
 };
 
 template <int NF, bool UP>
@@ -399,20 +409,21 @@ STRATA_DEVICE void write_slice(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], uint1
   using EP = Epilogue<NF, UP>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 31, hh = lane >> 5;
+  uint16_t* const wr = epi + wave * EP::kRegion;  // this wave's region
   // this lane's first staged element (tile row 4 hh, its column); register r of a tile adds
   // rows 8 (r >> 2) + (r & 3), a constant offset
-  const int lcol = UP ? wave * 32 + (nl & ~7) + p8inv(nl & 7) : wave * 64 + nl;
-  uint16_t* const e0 = epi + 4 * hh * EP::kRow + lcol;
+  const int lcol = UP ? (nl & ~7) + p8inv(nl & 7) : nl;
+  uint16_t* const e0 = wr + 4 * hh * EP::kRow + lcol;
   // (opaque to the optimizer, so that the store addresses are not computed once for every slice
   // and held in registers across the main loop)
   asm volatile("" : "+s"(out_ld));
+  const int cw = col0 + wave * EP::kCols;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     // One fragment at a time: the empty asm re-defines this fragment's sums in the accumulation
     // registers here, so their copies into VGPRs cannot be hoisted above it (all fragments'
     // copies at once would need 32 NF VGPRs).
     asm volatile("" : "+a"(acc0[f]), "+a"(acc1[f]));
-    uint16_t* eb = e0 + (f & 1) * EP::kBuf;
     // exponents of this lane's rows f*32 + 8 q + 4 hh + (0..3), q = r >> 2
     int ex[16];
 #pragma unroll
@@ -421,34 +432,34 @@ STRATA_DEVICE void write_slice(f32x16_t (&acc0)[NF], f32x16_t (&acc1)[NF], uint1
       ex[4 * q] = v.x; ex[4 * q + 1] = v.y; ex[4 * q + 2] = v.z; ex[4 * q + 3] = v.w;
     }
     if constexpr (UP) {
-      // acc0 columns: gate of outputs w*32 + n; acc1: up of the same outputs
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ecg = (int)(int16_t)(ex[r] & 0xFFFF), es = ex[r] >> 16;
-        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] =
+        e0[(8 * (r >> 2) + (r & 3)) * EP::kRow] =
             __builtin_bit_cast(uint16_t, silu_mul_scaled(acc0[f][r], acc1[f][r], ecg, es));
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow] = f32_to_bf16(__builtin_ldexpf(acc0[f][r], ex[r]));
-        eb[(8 * (r >> 2) + (r & 3)) * EP::kRow + 32] = f32_to_bf16(__builtin_ldexpf(acc1[f][r], ex[r]));
+        const uint32_t b = bf16_pair_rne(__builtin_ldexpf(acc0[f][r], ex[r]), __builtin_ldexpf(acc1[f][r], ex[r]));
+        e0[(8 * (r >> 2) + (r & 3)) * EP::kRow] = (uint16_t)b;
+        e0[(8 * (r >> 2) + (r & 3)) * EP::kRow + 32] = (uint16_t)(b >> 16);
       }
     }
-    // the buffer is complete for every wave; (the other buffer's previous reads finished before
-    // each wave's own barrier here, so the next fragment may overwrite it)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    const uint16_t* rb = epi + (f & 1) * EP::kBuf;
+    // the wave's values are in place (a wave's LDS operations complete in order; the clobber keeps
+    // the compiler from moving the reads above the writes)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < EP::kStores; ++i) {
-      const int p = threadIdx.x + i * kGemmThreads;
+      const int p = lane + i * kWave;
       const int r = p / EP::kPieces, c = p % EP::kPieces;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rb + r * EP::kRow + c * 8);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)dst_lds[f * 32 + r] * out_ld + col0 + c * 8);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wr + r * EP::kRow + c * 8);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)dst_lds[f * 32 + r] * out_ld + cw + c * 8);
       if constexpr (UP) *dst = v;                         // a: read again by the down GEMM
       else __builtin_nontemporal_store(v, dst);           // expert outputs: read once, by the combine
     }
+    // (the next fragment's writes come after these reads)
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -1030,17 +1041,21 @@ __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4
 #pragma unroll
         for (int pass = 0; pass < (UP ? 1 : 2); ++pass) {  // down: the two 32-row halves
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
+          for (int q = 0; q < 16; q += 2) {  // rows d and d + 1 (q and q + 1 share q >> 2)
             const int d = 8 * (q >> 2) + (q & 3);
-            if (d < lim) {
-              const int ex = exr[d];
-              uint16_t v;
-              if constexpr (UP)
-                v = __builtin_bit_cast(uint16_t, silu_mul_scaled(acc0[q], acc1[q], (int)(int16_t)(ex & 0xFFFF), ex >> 16));
-              else
-                v = f32_to_bf16(__builtin_ldexpf(pass ? acc1[q] : acc0[q], ex));
-              *reinterpret_cast<uint16_t*>(lb + d * kSkOutRow) = v;
+            uint16_t v0, v1;
+            if constexpr (UP) {
+              const int e0 = exr[d], e1 = exr[d + 1];
+              v0 = __builtin_bit_cast(uint16_t, silu_mul_scaled(acc0[q], acc1[q], (int)(int16_t)(e0 & 0xFFFF), e0 >> 16));
+              v1 = __builtin_bit_cast(uint16_t, silu_mul_scaled(acc0[q + 1], acc1[q + 1], (int)(int16_t)(e1 & 0xFFFF), e1 >> 16));
+            } else {
+              const uint32_t b = bf16_pair_rne(__builtin_ldexpf(pass ? acc1[q] : acc0[q], exr[d]),
+                                               __builtin_ldexpf(pass ? acc1[q + 1] : acc0[q + 1], exr[d + 1]));
+              v0 = (uint16_t)b;
+              v1 = (uint16_t)(b >> 16);
             }
+            if (d < lim) *reinterpret_cast<uint16_t*>(lb + d * kSkOutRow) = v0;
+            if (d + 1 < lim) *reinterpret_cast<uint16_t*>(lb + (d + 1) * kSkOutRow) = v1;
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's values are in place
           for (int pc = lane; pc < 4 * nr; pc += 64) {  // 4 pieces of 8 values per row
