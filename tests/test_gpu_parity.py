@@ -237,8 +237,9 @@ def test_layer_against_oracle(s):
     np.testing.assert_allclose(ya, y0 + y, rtol=1e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("n_small", [70, 161, 60], ids=["split", "small", "fallback"])
-def test_chunk_list_boundaries(n_small):
+@pytest.mark.parametrize("n_small,fmt", [(70, 2), (70, 3), (161, 2), (60, 2)],
+                         ids=["split", "split_q3", "small", "fallback"])
+def test_chunk_list_boundaries(n_small, fmt):
     """Routing crafted so that experts hold exactly 1, 2, 31, 32, 33, 63 and 64 rows (the small part
     of the GEMM chunk list) and 65, 96, 97, 224, 225, 300 and 449 rows (the large part: 224 is one
     7-fragment chunk, 225 two, 449 three), plus untouched experts.  With I = 1024 the small part
@@ -252,7 +253,7 @@ def test_chunk_list_boundaries(n_small):
     counts = [small[i % len(small)] for i in range(n_small)] + large + [0] * 4
     E = len(counts)
     T = sum(counts)
-    s = mi.Shape(f"chunks_{n_small}", T=T, H=256, E=E, k=1, I=1024)
+    s = mi.Shape(f"chunks_{n_small}", T=T, H=256, E=E, k=1, I=1024, fmt=fmt)
     rng = np.random.default_rng(11 + n_small)
     target = rng.permutation(np.repeat(np.arange(E), counts))
     L = Layer(s)
