@@ -208,6 +208,41 @@ STRATA_DEVICE void load_row_chunks(RowChunks<FMT, MC>& rc, const uint8_t* row_co
   }
 }
 
+// The chunks of two rows (codes0 / scales0 and codes1 / scales1: each row's chunk 0, from
+// tiled_row_codes / tiled_row_scales), loaded chunk by chunk, both rows' words of a chunk
+// together: row_dots works chunk by chunk, so the counter wait before chunk i then covers chunks
+// 0..i only.  Used by K2, whose lane groups start computing as their only unit's data lands
+// (K2 12.04 -> 11.64 us); K1's waves, which take items one after another, keep the row order.
+template <int FMT, int MC>
+STRATA_DEVICE void load_row_pair_chunks(RowChunks<FMT, MC> (&rc)[2], const uint8_t* codes0,
+                                        const uint16_t* scales0, const uint8_t* codes1,
+                                        const uint16_t* scales1, int nchunk, int c0, int cstep) {
+  constexpr int CB = FMT == 2 ? 8 : 12;
+#pragma unroll
+  for (int i = 0; i < MC; ++i) {
+    const int ch = c0 + cstep * i;
+    if (ch < nchunk) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint8_t* cp = (j ? codes1 : codes0) + (size_t)ch * (8 * CB);
+        if constexpr (FMT == 2) {
+          const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp));
+          rc[j].w[i][0] = v[0]; rc[j].w[i][1] = v[1]; rc[j].w[i][2] = v[2]; rc[j].w[i][3] = v[3];
+        } else {
+          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+          const u32x2_t* p = reinterpret_cast<const u32x2_t*>(cp);
+          const u32x2_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1),
+                        d = __builtin_nontemporal_load(p + 2);
+          rc[j].w[i][0] = a[0]; rc[j].w[i][1] = a[1]; rc[j].w[i][2] = b[0]; rc[j].w[i][3] = b[1];
+          rc[j].w[i][4] = d[0]; rc[j].w[i][5] = d[1];
+        }
+        rc[j].sc[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>((j ? scales1 : scales0) + (size_t)ch * 8));
+      }
+    }
+  }
+}
+
 // Masks and the bf16 2.0 pattern of the 2-bit decode, held in VGPRs so that each pair is one
 // v_and_or_b32 (gfx9 VOP3 takes no literal operand).
 struct Q2Consts {
@@ -641,10 +676,10 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(
     int r0, r1;
     unit_rows(u, r0, r1);
     const size_t base = (size_t)rt.dexp[u / RH] * H + h0;
-    load_row_chunks<FMT, MC>(rr[0], tiled_row_codes<FMT>(down_codes, base + r0, nchunk),
-                             tiled_row_scales(down_scales, base + r0, nchunk), nchunk, j, LPU);
-    load_row_chunks<FMT, MC>(rr[1], tiled_row_codes<FMT>(down_codes, base + r1, nchunk),
-                             tiled_row_scales(down_scales, base + r1, nchunk), nchunk, j, LPU);
+    load_row_pair_chunks<FMT, MC>(rr, tiled_row_codes<FMT>(down_codes, base + r0, nchunk),
+                                  tiled_row_scales(down_scales, base + r0, nchunk),
+                                  tiled_row_codes<FMT>(down_codes, base + r1, nchunk),
+                                  tiled_row_scales(down_scales, base + r1, nchunk), nchunk, j, LPU);
   };
   {
     // piece q: row q / ppr, chunk (q % ppr) / 8, dwords 4 (q % 8) .. + 3 of the chunk, pairs
