@@ -18,6 +18,7 @@
 //              counts of the earlier waves, plus the tile's starting position for its expert.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace strata {
 
@@ -42,56 +43,60 @@ __global__ __launch_bounds__(kPermThreads) void permute_count_kernel(const int* 
   for (int e = threadIdx.x; e < E; e += kPermThreads) hist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// Exclusive prefix sum over the block (blockDim.x = 1024 = 16 waves); returns the block total.
-__device__ int block_exclusive_scan(int v, int* lds16, int& total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int inc = v;
+// Exclusive prefix sums over the block (1024 threads = 16 waves) of N values a thread at once,
+// and their block totals: a DPP scan within each wave, then every wave scans the 16 wave totals
+// from LDS (lds: 16 N ints).  Independent scans share the two barriers.
+template <int N>
+__device__ void block_scan(const int (&v)[N], int (&excl)[N], int (&total)[N], int* lds) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int inc[N];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) lds16[wv] = inc;
-  __syncthreads();
-  int wbase = 0, tot = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
-    const int t = lds16[i];
-    if (i < wv) wbase += t;
-    tot += t;
+  for (int n = 0; n < N; ++n) {
+    inc[n] = wave_scan_dpp(v[n]);
+    if (lane == 63) lds[16 * n + wv] = inc[n];
   }
   __syncthreads();
-  total = tot;
-  return wbase + inc - v;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int t = lane < 16 ? lds[16 * n + lane] : 0;
+    const int ti = wave_scan_dpp(t);
+    excl[n] = __builtin_amdgcn_readlane(ti - t, wv) + inc[n] - v[n];
+    total[n] = __builtin_amdgcn_readlane(ti, 15);
+  }
+  __syncthreads();  // (lds is reused by the next scan)
 }
 
 // The two-part GEMM chunk list (see ChunkList), built by a whole 1024-thread workgroup; a thread
-// with mine holds expert e, its rows at sorted positions [off, off + cnt).  The small part is used
+// with mine holds expert e, its rows at sorted positions [off, off + cnt); nsmall: the number of
+// experts with small_chunks_of(cnt, cl.small_rows) (the caller's scan).  The small part is used
 // only when at least cl.min_small experts qualify for it; within it the chunks of at most
 // kSkinnyRows rows come first (with the experts of up to 2 kSkinnyRows rows split in two when at
-// most kSkinnySplitMax of them exist), each group in expert order.
-__device__ void build_chunk_list(bool mine, int e, int off, int cnt, const ChunkList& cl, int* lds16) {
-  int nsmall;
-  (void)block_exclusive_scan(mine ? small_chunks_of(cnt, cl.small_rows) : 0, lds16, nsmall);
+// most kSkinnySplitMax of them exist), each group in expert order.  lds: 48 ints.
+__device__ void build_chunk_list(bool mine, int e, int off, int cnt, const ChunkList& cl,
+                                 int nsmall, int* lds) {
   const int sr = nsmall >= cl.min_small ? cl.small_rows : 0;
   const int small = mine ? small_chunks_of(cnt, sr) : 0;
-  int nwide;  // small-part experts of more than kSkinnyRows rows
-  (void)block_exclusive_scan(small && cnt > kSkinnyRows ? 1 : 0, lds16, nwide);
+  // small-part experts of more than kSkinnyRows rows
+  const int vw[1] = {small && cnt > kSkinnyRows ? 1 : 0};
+  int ew[1], nwide[1];
+  block_scan<1>(vw, ew, nwide, lds);
   // skinny chunks of this expert: one, two halves of a split one, or none
-  const int nsk = !small ? 0 : cnt <= kSkinnyRows ? 1 : nwide <= kSkinnySplitMax ? 2 : 0;
-  int nskinny, nrest, ltotal;
-  const int kb = block_exclusive_scan(nsk, lds16, nskinny);
-  const int rb = block_exclusive_scan(small && !nsk ? 1 : 0, lds16, nrest);
-  const int lb = block_exclusive_scan(mine ? large_chunks_of(cnt, sr) : 0, lds16, ltotal);
+  const int nsk = !small ? 0 : cnt <= kSkinnyRows ? 1 : nwide[0] <= kSkinnySplitMax ? 2 : 0;
+  // positions in the skinny list, in the rest of the small part and in the large part
+  const int v[3] = {nsk, small && !nsk ? 1 : 0, mine ? large_chunks_of(cnt, sr) : 0};
+  int b[3], n[3];
+  block_scan<3>(v, b, n, lds);
+  const int nskinny = n[0];
   if (nsk == 2) {
-    cl.chunks[kb] = Chunk{e, off, kSkinnyRows, 0};
-    cl.chunks[kb + 1] = Chunk{e, off + kSkinnyRows, cnt - kSkinnyRows, 0};
+    cl.chunks[b[0]] = Chunk{e, off, kSkinnyRows, 0};
+    cl.chunks[b[0] + 1] = Chunk{e, off + kSkinnyRows, cnt - kSkinnyRows, 0};
   } else if (mine) {
-    write_expert_chunks(e, off, cnt, sr, cl.chunks, nsk ? kb : nskinny + rb,
-                        cl.chunks + cl.max_small, lb);
+    write_expert_chunks(e, off, cnt, sr, cl.chunks, nsk ? b[0] : nskinny + b[1],
+                        cl.chunks + cl.max_small, b[2]);
   }
   if (threadIdx.x == 0) {
-    cl.n_chunks[0] = nskinny + nrest;
-    cl.n_chunks[1] = ltotal;
+    cl.n_chunks[0] = nskinny + n[1];
+    cl.n_chunks[1] = n[2];
     cl.n_chunks[2] = nskinny;
   }
 }
@@ -115,7 +120,7 @@ __device__ int tile_sum(const int* __restrict__ hist, int E, int e, int t0, int 
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     const int* __restrict__ hist, int ntiles, int E, int P, int* __restrict__ tile_base,
     int* __restrict__ counts, int* __restrict__ offsets, ChunkList cl) {
-  __shared__ int lds16[16];
+  __shared__ int lds[48];
   __shared__ int psum[1024];  // [part][e]
   const int Ep = 1024 / P;    // threads of one part (>= E)
   const int q = threadIdx.x / Ep, e = threadIdx.x % Ep;
@@ -132,8 +137,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
       before += r < q ? v : 0;
     }
   }
-  int total;
-  const int off = block_exclusive_scan(q == 0 && mine ? cnt : 0, lds16, total);
+  // the experts' offsets, and (for the chunk list) how many qualify for the small part
+  const bool own = q == 0 && mine;
+  const int v[2] = {own ? cnt : 0, own ? small_chunks_of(cnt, cl.small_rows) : 0};
+  int ex[2], tot[2];
+  block_scan<2>(v, ex, tot, lds);
+  const int off = ex[0];
   __shared__ int off_e[1024];
   if (q == 0) off_e[e] = off;
   __syncthreads();
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     }
   }
   if (cl.chunks == nullptr) return;
-  build_chunk_list(q == 0 && mine, e, off, cnt, cl, lds16);
+  build_chunk_list(own, e, off, cnt, cl, tot[1], lds);
 }
 
 // One workgroup of 1024 threads (16 waves) per tile of kPermTile = 1024 slots, in one round: a
@@ -220,11 +229,14 @@ hipError_t launch_permute(const int* ids, int T, int E, int k, int* counts, int*
 // One workgroup of 1024 threads, thread e = expert.
 __global__ __launch_bounds__(1024) void chunks_from_offsets_kernel(const int* __restrict__ offsets,
                                                                   int E, ChunkList cl) {
-  __shared__ int lds16[16];
+  __shared__ int lds[48];
   const int e = threadIdx.x;
   const bool mine = e < E;
   const int off = mine ? offsets[e] : 0, cnt = mine ? offsets[e + 1] - off : 0;
-  build_chunk_list(mine, e, off, cnt, cl, lds16);
+  const int v[1] = {mine ? small_chunks_of(cnt, cl.small_rows) : 0};
+  int ex[1], nsmall[1];
+  block_scan<1>(v, ex, nsmall, lds);
+  build_chunk_list(mine, e, off, cnt, cl, nsmall[0], lds);
 }
 
 hipError_t launch_chunks_from_offsets(const int* offsets, int E, const ChunkList& cl, hipStream_t s) {
