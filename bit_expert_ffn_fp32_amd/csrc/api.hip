@@ -373,11 +373,10 @@ strata_status strata_moe_layer(const strata_moe_weights* w, const uint16_t* x, c
   int* counts = opt_counts ? opt_counts : p.counts;
   int* offsets = opt_offsets ? opt_offsets : p.offsets;
   int* sorted = opt_sorted_slot ? opt_sorted_slot : p.sorted_slot;
-  hipError_t e = strata::launch_route(logits, T, E, k, ids, rw, stream);
+  hipError_t e = strata::launch_route_x16(logits, T, E, k, ids, rw, x, H, p.x16, p.xinfo, stream);
   if (e == hipSuccess)
     e = strata::launch_permute(ids, T, E, k, counts, offsets, sorted, p.slot_pos, p.tile_hist,
                                p.tile_base, p.cl, stream);
-  if (e == hipSuccess) e = strata::launch_x_to_f16(x, T, H, p.x16, p.xinfo, stream);
   if (e == hipSuccess)
     e = strata::launch_ffn_up(w->fmt, p.x16, p.xinfo, sorted, k, (int64_t)T * k, p.chunks,
                               p.n_chunks, p.cl.max_small, p.max_large, w->gate_codes, w->up_codes,

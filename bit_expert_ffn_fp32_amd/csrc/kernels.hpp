@@ -123,6 +123,9 @@ struct XInfo {
 // prefill.hip), and each token's XInfo.
 hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo* xinfo,
                            hipStream_t s);
+// launch_route and launch_x_to_f16 in one launch (T >= 1).
+hipError_t launch_route_x16(const float* logits, int T, int E, int k, int* ids, float* w,
+                            const uint16_t* x, int H, uint16_t* x16, XInfo* xinfo, hipStream_t s);
 
 // S: the number of slots (sizes the work units; the chunk list itself is read on the device).
 // chunks / n_chunks: the two-part list of launch_permute, with max_small and max_large its parts'

@@ -34,6 +34,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "strata_moe.h"
+#include "topk.hpp"
 
 namespace strata {
 
@@ -1124,12 +1125,10 @@ STRATA_DEVICE u32x4_t x_piece_to_f16(const u32x4_t v, int sx, float& n2) {
   return o;
 }
 
-__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                       uint16_t* __restrict__ x16,
-                                                       XInfo* __restrict__ xinfo) {
+// Row t (this wave).
+STRATA_DEVICE void x_to_f16_row(const uint16_t* __restrict__ x, int t, int H, uint16_t* __restrict__ x16,
+                                XInfo* __restrict__ xinfo) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kXRowsPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
   const int n8 = H / 8;
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)t * H);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(x16 + (size_t)t * H);
@@ -1160,6 +1159,35 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
   for (int i = lane + 64 * kXRegPieces; i < n8; i += 64) dst[i] = x_piece_to_f16(src[i], sx, n2);
   n2 = wave_sum(n2);
   if (lane == 0) xinfo[t] = XInfo{sx, n2};
+}
+
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                       uint16_t* __restrict__ x16,
+                                                       XInfo* __restrict__ xinfo) {
+  const int t = blockIdx.x * kXRowsPerBlock + (threadIdx.x >> 6);
+  if (t < T) x_to_f16_row(x, t, H, x16, xinfo);
+}
+
+// The layer call's first launch: the router's top-k (workgroups [0, nroute), one wave per token,
+// the selection of route_kernel) and the conversion of x above (the other workgroups, one wave per
+// row).  The two steps are independent, and each would otherwise pay a launch of its own.
+template <int NPL>
+__global__ __launch_bounds__(64 * kXRowsPerBlock) void route_x16_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int* __restrict__ ids,
+    float* __restrict__ w, int nroute, const uint16_t* __restrict__ x, int H,
+    uint16_t* __restrict__ x16, XInfo* __restrict__ xinfo) {
+  __shared__ __align__(16) uint64_t sel[kXRowsPerBlock][80];
+  const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < nroute) {
+    const int t = blockIdx.x * kXRowsPerBlock + wave;
+    if (t >= T) return;
+    TokenKeys<NPL> tk;
+    load_token_logits<NPL>(logits + (size_t)t * E, E, tk);
+    select_token_wave<NPL>(tk, E, k, ids + (size_t)t * k, w + (size_t)t * k, sel[wave]);
+    return;
+  }
+  const int t = (blockIdx.x - nroute) * kXRowsPerBlock + wave;
+  if (t < T) x_to_f16_row(x, t, H, x16, xinfo);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1296,6 +1324,18 @@ hipError_t launch_x_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, XInfo
                            hipStream_t s) {
   const unsigned grid = (unsigned)((T + kXRowsPerBlock - 1) / kXRowsPerBlock);
   x_to_f16_kernel<<<grid, 256, 0, s>>>(x, T, H, x16, xinfo);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_x16(const float* logits, int T, int E, int k, int* ids, float* w,
+                            const uint16_t* x, int H, uint16_t* x16, XInfo* xinfo, hipStream_t s) {
+  const int n = (T + kXRowsPerBlock - 1) / kXRowsPerBlock;  // workgroups of each half
+  const dim3 grid(2 * n), block(64 * kXRowsPerBlock);
+  if (E <= 64) route_x16_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, n, x, H, x16, xinfo);
+  else if (E <= 128) route_x16_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, n, x, H, x16, xinfo);
+  else if (E <= 256) route_x16_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, n, x, H, x16, xinfo);
+  else if (E <= 512) route_x16_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, n, x, H, x16, xinfo);
+  else route_x16_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, w, n, x, H, x16, xinfo);
   return hipGetLastError();
 }
 
