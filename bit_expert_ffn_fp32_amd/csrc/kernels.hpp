@@ -47,6 +47,15 @@ inline int64_t max_small_chunks(int64_t S, int64_t E, int small_rows) {
   const int64_t split = S / (kSkinnyRows + 1) < kSkinnySplitMax ? S / (kSkinnyRows + 1) : kSkinnySplitMax;
   return (E < S ? E : S) + split;  // one chunk per expert, plus the second halves of split ones
 }
+// Chunks of the small part that run on the small-fragment GEMMs: its experts of more than
+// kSkinnyRows rows, and only when more than kSkinnySplitMax of them exist (else they are split for
+// the skinny GEMMs).  None when S slots cannot give kSkinnySplitMax + 1 experts kSkinnyRows + 1
+// rows each, so those launches are skipped; else at most S / (kSkinnyRows + 1).
+inline int64_t max_rest_chunks(int64_t S, int64_t max_small) {
+  if (S < (int64_t)(kSkinnySplitMax + 1) * (kSkinnyRows + 1)) return 0;
+  const int64_t n = S / (kSkinnyRows + 1);
+  return n < max_small ? n : max_small;
+}
 inline int64_t max_large_chunks(int64_t S, int64_t E, int small_rows, int min_small) {
   // experts in the large part: those with more than small_rows rows, plus (when the small part
   // is not used) fewer than min_small others

@@ -28,7 +28,6 @@
 // consecutive; blockIdx is mapped so that consecutive units run on the same XCD (workgroups are
 // dealt to the 8 XCDs round-robin), which keeps an expert's weights and its tokens' activations
 // in that XCD's L2 while all of its slices run.
-#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -1366,8 +1365,8 @@ hipError_t launch_ffn_up(int fmt, const uint16_t* x16, const XInfo* xinfo, const
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // the rest of the small part has chunks of more than kSkinnyRows rows: at most S / 33 of them
-  const int64_t max_rest = std::min<int64_t>(max_small, S / (kSkinnyRows + 1));
+  // the rest of the small part has chunks of more than kSkinnyRows rows
+  const int64_t max_rest = max_rest_chunks(S, max_small);
   if (max_rest > 0) {  // the rest of the small part: one slice per unit
     const int grid = grid_for_units(max_rest * (I / 128));
     if (fmt == 2) STRATA_LAUNCH_UP(2, 2, kGemmLdsSmall, chunks, n_chunks, 1, grid);
@@ -1415,7 +1414,7 @@ hipError_t launch_ffn_down(int fmt, const uint16_t* a16, const XInfo* xinfo,
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t max_rest = std::min<int64_t>(max_small, S / (kSkinnyRows + 1));
+  const int64_t max_rest = max_rest_chunks(S, max_small);
   if (max_rest > 0) {  // the rest of the small part: two slices per unit (24 stages: K = I is short)
     const int Gs = (H / 256) % 2 == 0 ? 2 : 1;
     const int grid = grid_for_units(max_rest * (H / 256 / Gs));
