@@ -173,19 +173,22 @@ const char* strata_status_string(strata_status st) {
     case STRATA_ERR_UNSUPPORTED: return "unsupported shape";
     case STRATA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case STRATA_ERR_HIP: return "HIP launch error";
+    default: break;
   }
   return "unknown status";
 }
 
+// The size queries answer 0 for every (T, E, k) the compute calls reject, which also keeps the
+// sizes' intermediate counts (E + 1 offsets, the chunk bounds) inside int.
 size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k) {
-  if (!shape_ok(T, E, k)) return 0;
+  if (check_route_shape(T, E, k) != STRATA_OK) return 0;
   const size_t S = (size_t)T * k;
   const size_t ntiles = (S + strata::kPermTile - 1) / strata::kPermTile;
   return 2 * round_up(ntiles * E * 4);
 }
 
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
-  if (!shape_ok(T, E, k) || H < 1 || I < 1) return 0;
+  if (check_route_shape(T, E, k) != STRATA_OK || H < 1 || I < 1) return 0;
   const size_t pre = carve_prefill(nullptr, T, E, k, H, I).bytes;
   const size_t dec = T <= kSplitDecodeMaxT ? carve_decode_perm(nullptr, T, E, k, H, I).bytes : 0;
   return pre > dec ? pre : dec;

@@ -48,7 +48,10 @@ typedef enum {
   STRATA_ERR_INVALID_ARGUMENT = 1,   /* null or misaligned pointer, non-positive size, k > E ... */
   STRATA_ERR_UNSUPPORTED = 2,        /* well-formed but outside what the kernels handle        */
   STRATA_ERR_WORKSPACE_TOO_SMALL = 3,
-  STRATA_ERR_HIP = 4                 /* a kernel launch failed                                  */
+  STRATA_ERR_HIP = 4,                /* a kernel launch failed                                  */
+  /* not a status: makes the type span every non-negative int32, so that an unknown code handed
+   * to strata_status_string is a valid value of it in C++ as well as in C */
+  STRATA_STATUS_MAX_ENUM_ = 0x7FFFFFFF
 } strata_status;
 
 /*
