@@ -403,7 +403,8 @@ strata_status strata_moe_usage_update(const int32_t* topk_ids, int32_t T, int32_
 strata_status strata_moe_usage_rank(const uint64_t* usage, int32_t E, int32_t* order,
                                    hipStream_t stream);
 
-/* Workspace sizes in bytes (host functions; 0 for invalid shapes). */
+/* Workspace sizes in bytes (host functions).  0 for a shape every compute call rejects: T < 0,
+ * E outside 1..1024, k outside 1..min(E, 16), T * k above 2^30 - 1, H or I below 1. */
 size_t strata_moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k);
 size_t strata_moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
 size_t strata_moe_shared_workspace_bytes(int32_t T, int32_t I);

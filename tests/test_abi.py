@@ -221,6 +221,15 @@ def test_usage_validation(L):
 
 def test_workspace_sizes(L):
     assert L.strata_moe_workspace_bytes(-1, 512, 10, 3072, 768) == 0
+    # shapes the compute calls reject get no size (E above 1024, k above 16 or E, T * k too big)
+    assert L.strata_moe_workspace_bytes(4, 2048, 10, 3072, 768) == 0
+    assert L.strata_moe_workspace_bytes(4, 2**31 - 1, 10, 3072, 768) == 0
+    assert L.strata_moe_workspace_bytes(4, 512, 17, 3072, 768) == 0
+    assert L.strata_moe_permute_workspace_bytes(4, 8, 9) == 0
+    assert L.strata_moe_permute_workspace_bytes(2**28, 512, 16) == 0
+    assert L.strata_moe_residual_workspace_bytes(4, 2048, 10, 3072, 768) == 0
+    assert L.strata_moe_block_workspace_bytes(4, 2048, 10, 3072, 768, 768) == 0
+    assert L.strata_moe_permute_workspace_bytes(4, 1024, 16) > 0
     small = L.strata_moe_workspace_bytes(16, 64, 4, 256, 128)
     big = L.strata_moe_workspace_bytes(8192, 512, 10, 3072, 768)
     assert 0 < small < big
